@@ -1,0 +1,28 @@
+"""CPU oracle for speculative-decoding draft verification.
+
+TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, float64 numpy
+statement of what the verification path computes, written from the source
+pages' descriptions.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import it; the library and its Python binding never do,
+and this package imports nothing from them.
+
+Parity status: every function here is pinned by tests against values other
+than itself (published Philox known answers and an independent Philox build,
+closed-form laws, library routines, brute force at tiny sizes).
+"""
+from . import philox  # noqa: F401
+from .verify import (  # noqa: F401
+    GREEDY_TEMPERATURE,
+    RNG_SLOT_SPAN,
+    chain_reject,
+    chain_reject_core,
+    chain_uniforms,
+    decode_logits,
+    greedy_verify,
+    gumbel_row,
+    gumbel_sample,
+    renorm_row,
+    residual_draw,
+    softmax_renorm,
+    temperature_softmax,
+)

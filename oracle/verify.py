@@ -1,0 +1,354 @@
+"""Plain CPU definitions of the verification path (numpy, float64).
+
+TEST INFRASTRUCTURE: see the package docstring.
+
+Sources (pages, by title and section):
+
+* TensorRT-LLM ``_torch/speculative/interface.py`` -- ``rejection_sampling_one_model``
+  (docstring: draft probs [batch, D, vocab], draft ids [batch, D], target probs
+  [batch, D+1, vocab], per-request Philox seed/offset; returns accepted tokens
+  [batch, D+1] = accepted drafts, the corrected or bonus token, then -1);
+  ``_sample_and_accept_draft_tokens_base`` (strict acceptance: count the leading
+  draft tokens equal to the target's); ``_sample_sharded_temperature``
+  (Gumbel-max is an exact temperature sample; rows below the greedy
+  temperature threshold stay greedy); the key-exchange comments in the draft
+  sampler (global argmax, lowest index on ties); ``_RNG_SLOT_SPAN`` (32 offsets
+  between consecutive rows of one request).
+* tokenspeed ``sampling/backends/flashinfer.py`` -- ``FlashInferSamplingBackend.verify``
+  (temperature softmax, then top-k renormalisation followed by top-p
+  renormalisation; greedy batches take the row argmax and a chain verify that
+  fills accept_index with -1 first; per-position coins plus one final coin).
+* The verification rule itself (accept x with probability min(1, p(x)/q(x)),
+  otherwise draw from the normalised residual max(0, p - q); a bonus token from
+  the last target row when every draft is accepted) is the one the pages'
+  rejection op implements.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes):
+
+* temperature below 1e-5 means greedy (one-hot at the lowest-index argmax);
+* top-k keeps every value >= the k-th largest (ties kept), disabled when k <= 0
+  or k >= V; top-p then keeps the smallest set of largest values whose mass
+  reaches top_p times the top-k mass (ties at the threshold kept), active iff
+  top_p < 1; selection compares logits, not rounded probabilities;
+* acceptance is ``u * q(x) < p(x)`` (product form; exact in float64);
+* the residual/bonus draw is an inverse CDF over ascending vocabulary index
+  with float64 running sums; an empty residual falls back to the target row,
+  and an all-zero target row to a uniform index floor(u * V);
+* a draft id outside [0, V) is rejected at its position;
+* uniforms: chain request b uses words 0..D-1 of stream (seed_b, offset_b) for
+  the accept tests and word D for the final draw; Gumbel row j of request b
+  uses word v of stream (seed_b, offset_b + 32 j) for vocabulary entry v.
+
+Decisions that floating point takes carry a margin; a decision inside its band
+flags the request (category and first affected output position).  The Gumbel
+scores are computed in float32, the precision the GPU decides them in.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import philox
+
+GREEDY_TEMPERATURE = 1e-5
+RNG_SLOT_SPAN = 32
+ACCEPT_BAND = 1e-6
+CDF_BAND = 1e-6
+TOPP_BAND = 1e-5
+GUMBEL_BAND = 1e-4
+_MASK64 = (1 << 64) - 1
+
+
+# --------------------------------------------------------------------------- inputs
+def decode_logits(logits, dtype: str) -> np.ndarray:
+    """bf16 bit patterns (uint16) or float32 values -> float64 (exact)."""
+    if dtype == "bf16":
+        bits = np.asarray(logits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    return np.asarray(logits, dtype=np.float32).astype(np.float64)
+
+
+def is_greedy(temperature) -> bool:
+    return float(temperature) < GREEDY_TEMPERATURE
+
+
+# --------------------------------------------------------------------------- softmax + renorm
+def temperature_softmax(z: np.ndarray, temperature: float) -> np.ndarray:
+    """softmax(z / T) of one row; T below the greedy threshold gives a one-hot at argmax.
+
+    tokenspeed flashinfer.py, ``verify``: ``softmax(logits, temperature=...)``.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    if is_greedy(temperature):
+        out = np.zeros_like(z)
+        out[int(np.argmax(z))] = 1.0
+        return out
+    w = np.exp((z - z.max()) / float(temperature))
+    return w / math.fsum(w)
+
+
+def renorm_row(z: np.ndarray, temperature: float, top_k: int, top_p: float):
+    """Temperature softmax, then top-k, then top-p renormalisation of one row.
+
+    tokenspeed flashinfer.py, ``verify``: ``top_k_renorm_prob`` followed by
+    ``top_p_renorm_prob`` (the fused kernel is a drop-in for that pair).
+    Returns (probs float64 [V], flagged: bool).  ``flagged`` marks a row whose
+    top-p threshold sits within TOPP_BAND (relative to the top-k mass) of a
+    mass boundary.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    V = z.shape[0]
+    if is_greedy(temperature):
+        return temperature_softmax(z, temperature), False
+    m = z.max()
+    w = np.exp((z - m) / float(temperature))
+    kept = np.ones(V, dtype=bool)
+    k = int(top_k)
+    if 0 < k < V:
+        kth = np.partition(z, V - k)[V - k]          # k-th largest, counted with multiplicity
+        kept = z >= kth
+    flagged = False
+    tp = float(top_p)
+    if tp < 1.0:
+        s_k = math.fsum(w[kept])
+        vals, inv = np.unique(z[kept], return_inverse=True)   # ascending distinct values
+        mass = np.bincount(inv.reshape(-1), weights=w[kept])
+        cum = np.cumsum(mass[::-1])                  # mass of values >= each distinct value, descending
+        target = tp * s_k
+        hit = np.nonzero(cum >= target)[0]
+        i = int(hit[0]) if hit.size else cum.shape[0] - 1
+        tau = vals[::-1][i]
+        kept &= z >= tau
+        if s_k > 0:
+            near = abs(cum[i] / s_k - tp) < TOPP_BAND
+            if i > 0:
+                near = near or abs(cum[i - 1] / s_k - tp) < TOPP_BAND
+            flagged = bool(near)
+    ws = np.where(kept, w, 0.0)
+    return ws / math.fsum(ws), flagged
+
+
+def softmax_renorm(logits, dtype, temperature, top_k=None, top_p=None, requests=None):
+    """Batch form: logits [B, N, V] -> probs float64 [B, N, V] (NaN rows = not computed).
+
+    Per-request parameters are arrays of length B; ``requests`` lists the batch
+    rows to compute (all when None).
+    """
+    z = decode_logits(logits, dtype)
+    B, N, V = z.shape
+    out = np.full((B, N, V), np.nan)
+    flags = np.zeros((B, N), dtype=bool)
+    reqs = range(B) if requests is None else [int(r) for r in requests]
+    for b in reqs:
+        k = 0 if top_k is None else int(top_k[b])
+        tp = 1.0 if top_p is None else float(top_p[b])
+        for j in range(N):
+            out[b, j], flags[b, j] = renorm_row(z[b, j], float(temperature[b]), k, tp)
+    return out, flags
+
+
+# --------------------------------------------------------------------------- chain rejection
+def chain_uniforms(seed: int, offset: int, D: int):
+    """Accept uniforms u_0..u_{D-1} and the final uniform (with its odd code) of one request."""
+    w = philox.words(seed, offset, D + 1)
+    u = philox.uniform(w)
+    code = int(philox.uniform_code(w[D:D + 1])[0])
+    return u[:D], float(u[D]), code
+
+
+def residual_draw(r: np.ndarray, fallback: np.ndarray, u_final: float, code: int):
+    """Inverse-CDF draw of one index from non-negative weights ``r``.
+
+    token = min{ j : sum_{v <= j} r_v > u * R }, R = sum r (float64 running sum
+    in ascending index order).  If R is not positive the target row
+    ``fallback`` is used instead; if that too has no positive mass the draw is
+    uniform: floor(u * V) computed exactly from the uniform's code.
+    Returns (token, near_boundary).
+    """
+    V = r.shape[0]
+    c = np.cumsum(r)
+    total = c[-1] if V else 0.0
+    if not total > 0.0:
+        r = fallback
+        c = np.cumsum(r)
+        total = c[-1] if V else 0.0
+    if not total > 0.0:
+        return int((code * V) >> 24), False
+    t = u_final * total
+    y = int(np.searchsorted(c, t, side="right"))
+    near = False
+    if y >= V:
+        y = int(np.nonzero(r > 0)[0][-1])
+        near = True
+    lo = c[y - 1] if y > 0 else 0.0
+    hi = c[y]
+    near = near or abs(u_final - lo / total) < CDF_BAND or abs(u_final - hi / total) < CDF_BAND
+    return y, bool(near)
+
+
+def chain_reject_core(q: np.ndarray, x: np.ndarray, p: np.ndarray,
+                      u_accept: np.ndarray, u_final: float, code: int):
+    """Chain rejection of one request given its uniforms.
+
+    q [D, V] draft probs, x [D] draft ids, p [D+1, V] target probs (float32 or
+    float64 values).  For i = 0..D-1: accept x_i iff u_i * q_i(x_i) < p_i(x_i);
+    stop at the first rejection and draw the correction from max(0, p_i - q_i);
+    if all D are accepted draw the bonus from p_D.
+    Returns dict(tokens [D+1], L, near_accept (position or None), near_cdf).
+    """
+    D = x.shape[0]
+    V = p.shape[-1]
+    L = D
+    near_accept = None
+    for i in range(D):
+        xi = int(x[i])
+        if 0 <= xi < V:
+            a = float(p[i, xi])
+            c = float(q[i, xi])
+            if near_accept is None and c > 0 and abs(float(u_accept[i]) - a / c) < ACCEPT_BAND:
+                near_accept = i
+            if float(u_accept[i]) * c < a:
+                continue
+        L = i
+        break
+    target_row = np.asarray(p[L], dtype=np.float64)
+    if L < D:
+        r = np.maximum(0.0, target_row - np.asarray(q[L], dtype=np.float64))
+    else:
+        r = target_row
+    y, near_cdf = residual_draw(r, target_row, u_final, code)
+    tokens = np.full(D + 1, -1, dtype=np.int64)
+    tokens[:L] = x[:L]
+    tokens[L] = y
+    return dict(tokens=tokens, L=L, near_accept=near_accept, near_cdf=near_cdf)
+
+
+def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, requests=None):
+    """Batch form of ``rejection_sampling_one_model``.
+
+    Returns accepted_tokens [B, D+1] (int64, -1 padded; rows not computed are
+    -2), accept_length [B] (number of accepted drafts, -2 if not computed),
+    flag_pos [B] (first output position affected by a near-boundary float
+    decision; D+1 when none) and near_accept [B] (position of a near-threshold
+    accept test, -1 when none; accept tests are exact products, so this is
+    informational).
+    """
+    B, D = np.asarray(draft_ids).shape
+    tokens = np.full((B, D + 1), -2, dtype=np.int64)
+    L = np.full(B, -2, dtype=np.int64)
+    flag_pos = np.full(B, D + 1, dtype=np.int64)
+    near_accept = np.full(B, -1, dtype=np.int64)
+    reqs = range(B) if requests is None else [int(r) for r in requests]
+    for b in reqs:
+        ua, uf, code = chain_uniforms(int(seed[b]), int(offset[b]), D)
+        res = chain_reject_core(draft_probs[b], draft_ids[b], target_probs[b], ua, uf, code)
+        tokens[b] = res["tokens"]
+        L[b] = res["L"]
+        if res["near_cdf"]:
+            flag_pos[b] = res["L"]
+        if res["near_accept"] is not None:
+            near_accept[b] = res["near_accept"]
+    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
+
+
+# --------------------------------------------------------------------------- greedy verify
+def greedy_verify(logits, dtype, draft_ids, requests=None):
+    """Greedy chain verify.
+
+    tokenspeed flashinfer.py, ``verify`` (all-greedy branch): target tokens are
+    the row argmax (lowest index on ties, as the TensorRT-LLM draft sampler's
+    key-exchange comments state); L = number of leading draft ids equal to the
+    target tokens.  Outputs: accepted_tokens = y_0..y_L then -1; predict[b, j] =
+    y_j for j <= L else -1; accept_index[b, j] = b*N + j (flat index into
+    predict) for j <= L else -1; argmax [B, N] = y for every row.
+    """
+    z = decode_logits(logits, dtype)
+    B, N, V = z.shape
+    D = N - 1
+    x = np.asarray(draft_ids)
+    tokens = np.full((B, N), -2, dtype=np.int64)
+    predict = np.full((B, N), -2, dtype=np.int64)
+    accept_index = np.full((B, N), -2, dtype=np.int64)
+    argmax = np.full((B, N), -2, dtype=np.int64)
+    L = np.full(B, -2, dtype=np.int64)
+    reqs = range(B) if requests is None else [int(r) for r in requests]
+    for b in reqs:
+        y = np.array([int(np.argmax(z[b, j])) for j in range(N)], dtype=np.int64)
+        n_acc = 0
+        while n_acc < D and int(x[b, n_acc]) == y[n_acc]:
+            n_acc += 1
+        L[b] = n_acc
+        tokens[b] = -1
+        tokens[b, :n_acc + 1] = y[:n_acc + 1]
+        predict[b] = tokens[b]
+        accept_index[b] = -1
+        accept_index[b, :n_acc + 1] = b * N + np.arange(n_acc + 1)
+        argmax[b] = y
+    return dict(accepted_tokens=tokens, accept_length=L, predict=predict,
+                accept_index=accept_index, argmax=argmax)
+
+
+# --------------------------------------------------------------------------- Gumbel-max
+def gumbel_row(z32: np.ndarray, temperature: float, seed: int, subseq: int):
+    """Temperature sample of one row by Gumbel-max, in float32.
+
+    s_v = z_v / T + G_v with G_v = -ln(-ln u_v), u_v = uniform of word v of
+    stream (seed, subseq); token = lowest-index argmax of s.  Returns (token,
+    near_tie) where near_tie marks a top-two score gap below GUMBEL_BAND.
+    """
+    z32 = np.asarray(z32, dtype=np.float32)
+    V = z32.shape[0]
+    u = philox.uniform(philox.words(seed, subseq, V)).astype(np.float32)
+    g = -np.log(-np.log(u))
+    s = z32 / np.float32(temperature) + g
+    y = int(np.argmax(s))
+    near = False
+    if V > 1:
+        top2 = np.partition(s, V - 2)[V - 2:]
+        near = bool(float(top2[1]) - float(top2[0]) < GUMBEL_BAND)
+    return y, near
+
+
+def gumbel_sample(logits, dtype, temperature, draft_ids, seed, offset, requests=None,
+                  all_rows=False):
+    """Temperature-only target sampling by Gumbel-max, then strict chain acceptance.
+
+    TensorRT-LLM interface.py, ``_sample_sharded_temperature`` and
+    ``_sample_and_accept_draft_tokens_base``.  Row j of request b draws from
+    stream (seed_b, offset_b + 32 j); rows with T below the greedy threshold
+    take the plain argmax.  Rows are computed up to the first mismatch unless
+    ``all_rows``.  Returns accepted_tokens, accept_length, sampled [B, N] (-2
+    where not computed), flag_pos [B] (first row whose decision is a near tie,
+    N when none).
+    """
+    z = decode_logits(logits, dtype).astype(np.float32)
+    B, N, V = z.shape
+    D = N - 1
+    x = np.asarray(draft_ids)
+    tokens = np.full((B, N), -2, dtype=np.int64)
+    sampled = np.full((B, N), -2, dtype=np.int64)
+    L = np.full(B, -2, dtype=np.int64)
+    flag_pos = np.full(B, N, dtype=np.int64)
+    reqs = range(B) if requests is None else [int(r) for r in requests]
+    for b in reqs:
+        T = float(np.float32(temperature[b]))
+        n_acc = None
+        for j in range(N):
+            if is_greedy(T):
+                yj, near = int(np.argmax(z[b, j])), False
+            else:
+                sub = (int(offset[b]) + RNG_SLOT_SPAN * j) & _MASK64
+                yj, near = gumbel_row(z[b, j], T, int(seed[b]), sub)
+            sampled[b, j] = yj
+            if near and flag_pos[b] == N:
+                flag_pos[b] = j
+            if n_acc is None and (j == D or int(x[b, j]) != yj):
+                n_acc = j
+                if not all_rows:
+                    break
+        L[b] = n_acc
+        tokens[b] = -1
+        tokens[b, :n_acc + 1] = sampled[b, :n_acc + 1]
+    return dict(accepted_tokens=tokens, accept_length=L, sampled=sampled, flag_pos=flag_pos)

@@ -1,0 +1,15 @@
+"""Seeded synthetic inputs for speculative-decoding draft verification.
+
+This package is the only code shared by the CPU oracle and the HIP path's
+tests and benchmark.  It synthesises logits, draft distributions, draft token
+ids and per-request Philox (seed, offset) pairs; it contains none of the
+verification arithmetic (no temperature softmax, no top-k/top-p filter, no
+acceptance rule, no argmax over target rows, no random-stream layout).
+"""
+from .synth import (  # noqa: F401
+    CONFIGS,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    make_config,
+    fuzz_case,
+)
