@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify path on one MI355X.
+
+Default workload: chain rejection sampling on the large-vocabulary batch
+(B=256 requests, D=5 drafts, V=128256, float32 target and draft
+probabilities).  One step = one ``specverify_chain_reject`` call over the
+whole batch.  Metric: verified vocab rows per second, B * (D + 1) per step,
+plus the dominant kernel's achieved HBM bandwidth (algorithmic bytes / kernel
+time) against the 8 TB/s peak.
+
+Inputs are synthetic (see workloads/), resident in HBM before timing; R
+replicas (copies at distinct addresses with distinct Philox offsets) rotate
+so consecutive calls never hit the 256 MB Infinity Cache with the previous
+call's rows.  Timing uses HIP events on the stream the kernels run on.
+
+Other workloads (``--workload``) exist for profiling: ``topk_topp_chain``
+(softmax_renorm -> chain_reject, B=64 D=3 V=32000 bf16), ``greedy`` (greedy
+verify, B=512 N=4 V=151936 bf16).
+
+The CPU baseline is the numpy oracle timed on this host on the same inputs
+(whole batches repeated for --cpu-seconds), single threaded.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified vocab rows/sec (batch×(D+1)) + achieved HBM GB/s vs MI355X peak"
+PEAK_HBM_GBS = 8000.0
+PROBE_GRANULE = 64     # bytes a single-element probe costs in HBM (one 64-byte line)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="large_vocab_chain_reject",
+                    choices=["large_vocab_chain_reject", "topk_topp_chain", "greedy"])
+    ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- device helpers
+def _t(a, dev):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint64:
+        a = a.view(np.int64)
+    return torch.from_numpy(a).to(dev)
+
+
+def _bf16(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "token_sampling_temp_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(summary, digest):
+    """HBM bytes per launch from a committed counter summary, if it was taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_digest:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != digest:
+        return None
+    return float(m_b.group(1))
+
+
+# --------------------------------------------------------------------------- workloads
+class ChainWorkload:
+    """B=256 D=5 V=128256 chain rejection on float32 probabilities."""
+    name = "large_vocab_chain_reject"
+    kernel = "chain_reject_kernel"
+    sources = ("chain_reject.hip", "sv_common.hpp")
+    counters = "chain_reject_large_vocab_counters.txt"
+    dtype = "f32"
+
+    def __init__(self, dev, replicas):
+        from workloads import make_config
+        t0 = time.time()
+        self.host = make_config(3)
+        log(f"generated inputs in {time.time() - t0:.1f}s")
+        h = self.host
+        self.B, self.D, self.V = h["B"], h["D"], h["V"]
+        self.R = replicas or 4
+        self.reps = []
+        for r in range(self.R):
+            off = np.full(self.B, 4096 * r, np.uint64)
+            self.reps.append(dict(q=_t(h["draft_probs"], dev), x=_t(h["draft_ids"], dev),
+                                  p=_t(h["target_probs"], dev), seed=_t(h["seed"], dev), off=_t(off, dev),
+                                  off_host=off))
+        import token_sampling_temp_amd as sv
+        self.sv = sv
+        import torch
+        self.acc = torch.empty((self.B, self.D + 1), dtype=torch.int32, device=dev)
+        self.alen = torch.empty((self.B,), dtype=torch.int32, device=dev)
+        self.rows = self.B * (self.D + 1)
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        self.sv.chain_reject(r["q"], r["x"], r["p"], r["seed"], r["off"], out=(self.acc, self.alen))
+
+    def algorithmic_bytes(self):
+        """Bytes the method must move per call, from each replica's realised accept lengths."""
+        per = []
+        self.L = []
+        for i in range(self.R):
+            self.step(i)
+            L = self.alen.cpu().numpy().astype(np.int64)
+            self.L.append(L)
+            D, V = self.D, self.V
+            rows = np.where(L < D, 8 * V, 4 * V)
+            probes = 2 * PROBE_GRANULE * np.minimum(L + 1, D)
+            per.append(int(rows.sum() + probes.sum() + self.B * (8 * D + 24)))
+        return float(np.mean(per))
+
+    def extra(self):
+        L = np.concatenate(self.L)
+        return {"mean_accept_length": round(float(L.mean()), 4),
+                "frac_all_accepted": round(float(np.mean(L == self.D)), 4)}
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "draft_tokens": self.D, "vocab": self.V,
+                "input": "float32 target/draft probabilities", "replicas": self.R}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, passes = 0, time.perf_counter(), 0
+        while True:
+            off = self.reps[passes % self.R]["off_host"]
+            oracle.chain_reject(h["draft_probs"], h["draft_ids"], h["target_probs"], h["seed"], off)
+            rows += self.rows
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
+                          f"{el:.1f}s single-threaded numpy"}
+
+
+class GreedyWorkload:
+    name = "greedy"
+    kernel = "greedy_verify_kernel"
+    sources = ("greedy_verify.hip", "sv_argmax.hpp", "sv_common.hpp")
+    counters = "greedy_verify_counters.txt"
+    dtype = "bf16"
+
+    def __init__(self, dev, replicas):
+        from workloads import make_config
+        import torch
+        import token_sampling_temp_amd as sv
+        self.sv = sv
+        h = make_config(4)
+        self.host = h
+        self.B, self.D, self.V = h["B"], h["D"], h["V"]
+        self.R = replicas or 2
+        self.reps = [dict(z=_bf16(h["logits"], dev), x=_t(h["draft_ids"], dev)) for _ in range(self.R)]
+        self.out = {"accepted_tokens": torch.empty((self.B, self.D + 1), dtype=torch.int32, device=dev),
+                    "accept_length": torch.empty((self.B,), dtype=torch.int32, device=dev)}
+        self.rows = self.B * (self.D + 1)
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        self.sv.greedy_verify(r["z"], r["x"], predict=False, accept_index=False, out=self.out)
+
+    def algorithmic_bytes(self):
+        self.step(0)
+        L = self.out["accept_length"].cpu().numpy().astype(np.int64)
+        self.L = L
+        return float(((L + 1) * self.V * 2).sum() + self.B * (4 * self.D + 4 * (self.D + 1) + 4))
+
+    def extra(self):
+        return {"mean_accept_length": round(float(self.L.mean()), 4)}
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "draft_tokens": self.D, "vocab": self.V,
+                "input": "bf16 logits", "replicas": self.R}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, n = 0, time.perf_counter(), 0
+        while True:
+            b = n % self.B
+            oracle.greedy_verify(h["logits"], "bf16", h["draft_ids"], requests=[b])
+            rows += self.D + 1
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} requests, {el:.1f}s single-threaded numpy"}
+
+
+class TopkToppWorkload:
+    name = "topk_topp_chain"
+    kernel = "softmax_renorm_kernel"
+    sources = ("softmax_renorm.hip", "sv_argmax.hpp", "sv_common.hpp")
+    counters = "softmax_renorm_topk_topp_counters.txt"
+    dtype = "bf16"
+
+    def __init__(self, dev, replicas):
+        from workloads import make_config
+        import torch
+        import token_sampling_temp_amd as sv
+        self.sv = sv
+        h = make_config(2)
+        self.host = h
+        self.B, self.D, self.V = h["B"], h["D"], h["V"]
+        self.R = replicas or 8
+        self.reps = [dict(z=_bf16(h["logits"], dev), q=_t(h["draft_probs"], dev), x=_t(h["draft_ids"], dev),
+                          T=_t(h["temperature"], dev), k=_t(h["top_k"], dev), p=_t(h["top_p"], dev),
+                          seed=_t(h["seed"], dev), off=_t(np.full(self.B, 4096 * r, np.uint64), dev))
+                     for r in range(self.R)]
+        N = self.D + 1
+        self.probs = [torch.empty((self.B, N, self.V), dtype=torch.float32, device=dev) for _ in range(self.R)]
+        self.acc = torch.empty((self.B, N), dtype=torch.int32, device=dev)
+        self.alen = torch.empty((self.B,), dtype=torch.int32, device=dev)
+        self.rows = self.B * N
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        pr = self.probs[i % self.R]
+        self.sv.softmax_renorm(r["z"], r["T"], r["k"], r["p"], out=pr)
+        self.sv.chain_reject(r["q"], r["x"], pr, r["seed"], r["off"], out=(self.acc, self.alen))
+
+    def algorithmic_bytes(self):
+        # softmax_renorm: read bf16 logits, write float32 probabilities (every row)
+        N = self.D + 1
+        return float(self.B * N * self.V * (2 + 4))
+
+    def extra(self):
+        return {}
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "draft_tokens": self.D, "vocab": self.V,
+                "temperature": 0.7, "top_k": 50, "top_p": 0.9, "input": "bf16 logits", "replicas": self.R}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, n = 0, time.perf_counter(), 0
+        while True:
+            b = n % self.B
+            probs, _ = oracle.softmax_renorm(h["logits"], "bf16", h["temperature"], h["top_k"], h["top_p"],
+                                             requests=[b])
+            full = np.zeros((self.B,) + probs.shape[1:])
+            full[b] = probs[0]
+            oracle.chain_reject(h["draft_probs"], h["draft_ids"], full, h["seed"], np.zeros(self.B, np.uint64),
+                                requests=[b])
+            rows += self.D + 1
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} requests, {el:.1f}s single-threaded numpy"}
+
+
+WORKLOADS = {c.name: c for c in (ChainWorkload, GreedyWorkload, TopkToppWorkload)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import token_sampling_temp_amd as sv
+    sv.lib()
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload](dev, args.replicas)
+    log(f"workload {wl.name}: warmup {args.warmup}, steps {args.steps}")
+    alg_bytes = wl.algorithmic_bytes()
+    for i in range(args.warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        wl.step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"timed {args.steps} steps: {ms * 1e3:.2f} us/step")
+    rows_per_s = wl.rows / (ms * 1e-3)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    digest = _source_digest(*wl.sources)
+    traffic = load_traffic(wl.counters, digest)
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle baseline")
+        cpu = wl.cpu_baseline(args.cpu_seconds)
+    out = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": wl.config(),
+        "roofline": {"bound": "hbm", "kernel": wl.kernel, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes, "kernel_source_digest": digest},
+        "cpu_baseline": cpu,
+    }
+    out.update(wl.extra())
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * specverify: speculative-decoding draft verification on AMD Instinct MI355X
+ * (gfx950).  C ABI over caller-owned device buffers.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers owned by the caller, contiguous and
+ *   row-major with the vocabulary innermost: a [B, N, V] tensor holds row
+ *   (b, j) at element offset (b * N + j) * V.  Element alignment is required;
+ *   16-byte alignment of rows is not (unaligned rows take a slower load path).
+ * - B = requests, D = draft tokens per request (0 <= D <= 16), N = D + 1
+ *   verified positions, V = vocabulary size (1 <= V < 2^31).
+ * - dtype: SPECVERIFY_F32 (float) or SPECVERIFY_BF16 (bfloat16 bit patterns).
+ * - req_index: optional device array of n_req batch rows to process; outputs
+ *   are written at those rows and other rows are left untouched.  NULL means
+ *   every row, and then n_req must equal B.  0 <= n_req <= B.  An index
+ *   outside [0, B) is skipped on the device.  Listing a row twice makes two
+ *   workgroups write identical values to it.
+ * - Per-request parameters (temperature, top_k, top_p, seed, offset) are
+ *   device arrays of length B indexed by batch row.
+ * - Temperature below 1e-5 (compared in double precision) means greedy: a
+ *   one-hot at the lowest-index maximum.  The page "TensorRT-LLM
+ *   _torch/speculative/interface.py", _sample_sharded_temperature, keeps rows
+ *   below the greedy threshold greedy; the threshold value is not on the
+ *   pages, 1e-5 is this library's.
+ * - Random numbers: Philox4x32-10 (Salmon et al., SC'11) with key = seed and
+ *   counter = (block index lo, hi, subsequence lo, hi); word t of a stream is
+ *   lane t % 4 of block t / 4; a word w maps to the uniform
+ *   u = (2 * (w >> 9) + 1) * 2^-24.  The per-request offset names the
+ *   request's own subsequence ("TensorRT-LLM interface.py",
+ *   rejection_sampling_one_model docstring).
+ * - stream is a hipStream_t passed as void*; NULL is the default stream.
+ *   Calls are asynchronous; nothing is read back to the host.  The library
+ *   never synchronises.  The softmax/top-k/top-p and greedy paths use no
+ *   device memory besides the arguments.
+ * - Host-side validation runs before any HIP call.  Return codes:
+ *   SPECVERIFY_OK, SPECVERIFY_INVALID_ARGUMENT (nothing launched),
+ *   SPECVERIFY_UNSUPPORTED (current device is not gfx950),
+ *   SPECVERIFY_HIP_ERROR (launch failed; see specverify_last_error()).
+ * - Outputs are written completely for every processed request, including the
+ *   -1 padding, so callers need not pre-fill them.
+ * - Non-finite inputs never cause out-of-bounds access or a hang; the tokens
+ *   they produce are unspecified except where stated.
+ * - A request's outputs depend only on its own inputs and (seed, offset), not
+ *   on its batch position, B, req_index order or the stream.
+ */
+#ifndef SPECVERIFY_H_
+#define SPECVERIFY_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPECVERIFY_OK 0
+#define SPECVERIFY_INVALID_ARGUMENT 1
+#define SPECVERIFY_UNSUPPORTED 2
+#define SPECVERIFY_HIP_ERROR 3
+
+#define SPECVERIFY_F32 0
+#define SPECVERIFY_BF16 1
+
+#define SPECVERIFY_MAX_DRAFT 16
+#define SPECVERIFY_RNG_SLOT_SPAN 32
+#define SPECVERIFY_VERSION 100
+
+/*
+ * Temperature softmax followed by top-k then top-p renormalisation.
+ *
+ * Passage: "tokenspeed sampling/backends/flashinfer.py",
+ * FlashInferSamplingBackend.verify -- softmax(logits, temperature) and then
+ * top_k_renorm_prob followed by top_p_renorm_prob (the fused kernel replaces
+ * that pair); per-row knobs are shared by a request's N positions.
+ *
+ * logits      [B, npos, V] dtype          input
+ * temperature [B] float                   T; T < 1e-5 gives a one-hot at the argmax
+ * top_k       [B] int32 or NULL           0 < k < V keeps every value >= the
+ *                                         k-th largest (ties kept); else off
+ * top_p       [B] float or NULL           top_p < 1 keeps the smallest set of
+ *                                         largest values whose mass reaches
+ *                                         top_p times the top-k mass (ties at
+ *                                         the threshold kept); else off
+ * probs_out   [B, npos, V] float          output: w_v / sum of kept w, 0 elsewhere,
+ *                                         w_v = exp((z_v - max z) / T)
+ * Selection compares logits, never rounded probabilities.  npos >= 1.
+ */
+int specverify_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t npos, int64_t V,
+                              const float* temperature, const int32_t* top_k, const float* top_p,
+                              const int32_t* req_index, int64_t n_req, float* probs_out,
+                              void* stream);
+
+/*
+ * Chain rejection sampling of a linear draft.
+ *
+ * Passage: "TensorRT-LLM _torch/speculative/interface.py",
+ * rejection_sampling_one_model -- draft probs [batch, D, vocab] float32,
+ * draft ids [batch, D] int32, target probs [batch, D+1, vocab] float32,
+ * per-request Philox seed/offset; returns the accepted draft tokens, the
+ * corrected or bonus token, then -1.
+ *
+ * draft_probs     [B, D, V] float   q (may be NULL when D == 0)
+ * draft_ids       [B, D] int32      x (may be NULL when D == 0)
+ * target_probs    [B, D+1, V] float p
+ * seed, offset    [B] uint64        Philox key and subsequence of each request
+ * accepted_tokens [B, D+1] int32    output: x_0..x_{L-1}, y, then -1
+ * accept_length   [B] int32         output: L in [0, D] (the request emits L+1 tokens)
+ *
+ * Rule: u_i = uniform of word i (i < D), u_f = uniform of word D.  For i = 0..D-1,
+ * accept x_i iff u_i * q_i(x_i) < p_i(x_i) (exact double product); a draft id
+ * outside [0, V) is rejected.  At the first rejection i, y is drawn from
+ * r = max(0, p_i - q_i); when all D are accepted, y is drawn from r = p_D.
+ * The draw is y = min{ j : sum_{v<=j} r_v > u_f * R }, R = sum r, with
+ * double-precision sums in ascending index order; an empty r falls back to
+ * the target row, and an all-zero target row to floor(u_f * V).
+ */
+int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids,
+                            const float* target_probs, const uint64_t* seed,
+                            const uint64_t* offset, int64_t B, int64_t D, int64_t V,
+                            const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
+                            int32_t* accept_length, void* stream);
+
+/*
+ * Greedy chain verify.
+ *
+ * Passage: "tokenspeed sampling/backends/flashinfer.py",
+ * FlashInferSamplingBackend.verify, all-greedy branch -- target tokens are the
+ * row argmax, then verify_chain_greedy writes predict, accept_index (pre-filled
+ * with -1) and the accept length; ties go to the lowest index ("TensorRT-LLM
+ * interface.py", the draft sampler's key-exchange comments).
+ *
+ * target_logits   [B, D+1, V] dtype
+ * draft_ids       [B, D] int32 (may be NULL when D == 0)
+ * accepted_tokens [B, D+1] int32   output: y_0..y_L then -1
+ * accept_length   [B] int32        output: L = leading draft ids equal to y
+ * predict         [B, D+1] int32 or NULL   output: y_j for j <= L else -1
+ * accept_index    [B, D+1] int32 or NULL   output: b*(D+1)+j for j <= L else -1
+ *                                          (flat index into predict)
+ * argmax_out      [B, D+1] int32 or NULL   output: y_j for every j; requesting
+ *                                          it makes every row be read
+ * Rows after the first mismatch are not read unless argmax_out is given.
+ * Equal values (including -0 and +0) tie; a NaN counts as the maximum, and
+ * the first NaN wins.
+ */
+int specverify_greedy_verify(const void* target_logits, int dtype, const int32_t* draft_ids,
+                             int64_t B, int64_t D, int64_t V, const int32_t* req_index,
+                             int64_t n_req, int32_t* accepted_tokens, int32_t* accept_length,
+                             int32_t* predict, int32_t* accept_index, int32_t* argmax_out,
+                             void* stream);
+
+/*
+ * Temperature-only target sampling by Gumbel-max, then strict chain acceptance.
+ *
+ * Passage: "TensorRT-LLM _torch/speculative/interface.py",
+ * _sample_sharded_temperature (Gumbel-max is an exact temperature sample; rows
+ * below the greedy threshold stay greedy) and
+ * _sample_and_accept_draft_tokens_base (strict acceptance counts the leading
+ * draft tokens equal to the target's).
+ *
+ * target_logits   [B, D+1, V] dtype
+ * temperature     [B] float
+ * draft_ids       [B, D] int32 (may be NULL when D == 0)
+ * seed, offset    [B] uint64
+ * accepted_tokens [B, D+1] int32   output: y_0..y_L then -1
+ * accept_length   [B] int32        output: L
+ * sampled_out     [B, D+1] int32 or NULL   output: y_j for every j (all rows read)
+ *
+ * Row j of request b: s_v = z_v / T + G_v, G_v = -ln(-ln u_v), u_v the uniform
+ * of word v of stream (seed_b, offset_b + 32 j); y_j = lowest-index argmax of
+ * s, computed in float.  The stream spacing of 32 per row follows the page's
+ * _RNG_SLOT_SPAN.  Rows after the first mismatch are not read unless
+ * sampled_out is given.
+ */
+int specverify_gumbel_sample(const void* target_logits, int dtype, const float* temperature,
+                             const int32_t* draft_ids, const uint64_t* seed,
+                             const uint64_t* offset, int64_t B, int64_t D, int64_t V,
+                             const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
+                             int32_t* accept_length, int32_t* sampled_out, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* specverify_status_string(int status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* specverify_last_error(void);
+
+/* SPECVERIFY_VERSION of the built library. */
+int specverify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H_ */

@@ -131,21 +131,22 @@ def renorm_row(z: np.ndarray, temperature: float, top_k: int, top_p: float):
 
 
 def softmax_renorm(logits, dtype, temperature, top_k=None, top_p=None, requests=None):
-    """Batch form: logits [B, N, V] -> probs float64 [B, N, V] (NaN rows = not computed).
+    """Batch form: logits [B, N, V] -> (probs float64, flags bool).
 
-    Per-request parameters are arrays of length B; ``requests`` lists the batch
-    rows to compute (all when None).
+    Per-request parameters are arrays of length B.  With ``requests`` None the
+    result covers every row ([B, N, V] and [B, N]); otherwise it holds the
+    listed requests in the given order ([len(requests), N, V]).
     """
-    z = decode_logits(logits, dtype)
-    B, N, V = z.shape
-    out = np.full((B, N, V), np.nan)
-    flags = np.zeros((B, N), dtype=bool)
-    reqs = range(B) if requests is None else [int(r) for r in requests]
-    for b in reqs:
+    B, N, V = np.shape(logits)
+    reqs = list(range(B)) if requests is None else [int(r) for r in requests]
+    out = np.empty((len(reqs), N, V))
+    flags = np.zeros((len(reqs), N), dtype=bool)
+    for i, b in enumerate(reqs):
+        z = decode_logits(logits[b], dtype)
         k = 0 if top_k is None else int(top_k[b])
         tp = 1.0 if top_p is None else float(top_p[b])
         for j in range(N):
-            out[b, j], flags[b, j] = renorm_row(z[b, j], float(temperature[b]), k, tp)
+            out[i, j], flags[i, j] = renorm_row(z[j], float(temperature[b]), k, tp)
     return out, flags
 
 
@@ -264,8 +265,7 @@ def greedy_verify(logits, dtype, draft_ids, requests=None):
     y_j for j <= L else -1; accept_index[b, j] = b*N + j (flat index into
     predict) for j <= L else -1; argmax [B, N] = y for every row.
     """
-    z = decode_logits(logits, dtype)
-    B, N, V = z.shape
+    B, N, V = np.shape(logits)
     D = N - 1
     x = np.asarray(draft_ids)
     tokens = np.full((B, N), -2, dtype=np.int64)
@@ -275,7 +275,8 @@ def greedy_verify(logits, dtype, draft_ids, requests=None):
     L = np.full(B, -2, dtype=np.int64)
     reqs = range(B) if requests is None else [int(r) for r in requests]
     for b in reqs:
-        y = np.array([int(np.argmax(z[b, j])) for j in range(N)], dtype=np.int64)
+        z = decode_logits(logits[b], dtype)
+        y = np.array([int(np.argmax(z[j])) for j in range(N)], dtype=np.int64)
         n_acc = 0
         while n_acc < D and int(x[b, n_acc]) == y[n_acc]:
             n_acc += 1
@@ -323,8 +324,7 @@ def gumbel_sample(logits, dtype, temperature, draft_ids, seed, offset, requests=
     where not computed), flag_pos [B] (first row whose decision is a near tie,
     N when none).
     """
-    z = decode_logits(logits, dtype).astype(np.float32)
-    B, N, V = z.shape
+    B, N, V = np.shape(logits)
     D = N - 1
     x = np.asarray(draft_ids)
     tokens = np.full((B, N), -2, dtype=np.int64)
@@ -333,14 +333,15 @@ def gumbel_sample(logits, dtype, temperature, draft_ids, seed, offset, requests=
     flag_pos = np.full(B, N, dtype=np.int64)
     reqs = range(B) if requests is None else [int(r) for r in requests]
     for b in reqs:
+        z = decode_logits(logits[b], dtype).astype(np.float32)
         T = float(np.float32(temperature[b]))
         n_acc = None
         for j in range(N):
             if is_greedy(T):
-                yj, near = int(np.argmax(z[b, j])), False
+                yj, near = int(np.argmax(z[j])), False
             else:
                 sub = (int(offset[b]) + RNG_SLOT_SPAN * j) & _MASK64
-                yj, near = gumbel_row(z[b, j], T, int(seed[b]), sub)
+                yj, near = gumbel_row(z[j], T, int(seed[b]), sub)
             sampled[b, j] = yj
             if near and flag_pos[b] == N:
                 flag_pos[b] = j

@@ -140,8 +140,10 @@ def test_batch_form_and_bf16_decode():
     z = rng.standard_normal((2, 3, 40)).astype(np.float32)
     zb = f32_to_bf16_bits(z)
     probs, flags = softmax_renorm(zb, "bf16", np.array([1.0, 0.0], np.float32),
-                                  np.array([5, 0], np.int32), np.array([0.8, 1.0], np.float32),
-                                  requests=[0, 1])
+                                  np.array([5, 0], np.int32), np.array([0.8, 1.0], np.float32))
+    sub, _ = softmax_renorm(zb, "bf16", np.array([1.0, 0.0], np.float32), np.array([5, 0], np.int32),
+                            np.array([0.8, 1.0], np.float32), requests=[1])
+    assert np.array_equal(sub[0], probs[1])
     assert probs.shape == (2, 3, 40)
     np.testing.assert_allclose(probs.sum(-1), 1.0, atol=1e-13)
     assert np.all((probs[1] == 0) | (probs[1] == 1))

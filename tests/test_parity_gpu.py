@@ -1,0 +1,386 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer results (tokens, accept lengths, predict, accept_index, argmax) must be
+bit-exact except decisions the oracle flags as falling inside a float band
+(CDF boundary 1e-6, top-p boundary 1e-5 of the top-k mass, Gumbel near tie
+1e-4); flagged requests are compared up to the flagged position.  Probabilities
+must agree within 1e-5 absolute.  Every test prints its case before launching.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import dev, dev_logits, guard_intact, guarded_i32, log, np_i, SENTINEL
+from workloads import MODE_GREEDY, MODE_TEMPERATURE, MODE_TOPK, MODE_TOPP, fuzz_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+PROB_ATOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def sv():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_sampling_temp_amd as m
+    m.lib()   # raises when the HIP library is missing: there is no fallback
+    return m
+
+
+# --------------------------------------------------------------------------- comparison helpers
+def assert_chain_match(gpu_tok, gpu_len, ref, reqs, ctx, check_flags=True):
+    """Bit-exact tokens/accept lengths except from a flagged position on."""
+    flagged = 0
+    for b in reqs:
+        L = int(ref["accept_length"][b])
+        fp = int(ref["flag_pos"][b])
+        assert int(gpu_len[b]) == L or fp <= L, (ctx, b, int(gpu_len[b]), L)
+        n = min(fp, L + 1) if check_flags else L + 1
+        assert list(gpu_tok[b, :n]) == list(ref["accepted_tokens"][b, :n]), (ctx, b, gpu_tok[b], ref["accepted_tokens"][b])
+        if int(gpu_len[b]) == L:
+            assert np.all(gpu_tok[b, L + 1:] == -1), (ctx, b)
+        flagged += fp <= L
+    return flagged
+
+
+def greedy_drafts(rng, z, dtype, D, p_match=0.7):
+    y = oracle.greedy_verify(z, dtype, np.zeros((z.shape[0], D), np.int32))["argmax"]
+    V = z.shape[-1]
+    rnd = rng.integers(0, V, size=(z.shape[0], D))
+    return np.where(rng.random((z.shape[0], D)) < p_match, y[:, :D], rnd).astype(np.int32)
+
+
+# --------------------------------------------------------------------------- greedy verify
+GREEDY_CASES = list(itertools.product(
+    [1, 2, 3, 7, 9, 31, 1000, 1001, 4099, 32000], [0, 1, 3, 16], ["f32", "bf16"], [None, "ties"]))
+
+
+def test_greedy_verify_fuzz(sv):
+    rng = np.random.default_rng(100)
+    for i, (V, D, dt, sp) in enumerate(GREEDY_CASES):
+        B = 5
+        log(f"greedy fuzz {i}: V={V} D={D} dtype={dt} special={sp}")
+        c = fuzz_case(i, B, D, V, dt, special=sp)
+        x = greedy_drafts(rng, c["logits"], dt, D)
+        ref = oracle.greedy_verify(c["logits"], dt, x)
+        z = dev_logits(c["logits"], dt)
+        acc, acc_full = guarded_i32((B, D + 1))
+        out = sv.greedy_verify(z, dev(x), argmax=True, out={"accepted_tokens": acc})
+        for k in ("accepted_tokens", "accept_length", "predict", "accept_index", "argmax"):
+            assert np.array_equal(np_i(out[k]), ref[k]), (k, V, D, dt, sp, np_i(out[k]), ref[k])
+        assert guard_intact(acc_full, B * (D + 1))
+        # without argmax: rows after the first mismatch are skipped, same results
+        out2 = sv.greedy_verify(z, dev(x))
+        for k in ("accepted_tokens", "accept_length", "predict", "accept_index"):
+            assert np.array_equal(np_i(out2[k]), ref[k]), (k, V, D, dt)
+
+
+def test_greedy_special_values(sv):
+    torch = __import__("torch")
+    rows = np.array([
+        [-0.0, 0.0, 0.0, -0.0, -1.0, -0.0, 0.0, -5.0, 0.0],        # signed zeros tie
+        [1.0, np.nan, 3.0, np.nan, 2.0, 3.0, 0.0, 1.0, 1.0],       # first NaN wins
+        [-np.inf] * 9,                                             # all -inf -> index 0
+        [2.0, 5.0, 5.0, np.inf, 1.0, np.inf, 0.0, 0.0, -np.inf],   # +inf, tie
+        [3.0, 3.0, 3.0, 3.0, 3.0, 3.0, 3.0, 3.0, 3.0],
+        [-1.0, -2.0, -3.0, -4.0, -5.0, -6.0, -7.0, -8.0, -0.5],
+    ], dtype=np.float32)
+    from workloads import f32_to_bf16_bits
+    for dt in ("f32", "bf16"):
+        for V in (9, 8 * 9):
+            z = np.tile(rows, (1, V // 9))[None].astype(np.float32)      # [1, 6, V]
+            zz = f32_to_bf16_bits(z) if dt == "bf16" else z
+            log(f"greedy special values dtype={dt} V={V}")
+            ref = oracle.greedy_verify(zz, dt, np.zeros((1, 5), np.int32) - 1)
+            out = sv.greedy_verify(dev_logits(zz, dt), dev(np.zeros((1, 5), np.int32) - 1), argmax=True)
+            assert np.array_equal(np_i(out["argmax"]), ref["argmax"]), (dt, V, np_i(out["argmax"]), ref["argmax"])
+            t = torch.from_numpy(oracle.decode_logits(zz, dt)[0])
+            assert list(ref["argmax"][0]) == [int(torch.argmax(r)) for r in t]
+
+
+def test_greedy_unaligned_rows_and_offsets(sv):
+    """Rows starting at every 2/4-byte offset modulo 16 (tensor views with a storage offset)."""
+    torch = __import__("torch")
+    rng = np.random.default_rng(7)
+    for dt in ("f32", "bf16"):
+        B, D, V = 3, 2, 517
+        c = fuzz_case(55, B, D, V, dt, special="ties")
+        x = greedy_drafts(rng, c["logits"], dt, D, 0.9)
+        ref = oracle.greedy_verify(c["logits"], dt, x)
+        z = dev_logits(c["logits"], dt).reshape(-1)
+        for shift in range(1, 8):
+            log(f"greedy unaligned dtype={dt} shift={shift}")
+            buf = torch.empty(z.numel() + 8, dtype=z.dtype, device=z.device)
+            view = buf[shift:shift + z.numel()]
+            view.copy_(z)
+            out = sv.greedy_verify(view.view(B, D + 1, V), dev(x), argmax=True)
+            assert np.array_equal(np_i(out["argmax"]), ref["argmax"])
+            assert np.array_equal(np_i(out["accepted_tokens"]), ref["accepted_tokens"])
+
+
+def test_greedy_config4_full(sv):
+    c = make_config(4)
+    log("greedy config 4 full: B=512 N=4 V=151936 bf16")
+    ref = oracle.greedy_verify(c["logits"], "bf16", c["draft_ids"])
+    out = sv.greedy_verify(dev_logits(c["logits"], "bf16"), dev(c["draft_ids"]), argmax=True)
+    for k in ("accepted_tokens", "accept_length", "predict", "accept_index", "argmax"):
+        assert np.array_equal(np_i(out[k]), ref[k]), k
+    assert np.array_equal(ref["argmax"], c["planted"])
+    out2 = sv.greedy_verify(dev_logits(c["logits"], "bf16"), dev(c["draft_ids"]))
+    assert np.array_equal(np_i(out2["accepted_tokens"]), ref["accepted_tokens"])
+
+
+# --------------------------------------------------------------------------- chain rejection
+CHAIN_CASES = (
+    [(V, D, None) for V in (1, 2, 3, 5, 31, 1000, 1001, 4097, 32000) for D in (0, 1, 3, 5)]
+    + [(V, 16, None) for V in (7, 1030)]
+    + [(V, D, sp) for sp in ("equal", "disjoint", "onehot", "zeros", "invalid_ids")
+       for V in (2, 33, 1000, 4099) for D in (1, 4)]
+)
+
+
+def test_chain_reject_fuzz(sv):
+    flagged = 0
+    for i, (V, D, sp) in enumerate(CHAIN_CASES):
+        B = 6
+        log(f"chain fuzz {i}: V={V} D={D} special={sp}")
+        c = fuzz_case(200 + i, B, D, V, "f32", special=sp)
+        ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
+        acc, acc_full = guarded_i32((B, D + 1))
+        alen, alen_full = guarded_i32((B,))
+        sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]), dev(c["seed"]),
+                        dev(c["offset"]), out=(acc, alen))
+        flagged += assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (V, D, sp))
+        assert guard_intact(acc_full, B * (D + 1)) and guard_intact(alen_full, B)
+        if sp == "equal":
+            assert np.all(np_i(alen) == D)
+        if sp == "disjoint" and V >= 2:
+            assert np.all(np_i(alen) == 0)
+    log(f"chain fuzz flagged requests: {flagged}")
+
+
+def test_chain_reject_unaligned_rows(sv):
+    torch = __import__("torch")
+    B, D, V = 4, 3, 1003
+    c = fuzz_case(77, B, D, V, "f32")
+    ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
+    for shift in (1, 2, 3):
+        log(f"chain unaligned shift={shift}")
+        p = torch.empty(B * (D + 1) * V + 4, device="cuda")[shift:shift + B * (D + 1) * V]
+        q = torch.empty(B * D * V + 4, device="cuda")[shift:shift + B * D * V]
+        p.copy_(dev(c["target_probs"]).reshape(-1))
+        q.copy_(dev(c["draft_probs"]).reshape(-1))
+        acc, alen = sv.chain_reject(q.view(B, D, V), dev(c["draft_ids"]), p.view(B, D + 1, V), dev(c["seed"]),
+                                    dev(c["offset"]))
+        assert_chain_match(np_i(acc), np_i(alen), ref, range(B), ("unaligned", shift))
+
+
+def test_chain_reject_request_subset_and_determinism(sv):
+    B, D, V = 9, 4, 3001
+    c = fuzz_case(91, B, D, V, "f32")
+    args = [dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]), dev(c["seed"]), dev(c["offset"])]
+    log("chain subset/determinism")
+    acc1, len1 = sv.chain_reject(*args)
+    acc2, len2 = sv.chain_reject(*args)
+    assert np.array_equal(np_i(acc1), np_i(acc2)) and np.array_equal(np_i(len1), np_i(len2))
+    reqs = np.array([7, 2, 5], np.int32)
+    acc3, acc3_full = guarded_i32((B, D + 1))
+    acc3.fill_(SENTINEL)
+    len3, _ = guarded_i32((B,))
+    len3.fill_(SENTINEL)
+    sv.chain_reject(*args, req_index=dev(reqs), out=(acc3, len3))
+    a3, l3 = np_i(acc3), np_i(len3)
+    for b in range(B):
+        if b in reqs:
+            assert np.array_equal(a3[b], np_i(acc1)[b]) and l3[b] == np_i(len1)[b]
+        else:
+            assert np.all(a3[b] == SENTINEL) and l3[b] == SENTINEL
+    # a request's draws follow its own (seed, offset), not its batch position
+    perm = np.array([3, 0, 8, 1, 6, 2, 5, 7, 4])
+    pargs = [dev(c["draft_probs"][perm]), dev(c["draft_ids"][perm]), dev(c["target_probs"][perm]),
+             dev(c["seed"][perm]), dev(c["offset"][perm])]
+    acc4, len4 = sv.chain_reject(*pargs)
+    assert np.array_equal(np_i(acc4), np_i(acc1)[perm]) and np.array_equal(np_i(len4), np_i(len1)[perm])
+
+
+def test_chain_reject_config3_full(sv):
+    c = make_config(3)
+    B, D, V = 256, 5, 128256
+    log("chain config 3 full: B=256 D=5 V=128256 f32")
+    ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
+    acc, alen = sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]),
+                                dev(c["seed"]), dev(c["offset"]))
+    flagged = assert_chain_match(np_i(acc), np_i(alen), ref, range(B), "cfg3")
+    L = np_i(alen)
+    log(f"config 3: mean L={L.mean():.3f} P(L=D)={np.mean(L == D):.3f} flagged={flagged}")
+    assert 2.0 < L.mean() < 4.5
+
+
+# --------------------------------------------------------------------------- softmax + top-k/top-p
+SOFTMAX_CASES = [
+    (V, dt, T, k, p)
+    for V in (1, 7, 100, 1001, 32000)
+    for dt in ("f32", "bf16")
+    for (T, k, p) in ((1.0, 0, 1.0), (0.7, 50, 0.9), (0.0, 0, 1.0), (1.3, 5, 1.0), (0.5, 0, 0.8),
+                      (0.9, 1, 0.5), (1.1, V - 1, 0.95), (0.8, V, 0.3), (2.0, 0, 0.0), (0.6, 3, 0.99))
+]
+
+
+def assert_probs_match(gpu, ref, flags, ctx):
+    ok_rows = ~flags
+    g, r = gpu[ok_rows], ref[ok_rows]
+    err = np.abs(g - r).max() if g.size else 0.0
+    assert err <= PROB_ATOL, (ctx, err)
+    # kept sets: zero exactly where the oracle is zero; non-zero where the oracle is not negligible
+    assert np.all(g[r == 0] == 0), ctx
+    assert np.all(g[r > 1e-30] > 0), ctx
+    return int(flags.sum())
+
+
+def test_softmax_renorm_fuzz(sv):
+    flagged = 0
+    for i, (V, dt, T, k, p) in enumerate(SOFTMAX_CASES):
+        B, npos = 3, 2
+        c = fuzz_case(300 + i, B, npos - 1, V, dt, special="ties" if i % 3 == 0 else None)
+        Ts = np.array([T, T * 1.1 if T > 0 else 0.0, T], np.float32)
+        ks = np.array([k, k, 0], np.int32)
+        ps = np.array([p, p, p], np.float32)
+        log(f"softmax fuzz {i}: V={V} dtype={dt} T={T} k={k} top_p={p}")
+        ref, fl = oracle.softmax_renorm(c["logits"], dt, Ts, ks, ps)
+        out = sv.softmax_renorm(dev_logits(c["logits"], dt), dev(Ts), dev(ks), dev(ps))
+        flagged += assert_probs_match(out.cpu().numpy().astype(np.float64), ref, fl, (V, dt, T, k, p))
+    log(f"softmax fuzz flagged rows: {flagged}")
+
+
+def test_softmax_renorm_optional_filters_and_subset(sv):
+    torch = __import__("torch")
+    B, npos, V = 5, 3, 2000
+    c = fuzz_case(333, B, npos - 1, V, "bf16")
+    T = np.array([1.0, 0.5, 0.0, 2.0, 0.8], np.float32)
+    log("softmax without top_k/top_p arrays, and via req_index")
+    ref, fl = oracle.softmax_renorm(c["logits"], "bf16", T)
+    out = sv.softmax_renorm(dev_logits(c["logits"], "bf16"), dev(T))
+    assert_probs_match(out.cpu().numpy().astype(np.float64), ref, fl, "no filters")
+    full = torch.full((B, npos, V), -3.0, device="cuda")
+    sv.softmax_renorm(dev_logits(c["logits"], "bf16"), dev(T), req_index=dev(np.array([4, 1], np.int32)), out=full)
+    f = full.cpu().numpy()
+    assert np.array_equal(f[[4, 1]], out.cpu().numpy()[[4, 1]])
+    assert np.all(f[[0, 2, 3]] == -3.0)
+
+
+def test_softmax_then_chain_config2_full(sv):
+    c = make_config(2)
+    B, D, V = 64, 3, 32000
+    log("config 2 full: softmax_renorm(T=0.7, k=50, p=0.9) -> chain_reject, bf16 V=32000")
+    z = dev_logits(c["logits"], "bf16")
+    probs = sv.softmax_renorm(z, dev(c["temperature"]), dev(c["top_k"]), dev(c["top_p"]))
+    ref, fl = oracle.softmax_renorm(c["logits"], "bf16", c["temperature"], c["top_k"], c["top_p"])
+    g = probs.cpu().numpy()
+    n_flag = assert_probs_match(g.astype(np.float64), ref, fl, "cfg2")
+    kept = (g > 0).sum(-1)
+    log(f"config 2: kept per row mean={kept.mean():.2f} flagged rows={n_flag}")
+    acc, alen = sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), probs, dev(c["seed"]), dev(c["offset"]))
+    # stage parity: the oracle chain on the GPU's own probabilities
+    ref_c = oracle.chain_reject(c["draft_probs"], c["draft_ids"], g, c["seed"], c["offset"])
+    assert_chain_match(np_i(acc), np_i(alen), ref_c, range(B), "cfg2 stage")
+    # end to end: the oracle chain on the oracle's probabilities (near-threshold accepts flagged)
+    ref_e = oracle.chain_reject(c["draft_probs"], c["draft_ids"], ref, c["seed"], c["offset"])
+    ok = [b for b in range(B) if not fl[b].any() and ref_e["near_accept"][b] < 0]
+    assert_chain_match(np_i(acc), np_i(alen), ref_e, ok, "cfg2 end-to-end")
+    log(f"config 2: mean L={np_i(alen).mean():.3f}")
+
+
+def test_config1_end_to_end(sv):
+    c = make_config(1)
+    B, D, V = 4, 3, 1000
+    log("config 1: softmax(T=1) -> chain_reject, and greedy verify")
+    probs = sv.softmax_renorm(dev_logits(c["logits"], "f32"), dev(c["temperature"]))
+    ref, fl = oracle.softmax_renorm(c["logits"], "f32", c["temperature"])
+    assert_probs_match(probs.cpu().numpy().astype(np.float64), ref, fl, "cfg1")
+    acc, alen = sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), probs, dev(c["seed"]), dev(c["offset"]))
+    ref_c = oracle.chain_reject(c["draft_probs"], c["draft_ids"], probs.cpu().numpy(), c["seed"], c["offset"])
+    assert_chain_match(np_i(acc), np_i(alen), ref_c, range(B), "cfg1 stage")
+    g = sv.greedy_verify(dev_logits(c["logits"], "f32"), dev(c["greedy_draft_ids"]), argmax=True)
+    rg = oracle.greedy_verify(c["logits"], "f32", c["greedy_draft_ids"])
+    for k in ("accepted_tokens", "accept_length", "predict", "accept_index", "argmax"):
+        assert np.array_equal(np_i(g[k]), rg[k]), k
+
+
+# --------------------------------------------------------------------------- Gumbel-max
+GUMBEL_CASES = [(V, D, dt) for V in (1, 3, 100, 1001, 32000) for D in (0, 1, 3, 7) for dt in ("f32", "bf16")]
+
+
+def test_gumbel_sample_fuzz(sv):
+    rng = np.random.default_rng(400)
+    flagged = 0
+    for i, (V, D, dt) in enumerate(GUMBEL_CASES):
+        B = 6
+        c = fuzz_case(400 + i, B, D, V, dt)
+        T = np.array([0.7, 1.0, 0.0, 1.5, 0.3, 1e-6], np.float32)
+        log(f"gumbel fuzz {i}: V={V} D={D} dtype={dt}")
+        # drafts: the oracle's own samples with probability 0.8 so chains run deep
+        full = oracle.gumbel_sample(c["logits"], dt, T, np.zeros((B, D), np.int32), c["seed"], c["offset"],
+                                    all_rows=True)
+        x = np.where(rng.random((B, D)) < 0.8, full["sampled"][:, :D], rng.integers(0, V, size=(B, D)))
+        x = x.astype(np.int32)
+        ref = oracle.gumbel_sample(c["logits"], dt, T, x, c["seed"], c["offset"], all_rows=True)
+        out = sv.gumbel_sample(dev_logits(c["logits"], dt), dev(T), dev(x), dev(c["seed"]), dev(c["offset"]),
+                               sampled=True)
+        s_gpu = np_i(out["sampled"])
+        for b in range(B):
+            fp = int(ref["flag_pos"][b])
+            assert list(s_gpu[b, :fp]) == list(ref["sampled"][b, :fp]), (V, D, dt, b, s_gpu[b], ref["sampled"][b])
+            flagged += fp < D + 1
+        assert_chain_match(np_i(out["accepted_tokens"]), np_i(out["accept_length"]), ref, range(B), (V, D, dt))
+        out2 = sv.gumbel_sample(dev_logits(c["logits"], dt), dev(T), dev(x), dev(c["seed"]), dev(c["offset"]))
+        assert np.array_equal(np_i(out2["accepted_tokens"]), np_i(out["accepted_tokens"]))
+    log(f"gumbel fuzz flagged requests: {flagged}")
+
+
+# --------------------------------------------------------------------------- config 5 (mixed modes)
+def test_config5_mixed_modes_sampled(sv):
+    torch = __import__("torch")
+    c = make_config(5)
+    B, D, V = 1024, 7, 129280
+    N = D + 1
+    modes = c["modes"]
+    log("config 5 full launch: B=1024 D=7 V=129280 bf16, each mode via req_index")
+    z = dev_logits(c["logits"], "bf16")
+    T = dev(c["temperature"])
+    x = dev(c["draft_ids"])
+    seed, off = dev(c["seed"]), dev(c["offset"])
+    idx = {m: np.nonzero(modes == m)[0].astype(np.int32) for m in range(4)}
+    acc = torch.full((B, N), SENTINEL, dtype=torch.int32, device="cuda")
+    alen = torch.full((B,), SENTINEL, dtype=torch.int32, device="cuda")
+    sv.greedy_verify(z, x, req_index=dev(idx[MODE_GREEDY]), predict=False, accept_index=False,
+                     out={"accepted_tokens": acc, "accept_length": alen})
+    sv.gumbel_sample(z, T, x, seed, off, req_index=dev(idx[MODE_TEMPERATURE]),
+                     out={"accepted_tokens": acc, "accept_length": alen})
+    filt = np.concatenate([idx[MODE_TOPK], idx[MODE_TOPP]]).astype(np.int32)
+    probs = torch.zeros((B, N, V), dtype=torch.float32, device="cuda")
+    sv.softmax_renorm(z, T, dev(c["top_k"]), dev(c["top_p"]), req_index=dev(filt), out=probs)
+    sv.chain_reject(dev(c["draft_probs"]), x, probs, seed, off, req_index=dev(filt), out=(acc, alen))
+    A, Ls = np_i(acc), np_i(alen)
+    assert np.all((Ls >= 0) & (Ls <= D))
+    for b in range(B):
+        assert np.all(A[b, Ls[b] + 1:] == -1) and np.all(A[b, :Ls[b] + 1] >= 0)
+    rng = np.random.default_rng(5)
+    sample = {m: rng.choice(idx[m], size=6, replace=False) for m in range(4)}
+    rg = oracle.greedy_verify(c["logits"], "bf16", c["draft_ids"], requests=sample[MODE_GREEDY])
+    for b in sample[MODE_GREEDY]:
+        assert list(A[b]) == list(rg["accepted_tokens"][b]) and Ls[b] == rg["accept_length"][b]
+    ru = oracle.gumbel_sample(c["logits"], "bf16", c["temperature"], c["draft_ids"], c["seed"], c["offset"],
+                              requests=sample[MODE_TEMPERATURE])
+    assert_chain_match(A, Ls, ru, sample[MODE_TEMPERATURE], "cfg5 gumbel")
+    sreq = np.concatenate([sample[MODE_TOPK], sample[MODE_TOPP]])
+    rp, fl = oracle.softmax_renorm(c["logits"], "bf16", c["temperature"], c["top_k"], c["top_p"], requests=sreq)
+    gp = probs.cpu().numpy()
+    assert_probs_match(gp[sreq].astype(np.float64), rp, fl, "cfg5 softmax")
+    rc = oracle.chain_reject(c["draft_probs"], c["draft_ids"], gp, c["seed"], c["offset"], requests=sreq)
+    assert_chain_match(A, Ls, rc, sreq, "cfg5 chain stage")
+    for m, name in ((MODE_GREEDY, "greedy"), (MODE_TEMPERATURE, "temperature"), (MODE_TOPK, "top-k"),
+                    (MODE_TOPP, "top-p")):
+        log(f"config 5 {name}: mean L={Ls[idx[m]].mean():.3f}")

@@ -1,0 +1,262 @@
+"""specverify: speculative-decoding draft verification on MI355X (gfx950).
+
+Thin ctypes binding over ``libspecverify.so`` (C ABI declared in
+``include/specverify.h``).  This module only marshals arguments: it checks
+tensor placement, dtype and contiguity, allocates outputs with torch, and
+passes raw device pointers plus the current HIP stream.  Every step of the
+verification runs in the library's HIP kernels; there is no CPU fallback, and
+a missing library raises.
+
+Functions mirror the C entry points:
+
+* ``softmax_renorm(logits, temperature, top_k=None, top_p=None, req_index=None)``
+* ``chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None)``
+* ``greedy_verify(target_logits, draft_ids, req_index=None, ...)``
+* ``gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, ...)``
+
+``accept_length`` is the number of accepted drafts L in [0, D]; a request
+emits L + 1 tokens.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+OK, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR = 0, 1, 2, 3
+F32, BF16 = 0, 1
+MAX_DRAFT = 16
+RNG_SLOT_SPAN = 32
+
+SYMBOLS = (
+    "specverify_softmax_renorm",
+    "specverify_chain_reject",
+    "specverify_greedy_verify",
+    "specverify_gumbel_sample",
+    "specverify_status_string",
+    "specverify_last_error",
+    "specverify_version",
+)
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    """A specverify call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {message} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspecverify.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m token_sampling_temp_amd.build` "
+            "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.specverify_softmax_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp, vp]
+    L.specverify_chain_reject.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
+    L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
+    for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_greedy_verify",
+                 "specverify_gumbel_sample"):
+        getattr(L, name).restype = ctypes.c_int
+    L.specverify_status_string.argtypes = [ctypes.c_int]
+    L.specverify_status_string.restype = ctypes.c_char_p
+    L.specverify_last_error.argtypes = []
+    L.specverify_last_error.restype = ctypes.c_char_p
+    L.specverify_version.argtypes = []
+    L.specverify_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        msg = lib().specverify_last_error().decode(errors="replace")
+        raise SpecVerifyError(fn, status, msg)
+
+
+# --------------------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtypes, device=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return t
+
+
+def _logit_dtype(t):
+    torch = _torch()
+    return BF16 if t.dtype == torch.bfloat16 else F32
+
+
+def _req(req_index, B, device):
+    torch = _torch()
+    if req_index is None:
+        return None, B
+    _need(req_index, "req_index", (torch.int32,), device, 1)
+    return req_index, int(req_index.shape[0])
+
+
+def _u64(t, name, B, device):
+    torch = _torch()
+    _need(t, name, (torch.int64, torch.uint64), device, 1)
+    if t.shape[0] != B:
+        raise ValueError(f"{name} must have shape [{B}], got {tuple(t.shape)}")
+    return t
+
+
+# --------------------------------------------------------------------------- entry points
+def softmax_renorm(logits, temperature, top_k=None, top_p=None, req_index=None, out=None):
+    """Temperature softmax then top-k then top-p renormalisation: [B, npos, V] -> float32 probs."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32, torch.bfloat16), None, 3)
+    dev = logits.device
+    B, npos, V = logits.shape
+    _need(temperature, "temperature", (torch.float32,), dev, 1)
+    if top_k is not None:
+        _need(top_k, "top_k", (torch.int32,), dev, 1)
+    if top_p is not None:
+        _need(top_p, "top_p", (torch.float32,), dev, 1)
+    for name, t in (("temperature", temperature), ("top_k", top_k), ("top_p", top_p)):
+        if t is not None and t.shape[0] != B:
+            raise ValueError(f"{name} must have shape [{B}]")
+    req_index, n_req = _req(req_index, B, dev)
+    if out is None:
+        out = torch.empty((B, npos, V), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev, 3)
+        if tuple(out.shape) != (B, npos, V):
+            raise ValueError("out has the wrong shape")
+    st = lib().specverify_softmax_renorm(
+        _ptr(logits), _logit_dtype(logits), B, npos, V, _ptr(temperature), _ptr(top_k), _ptr(top_p),
+        _ptr(req_index), n_req, _ptr(out), _stream_ptr(dev))
+    _check("specverify_softmax_renorm", st)
+    return out
+
+
+def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None, out=None):
+    """Chain rejection sampling; returns (accepted_tokens [B, D+1] int32, accept_length [B] int32)."""
+    torch = _torch()
+    _need(target_probs, "target_probs", (torch.float32,), None, 3)
+    dev = target_probs.device
+    B, N, V = target_probs.shape
+    D = N - 1
+    _need(draft_probs, "draft_probs", (torch.float32,), dev, 3)
+    _need(draft_ids, "draft_ids", (torch.int32,), dev, 2)
+    if tuple(draft_probs.shape) != (B, D, V) or tuple(draft_ids.shape) != (B, D):
+        raise ValueError(f"draft_probs must be [{B},{D},{V}] and draft_ids [{B},{D}]")
+    _u64(seed, "seed", B, dev)
+    _u64(offset, "offset", B, dev)
+    req_index, n_req = _req(req_index, B, dev)
+    if out is None:
+        acc = torch.empty((B, N), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        acc, alen = out
+    st = lib().specverify_chain_reject(
+        _ptr(draft_probs), _ptr(draft_ids), _ptr(target_probs), _ptr(seed), _ptr(offset), B, D, V,
+        _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
+    _check("specverify_chain_reject", st)
+    return acc, alen
+
+
+def greedy_verify(target_logits, draft_ids, req_index=None, predict=True, accept_index=True,
+                  argmax=False, out=None):
+    """Greedy chain verify; returns a dict of int32 tensors:
+    accepted_tokens [B, N], accept_length [B], and optionally predict [B, N],
+    accept_index [B, N] (flat index into predict), argmax [B, N] (forces every row)."""
+    torch = _torch()
+    _need(target_logits, "target_logits", (torch.float32, torch.bfloat16), None, 3)
+    dev = target_logits.device
+    B, N, V = target_logits.shape
+    D = N - 1
+    _need(draft_ids, "draft_ids", (torch.int32,), dev, 2)
+    if tuple(draft_ids.shape) != (B, D):
+        raise ValueError(f"draft_ids must be [{B},{D}]")
+    req_index, n_req = _req(req_index, B, dev)
+    o = dict(out) if out is not None else {}
+
+    def mk(key, shape, want=True):
+        if not want:
+            return None
+        if key not in o:
+            o[key] = torch.empty(shape, dtype=torch.int32, device=dev)
+        return o[key]
+
+    acc = mk("accepted_tokens", (B, N))
+    alen = mk("accept_length", (B,))
+    pr = mk("predict", (B, N), predict)
+    ai = mk("accept_index", (B, N), accept_index)
+    am = mk("argmax", (B, N), argmax)
+    st = lib().specverify_greedy_verify(
+        _ptr(target_logits), _logit_dtype(target_logits), _ptr(draft_ids), B, D, V, _ptr(req_index), n_req,
+        _ptr(acc), _ptr(alen), _ptr(pr), _ptr(ai), _ptr(am), _stream_ptr(dev))
+    _check("specverify_greedy_verify", st)
+    return o
+
+
+def gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, sampled=False,
+                  out=None):
+    """Gumbel-max temperature sampling + strict acceptance; returns a dict of
+    int32 tensors accepted_tokens [B, N], accept_length [B] and optionally
+    sampled [B, N] (forces every row)."""
+    torch = _torch()
+    _need(target_logits, "target_logits", (torch.float32, torch.bfloat16), None, 3)
+    dev = target_logits.device
+    B, N, V = target_logits.shape
+    D = N - 1
+    _need(temperature, "temperature", (torch.float32,), dev, 1)
+    _need(draft_ids, "draft_ids", (torch.int32,), dev, 2)
+    if tuple(draft_ids.shape) != (B, D) or temperature.shape[0] != B:
+        raise ValueError(f"draft_ids must be [{B},{D}] and temperature [{B}]")
+    _u64(seed, "seed", B, dev)
+    _u64(offset, "offset", B, dev)
+    req_index, n_req = _req(req_index, B, dev)
+    o = dict(out) if out is not None else {}
+    for key, shape, want in (("accepted_tokens", (B, N), True), ("accept_length", (B,), True),
+                             ("sampled", (B, N), sampled)):
+        if want and key not in o:
+            o[key] = torch.empty(shape, dtype=torch.int32, device=dev)
+    st = lib().specverify_gumbel_sample(
+        _ptr(target_logits), _logit_dtype(target_logits), _ptr(temperature), _ptr(draft_ids), _ptr(seed),
+        _ptr(offset), B, D, V, _ptr(req_index), n_req, _ptr(o["accepted_tokens"]), _ptr(o["accept_length"]),
+        _ptr(o.get("sampled")), _stream_ptr(dev))
+    _check("specverify_gumbel_sample", st)
+    return o
+
+
+def version() -> int:
+    return int(lib().specverify_version())

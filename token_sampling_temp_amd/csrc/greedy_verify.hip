@@ -1,0 +1,64 @@
+// Greedy chain verify: target token y_j = lowest-index argmax of row j; the
+// accept length L counts the leading draft ids equal to y (strict acceptance).
+// One workgroup per request walks its rows in order and stops after the first
+// mismatch unless every row's argmax is requested.
+#include "sv_argmax.hpp"
+#include "sv_launch.hpp"
+
+namespace sv {
+
+constexpr int kGreedyBlock = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(kGreedyBlock) void greedy_verify_kernel(
+    const T* __restrict__ logits, const int32_t* __restrict__ draft_ids, int64_t B, int D, int64_t V,
+    const int32_t* __restrict__ req_index, int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ predict, int32_t* __restrict__ accept_index, int32_t* __restrict__ argmax_out) {
+    __shared__ ArgmaxShared<kGreedyBlock> sh;
+    __shared__ int32_t s_y[kMaxDraft + 1];
+    const int64_t b = req_index ? (int64_t)req_index[blockIdx.x] : (int64_t)blockIdx.x;
+    if (b < 0 || b >= B) return;
+    const int N = D + 1;
+    const bool all_rows = argmax_out != nullptr;
+    int L = -1;
+    int rows = 0;
+    for (int j = 0; j < N; ++j) {
+        const T* row = logits + ((int64_t)b * N + j) * V;
+        const int64_t y = row_argmax<kGreedyBlock, true>(row, V, sh);
+        if (threadIdx.x == 0) s_y[j] = (int32_t)y;
+        rows = j + 1;
+        if (L < 0 && (j == D || draft_ids[(int64_t)b * D + j] != (int32_t)y)) {
+            L = j;
+            if (!all_rows) break;
+        }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < N) {
+        const int64_t o = (int64_t)b * N + t;
+        const int32_t yt = t <= L ? s_y[t] : -1;
+        accepted[o] = yt;
+        if (predict) predict[o] = yt;
+        if (accept_index) accept_index[o] = t <= L ? (int32_t)o : -1;
+        if (argmax_out) argmax_out[o] = t < rows ? s_y[t] : -1;
+    }
+    if (t == 0) accept_len[b] = L;
+}
+
+hipError_t launch_greedy_verify(const void* logits, int dtype, const int32_t* draft_ids, int64_t B, int D,
+                                int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted,
+                                int32_t* accept_len, int32_t* predict, int32_t* accept_index,
+                                int32_t* argmax_out, hipStream_t stream) {
+    const dim3 grid((unsigned)n_req), block(kGreedyBlock);
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL(greedy_verify_kernel<uint16_t>, grid, block, 0, stream,
+                           static_cast<const uint16_t*>(logits), draft_ids, B, D, V, req_index, accepted,
+                           accept_len, predict, accept_index, argmax_out);
+    else
+        hipLaunchKernelGGL(greedy_verify_kernel<float>, grid, block, 0, stream,
+                           static_cast<const float*>(logits), draft_ids, B, D, V, req_index, accepted,
+                           accept_len, predict, accept_index, argmax_out);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,130 @@
+// Temperature-only target sampling by Gumbel-max, then strict chain
+// acceptance.  One workgroup per request walks rows j = 0..D in order and
+// stops after the first draft mismatch (unless every row is requested).
+//
+// Row j of request b: s_v = z_v / T + G_v, G_v = -ln(-ln u_v), u_v the uniform
+// of Philox word v of stream (seed_b, offset_b + 32 j); the sample is the
+// lowest-index maximum of s (float scores, packed (key, index) maximum).
+// Thread work unit = 4 consecutive vocabulary entries = one Philox block.
+#include "sv_argmax.hpp"
+#include "sv_launch.hpp"
+
+namespace sv {
+
+constexpr int kGbBlock = 1024;
+
+__device__ __forceinline__ uint64_t gumbel_key(float z, float T, uint32_t w, int64_t idx) {
+    const float u = uniform_of(w);
+    const float g = -logf(-logf(u));
+    const float s = z / T + g;
+    return pack_key_index(float_key(s), idx);
+}
+
+template <typename T>
+__device__ __forceinline__ void load_group4(const T* row, int64_t v0, int64_t V, bool aligned, float (&f)[4]);
+
+template <>
+__device__ __forceinline__ void load_group4<float>(const float* row, int64_t v0, int64_t V, bool aligned,
+                                                   float (&f)[4]) {
+    if (aligned && v0 + 3 < V) {
+        unpack(load_vec<true>(row + v0, 0), f);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = (v0 + e < V) ? row[v0 + e] : 0.0f;
+    }
+}
+
+template <>
+__device__ __forceinline__ void load_group4<uint16_t>(const uint16_t* row, int64_t v0, int64_t V, bool aligned,
+                                                      float (&f)[4]) {
+    if (aligned && v0 + 3 < V) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + v0));
+        f[0] = __uint_as_float(w.x << 16);
+        f[1] = __uint_as_float(w.x & 0xFFFF0000u);
+        f[2] = __uint_as_float(w.y << 16);
+        f[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = (v0 + e < V) ? bf16_to_float(row[v0 + e]) : 0.0f;
+    }
+}
+
+template <int BLOCK, typename T>
+__device__ int64_t row_gumbel(const T* row, int64_t V, float Tm, uint64_t seed, uint64_t subseq,
+                              ArgmaxShared<BLOCK>& sh) {
+    const bool aligned = ((uintptr_t)row % (4 * sizeof(T))) == 0;
+    const int64_t ngroups = (V + 3) / 4;
+    uint64_t best = 0;
+    for (int64_t g = threadIdx.x; g < ngroups; g += BLOCK) {
+        const int64_t v0 = g * 4;
+        float f[4];
+        load_group4<T>(row, v0, V, aligned, f);
+        const uint4 w = philox_block(seed, subseq, (uint64_t)g);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (v0 + e < V) {
+                const uint64_t k = gumbel_key(f[e], Tm, ws[e], v0 + e);
+                best = k > best ? k : best;
+            }
+        }
+    }
+    const uint64_t m = block_reduce<BLOCK>(best, OpMaxU64{}, (uint64_t)0, sh.red_u);
+    return packed_index(m);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGbBlock) void gumbel_sample_kernel(
+    const T* __restrict__ logits, const float* __restrict__ temperature, const int32_t* __restrict__ draft_ids,
+    const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
+    const int32_t* __restrict__ req_index, int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ sampled_out) {
+    __shared__ ArgmaxShared<kGbBlock> sh;
+    __shared__ int32_t s_y[kMaxDraft + 1];
+    const int64_t b = req_index ? (int64_t)req_index[blockIdx.x] : (int64_t)blockIdx.x;
+    if (b < 0 || b >= B) return;
+    const int N = D + 1;
+    const float Tm = temperature[b];
+    const bool greedy = (double)Tm < kGreedyTemperature;
+    const uint64_t sd = seed[b], off = offset[b];
+    const bool all_rows = sampled_out != nullptr;
+    int L = -1;
+    for (int j = 0; j < N; ++j) {
+        const T* row = logits + ((int64_t)b * N + j) * V;
+        const int64_t y = greedy ? row_argmax<kGbBlock, true>(row, V, sh)
+                                 : row_gumbel<kGbBlock>(row, V, Tm, sd, off + kRngSlotSpan * (uint64_t)j, sh);
+        if (threadIdx.x == 0) s_y[j] = (int32_t)y;
+        if (L < 0 && (j == D || draft_ids[(int64_t)b * D + j] != (int32_t)y)) {
+            L = j;
+            if (!all_rows) break;
+        }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < N) {
+        const int64_t o = (int64_t)b * N + t;
+        accepted[o] = t <= L ? s_y[t] : -1;
+        if (sampled_out) sampled_out[o] = s_y[t];
+    }
+    if (t == 0) accept_len[b] = L;
+}
+
+hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temperature,
+                                const int32_t* draft_ids, const uint64_t* seed, const uint64_t* offset,
+                                int64_t B, int D, int64_t V, const int32_t* req_index, int64_t n_req,
+                                int32_t* accepted, int32_t* accept_len, int32_t* sampled_out,
+                                hipStream_t stream) {
+    const dim3 grid((unsigned)n_req), block(kGbBlock);
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL(gumbel_sample_kernel<uint16_t>, grid, block, 0, stream,
+                           static_cast<const uint16_t*>(logits), temperature, draft_ids, seed, offset, B, D, V,
+                           req_index, accepted, accept_len, sampled_out);
+    else
+        hipLaunchKernelGGL(gumbel_sample_kernel<float>, grid, block, 0, stream,
+                           static_cast<const float*>(logits), temperature, draft_ids, seed, offset, B, D, V,
+                           req_index, accepted, accept_len, sampled_out);
+    return hipGetLastError();
+}
+
+}  // namespace sv

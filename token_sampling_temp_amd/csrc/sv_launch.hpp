@@ -1,0 +1,35 @@
+// Host-side launchers of the verification kernels (called by the C ABI layer
+// after argument validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+constexpr int kMaxDraft = 16;
+
+hipError_t launch_greedy_verify(const void* logits, int dtype, const int32_t* draft_ids, int64_t B, int D,
+                                int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted,
+                                int32_t* accept_len, int32_t* predict, int32_t* accept_index,
+                                int32_t* argmax_out, hipStream_t stream);
+
+hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
+                               const uint64_t* seed, const uint64_t* offset, int64_t B, int D, int64_t V,
+                               const int32_t* req_index, int64_t n_req, int32_t* accepted,
+                               int32_t* accept_len, hipStream_t stream);
+
+hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t npos, int64_t V,
+                                 const float* temperature, const int32_t* top_k, const float* top_p,
+                                 const int32_t* req_index, int64_t n_req, float* probs_out,
+                                 hipStream_t stream);
+
+hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temperature,
+                                const int32_t* draft_ids, const uint64_t* seed, const uint64_t* offset,
+                                int64_t B, int D, int64_t V, const int32_t* req_index, int64_t n_req,
+                                int32_t* accepted, int32_t* accept_len, int32_t* sampled_out,
+                                hipStream_t stream);
+
+}  // namespace sv

@@ -1,7 +1,9 @@
 """Seeded generators for the five verification workloads and for fuzz shapes.
 
 Every array is produced from ``numpy.random.Generator(PCG64(SeedSequence([cfg,
-replica])))`` in a fixed order, so a (cfg, replica) pair names one input set.
+replica])))`` in a fixed order (workloads 3 and 5 draw each request's rows from
+its own stream ``SeedSequence([cfg, replica, b])``, so requests can be
+generated in parallel), so a (cfg, replica) pair names one input set.
 Logits are drawn in float32 and stored as float32 or as bfloat16 bit patterns
 (uint16, round-to-nearest-even from float32).  Draft token ids are drawn from
 the draft distribution by inverse CDF on float64 weights with the data RNG; this
@@ -140,13 +142,17 @@ def _cfg3(rng, replica, B=256):
     q = np.empty((B, D, V), np.float32)
     x = np.empty((B, D), np.int32)
     base = np.arange(V)
-    for b in range(B):
-        perms = rng.permuted(np.broadcast_to(base, (D + 1, V)), axis=1)
+
+    def one(b):
+        r = _request_rng(3, replica, b)
+        perms = r.permuted(np.broadcast_to(base, (D + 1, V)), axis=1)
         pb = zipf[perms]
         p[b] = pb
-        qb = _normalised(pb[:D] * np.exp(rng.standard_normal((D, V)) * 0.4))
+        qb = _normalised(pb[:D] * np.exp(r.standard_normal((D, V)) * 0.4))
         q[b] = qb
-        x[b] = _draw_from_rows(rng, qb)
+        x[b] = _draw_from_rows(r, qb)
+
+    _parallel_rows(B, one)
     return dict(
         dtype="f32", target_probs=p, draft_probs=q, draft_ids=x,
         temperature=np.ones(B, np.float32),
@@ -179,6 +185,19 @@ def _cfg4(rng, replica, B=512):
     return dict(dtype="bf16", logits=zb, draft_ids=x, planted=pos)
 
 
+def _request_rng(cfg: int, replica: int, b: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg, replica, b])))
+
+
+def _parallel_rows(n: int, fn, threads: int | None = None):
+    """Run fn(b) for b in range(n) on a thread pool (numpy releases the GIL)."""
+    import concurrent.futures
+    import os
+    threads = threads or min(16, os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fn, range(n)))
+
+
 def _cfg5(rng, replica, B=1024):
     D, V = 7, 129280
     N = D + 1
@@ -193,19 +212,27 @@ def _cfg5(rng, replica, B=1024):
     zb = np.empty((B, N, V), np.uint16)
     q = np.zeros((B, D, V), np.float32)
     x = np.empty((B, D), np.int32)
-    for b in range(B):
-        z = rng.standard_normal((N, V), dtype=np.float32) * np.float32(2.5)
+
+    def one(b):
+        r = _request_rng(5, replica, b)
+        z = r.standard_normal((N, V), dtype=np.float32)
+        z *= np.float32(2.5)
         zb[b] = f32_to_bf16_bits(z)
-        zd = bf16_bits_to_f32(zb[b]).astype(np.float64)
+        zd = bf16_bits_to_f32(zb[b])
         if modes[b] == MODE_GREEDY:
             am = np.argmax(zd[:D], axis=-1)
-            keep = rng.random(D) < 0.8
-            x[b] = np.where(keep, am, rng.integers(0, V, size=D))
+            keep = r.random(D) < 0.8
+            x[b] = np.where(keep, am, r.integers(0, V, size=D))
         else:
-            w = _exp_weights((zd[:D] + rng.standard_normal((D, V)) * 0.3) / float(T[b]))
-            qb = _normalised(w)
-            q[b] = qb
-            x[b] = _draw_from_rows(rng, qb)
+            a = zd[:D] + r.standard_normal((D, V), dtype=np.float32) * np.float32(0.3)
+            a *= np.float32(1.0 / float(T[b]))
+            a -= a.max(axis=-1, keepdims=True)
+            w = np.exp(a)
+            w /= w.sum(axis=-1, keepdims=True, dtype=np.float64).astype(np.float32)
+            q[b] = w
+            x[b] = _draw_from_rows(r, w.astype(np.float64))
+
+    _parallel_rows(B, one)
     return dict(
         dtype="bf16", logits=zb, temperature=T, top_k=top_k, top_p=top_p, modes=modes,
         draft_probs=q, draft_ids=x,
