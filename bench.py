@@ -54,7 +54,21 @@ def parse():
                     choices=["large_vocab_chain_reject", "topk_topp_chain", "greedy"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB -> 1 GiB elementwise copy 5 times (HBM counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 2**28 floats read and written per launch."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": 4 << 28,
+                      "copy_calibration_bytes_written_per_launch": 4 << 28, "launches": 5}), flush=True)
 
 
 # --------------------------------------------------------------------------- device helpers
@@ -297,6 +311,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import token_sampling_temp_amd as sv
     sv.lib()
     dev = torch.device("cuda:0")

@@ -5,7 +5,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "specverify.h"
 #include "sv_launch.hpp"
@@ -93,6 +98,53 @@ int check_dtype(const char* fn, int dtype) {
         if (_s != SPECVERIFY_OK) return _s; \
     } while (0)
 
+// Chain-rejection workspace, one per (device, stream) so that calls on
+// different streams never share counters.  Allocated on first use and grown
+// geometrically; a replaced buffer is kept (a queued kernel may still use it)
+// until process exit.  The counter region is zeroed once; every kernel leaves
+// its counters at zero.
+struct ChainWorkspace {
+    char* ptr = nullptr;
+    int64_t cap_req = 0;         // counters available
+    int64_t cap_partial = 0;     // doubles available
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, void*>, ChainWorkspace> g_ws;
+std::vector<void*> g_ws_retired;
+
+int64_t counter_region(int64_t cap_req) { return ((cap_req * 4 + 255) / 256) * 256; }
+
+int chain_workspace(const char* fn, hipStream_t stream, int64_t n_req, int64_t V, uint32_t** counter,
+                    double** partial) {
+    const int64_t need_partial = n_req * sv::chain_partials_per_request(V);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SPECVERIFY_HIP_ERROR, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    ChainWorkspace& w = g_ws[{dev, static_cast<void*>(stream)}];
+    if (!w.ptr || n_req > w.cap_req || need_partial > w.cap_partial) {
+        const int64_t cap_req = std::max<int64_t>(n_req, 2 * w.cap_req);
+        const int64_t cap_partial = std::max<int64_t>(need_partial, 2 * w.cap_partial);
+        const size_t bytes = (size_t)(counter_region(cap_req) + cap_partial * 8);
+        void* ptr = nullptr;
+        e = hipMalloc(&ptr, bytes);
+        if (e != hipSuccess)
+            return fail(SPECVERIFY_HIP_ERROR, "%s: workspace hipMalloc(%zu): %s", fn, bytes, hipGetErrorString(e));
+        e = hipMemsetAsync(ptr, 0, (size_t)counter_region(cap_req), stream);
+        if (e != hipSuccess) {
+            (void)hipFree(ptr);
+            return fail(SPECVERIFY_HIP_ERROR, "%s: workspace hipMemsetAsync: %s", fn, hipGetErrorString(e));
+        }
+        if (w.ptr) g_ws_retired.push_back(w.ptr);
+        w.ptr = static_cast<char*>(ptr);
+        w.cap_req = cap_req;
+        w.cap_partial = cap_partial;
+    }
+    *counter = reinterpret_cast<uint32_t*>(w.ptr);
+    *partial = reinterpret_cast<double*>(w.ptr + counter_region(w.cap_req));
+    return SPECVERIFY_OK;
+}
+
 int launched(const char* fn, hipError_t e) {
     if (e != hipSuccess) return fail(SPECVERIFY_HIP_ERROR, "%s: launch failed: %s", fn, hipGetErrorString(e));
     g_last_error.clear();
@@ -138,8 +190,11 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids, 
     SV_REQUIRE(accepted_tokens, "accepted_tokens");
     SV_REQUIRE(accept_length, "accept_length");
     SV_TRY(check_device());
+    uint32_t* counter = nullptr;
+    double* partial = nullptr;
+    SV_TRY(chain_workspace(fn, static_cast<hipStream_t>(stream), n_req, V, &counter, &partial));
     return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, seed, offset, B, (int)D, V,
-                                                req_index, n_req, accepted_tokens, accept_length,
+                                                req_index, n_req, accepted_tokens, accept_length, counter, partial,
                                                 static_cast<hipStream_t>(stream)));
 }
 

@@ -16,10 +16,14 @@ hipError_t launch_greedy_verify(const void* logits, int dtype, const int32_t* dr
                                 int32_t* accept_len, int32_t* predict, int32_t* accept_index,
                                 int32_t* argmax_out, hipStream_t stream);
 
+// Chain rejection needs a workspace: n_req uint32 counters that are zero
+// between calls (the kernel resets them) and n_req * chain_partials_per_request(V)
+// doubles of partial sums.
+int64_t chain_partials_per_request(int64_t V);
 hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
                                const uint64_t* seed, const uint64_t* offset, int64_t B, int D, int64_t V,
-                               const int32_t* req_index, int64_t n_req, int32_t* accepted,
-                               int32_t* accept_len, hipStream_t stream);
+                               const int32_t* req_index, int64_t n_req, int32_t* accepted, int32_t* accept_len,
+                               uint32_t* counter, double* partial, hipStream_t stream);
 
 hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t npos, int64_t V,
                                  const float* temperature, const int32_t* top_k, const float* top_p,
