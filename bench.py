@@ -15,7 +15,9 @@ call's rows.  Timing uses HIP events on the stream the kernels run on.
 
 Other workloads (``--workload``) exist for profiling: ``topk_topp_chain``
 (softmax_renorm -> chain_reject, B=64 D=3 V=32000 bf16), ``greedy`` (greedy
-verify, B=512 N=4 V=151936 bf16).
+verify, B=512 N=4 V=151936 bf16) and ``mixed`` (B=1024 D=7 V=129280 bf16: 256
+requests each greedy, temperature-only (Gumbel), top-k and top-p, every mode
+dispatched through req_index; per-call times are reported).
 
 The CPU baseline is the numpy oracle timed on this host on the same inputs
 (whole batches repeated for --cpu-seconds), single threaded.
@@ -51,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large_vocab_chain_reject",
-                    choices=["large_vocab_chain_reject", "topk_topp_chain", "greedy"])
+                    choices=["large_vocab_chain_reject", "topk_topp_chain", "greedy", "mixed"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -260,16 +262,31 @@ class TopkToppWorkload:
         self.alen = torch.empty((self.B,), dtype=torch.int32, device=dev)
         self.rows = self.B * N
 
-    def step(self, i):
+        self.calls = {"softmax_renorm": self.softmax, "chain_reject": self.chain}
+
+    def softmax(self, i):
         r = self.reps[i % self.R]
-        pr = self.probs[i % self.R]
-        self.sv.softmax_renorm(r["z"], r["T"], r["k"], r["p"], out=pr)
-        self.sv.chain_reject(r["q"], r["x"], pr, r["seed"], r["off"], out=(self.acc, self.alen))
+        self.sv.softmax_renorm(r["z"], r["T"], r["k"], r["p"], out=self.probs[i % self.R])
+
+    def chain(self, i):
+        r = self.reps[i % self.R]
+        self.sv.chain_reject(r["q"], r["x"], self.probs[i % self.R], r["seed"], r["off"], out=(self.acc, self.alen))
+
+    def step(self, i):
+        self.softmax(i)
+        self.chain(i)
 
     def algorithmic_bytes(self):
         # softmax_renorm: read bf16 logits, write float32 probabilities (every row)
         N = self.D + 1
-        return float(self.B * N * self.V * (2 + 4))
+        self.step(0)
+        L = self.alen.cpu().numpy().astype(np.int64)
+        self.bytes_by_call = {
+            "softmax_renorm": float(self.B * N * self.V * (2 + 4)),
+            "chain_reject": float((np.where(L < self.D, 8 * self.V, 4 * self.V)
+                                   + 2 * PROBE_GRANULE * np.minimum(L + 1, self.D)).sum()),
+        }
+        return self.bytes_by_call["softmax_renorm"]
 
     def extra(self):
         return {}
@@ -299,7 +316,150 @@ class TopkToppWorkload:
                 "sample": f"{n} requests, {el:.1f}s single-threaded numpy"}
 
 
-WORKLOADS = {c.name: c for c in (ChainWorkload, GreedyWorkload, TopkToppWorkload)}
+class MixedWorkload:
+    """B=1024 D=7 V=129280 bf16 logits, 256 requests per mode, each mode through req_index."""
+    name = "mixed"
+    kernel = "softmax_renorm_kernel"
+    sources = ("softmax_renorm.hip", "sv_argmax.hpp", "sv_common.hpp")
+    counters = "softmax_renorm_mixed_counters.txt"
+    dtype = "bf16"
+
+    def __init__(self, dev, replicas):
+        from workloads import MODE_GREEDY, MODE_TEMPERATURE, MODE_TOPK, MODE_TOPP, make_config
+        import torch
+        import token_sampling_temp_amd as sv
+        self.sv = sv
+        t0 = time.time()
+        h = make_config(5)
+        log(f"generated inputs in {time.time() - t0:.1f}s")
+        self.host = h
+        self.B, self.D, self.V = h["B"], h["D"], h["V"]
+        N = self.D + 1
+        self.R = 1
+        self.z = _bf16(h["logits"], dev)
+        self.q = _t(h["draft_probs"], dev)
+        self.x = _t(h["draft_ids"], dev)
+        self.T = _t(h["temperature"], dev)
+        self.k = _t(h["top_k"], dev)
+        self.p = _t(h["top_p"], dev)
+        self.seed = _t(h["seed"], dev)
+        self.off = _t(h["offset"], dev)
+        modes = h["modes"]
+        self.idx_host = {m: np.nonzero(modes == m)[0].astype(np.int32) for m in range(4)}
+        self.greedy_idx = _t(self.idx_host[MODE_GREEDY], dev)
+        self.temp_idx = _t(self.idx_host[MODE_TEMPERATURE], dev)
+        filt = np.concatenate([self.idx_host[MODE_TOPK], self.idx_host[MODE_TOPP]]).astype(np.int32)
+        self.filt_host = filt
+        self.filt_idx = _t(filt, dev)
+        self.probs = torch.zeros((self.B, N, self.V), dtype=torch.float32, device=dev)
+        self.acc = torch.empty((self.B, N), dtype=torch.int32, device=dev)
+        self.alen = torch.empty((self.B,), dtype=torch.int32, device=dev)
+        self.out = {"accepted_tokens": self.acc, "accept_length": self.alen}
+        self.rows = self.B * N
+        self.calls = {"greedy_verify": self.greedy, "gumbel_sample": self.gumbel,
+                      "softmax_renorm": self.softmax, "chain_reject": self.chain}
+
+    def greedy(self, i=0):
+        self.sv.greedy_verify(self.z, self.x, req_index=self.greedy_idx, predict=False, accept_index=False,
+                              out=self.out)
+
+    def gumbel(self, i=0):
+        self.sv.gumbel_sample(self.z, self.T, self.x, self.seed, self.off, req_index=self.temp_idx, out=self.out)
+
+    def softmax(self, i=0):
+        self.sv.softmax_renorm(self.z, self.T, self.k, self.p, req_index=self.filt_idx, out=self.probs)
+
+    def chain(self, i=0):
+        self.sv.chain_reject(self.q, self.x, self.probs, self.seed, self.off, req_index=self.filt_idx,
+                             out=(self.acc, self.alen))
+
+    def step(self, i):
+        self.greedy(i)
+        self.gumbel(i)
+        self.softmax(i)
+        self.chain(i)
+
+    def algorithmic_bytes(self):
+        from workloads import MODE_GREEDY, MODE_TEMPERATURE
+        self.step(0)
+        L = self.alen.cpu().numpy().astype(np.int64)
+        self.L = L
+        D, V, N = self.D, self.V, self.D + 1
+        g = self.idx_host[MODE_GREEDY]
+        t = self.idx_host[MODE_TEMPERATURE]
+        f = self.filt_host
+        self.bytes_by_call = {
+            "greedy_verify": float(((L[g] + 1) * V * 2).sum()),
+            "gumbel_sample": float(((L[t] + 1) * V * 2).sum()),
+            "softmax_renorm": float(f.size * N * V * (2 + 4)),
+            "chain_reject": float((np.where(L[f] < D, 8 * V, 4 * V) + 2 * PROBE_GRANULE * np.minimum(L[f] + 1, D)).sum()),
+        }
+        return self.bytes_by_call["softmax_renorm"]
+
+    def extra(self):
+        from workloads import MODE_GREEDY, MODE_TEMPERATURE, MODE_TOPK, MODE_TOPP
+        return {"mean_accept_length_by_mode": {
+            name: round(float(self.L[self.idx_host[m]].mean()), 4)
+            for m, name in ((MODE_GREEDY, "greedy"), (MODE_TEMPERATURE, "temperature"), (MODE_TOPK, "top_k"),
+                            (MODE_TOPP, "top_p"))}}
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "draft_tokens": self.D, "vocab": self.V,
+                "input": "bf16 logits; float32 draft probabilities", "modes": "256 greedy / 256 temperature / "
+                "256 top-k / 256 top-p", "replicas": self.R}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, n = 0, time.perf_counter(), 0
+        order = np.random.default_rng(0).permutation(self.B)
+        while True:
+            b = int(order[n % self.B])
+            if h["modes"][b] == 0:
+                oracle.greedy_verify(h["logits"], "bf16", h["draft_ids"], requests=[b])
+            elif h["modes"][b] == 1:
+                oracle.gumbel_sample(h["logits"], "bf16", h["temperature"], h["draft_ids"], h["seed"], h["offset"],
+                                     requests=[b])
+            else:
+                probs, _ = oracle.softmax_renorm(h["logits"], "bf16", h["temperature"], h["top_k"], h["top_p"],
+                                                 requests=[b])
+                one = slice(b, b + 1)
+                oracle.chain_reject(h["draft_probs"][one], h["draft_ids"][one], probs, h["seed"][one],
+                                    h["offset"][one])
+            rows += self.D + 1
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} requests (random order over all modes), {el:.1f}s single-threaded numpy"}
+
+
+WORKLOADS = {c.name: c for c in (ChainWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload)}
+
+
+def per_call_times(wl, steps):
+    """Average time of each call type of a multi-call step (each timed alone)."""
+    import torch
+    out = {}
+    for name, fn in getattr(wl, "calls", {}).items():
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(steps):
+            fn(i)
+        e.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) / steps * 1e3
+        entry = {"us": round(us, 2)}
+        b = getattr(wl, "bytes_by_call", {}).get(name)
+        if b is not None:
+            entry["algorithmic_GBps"] = round(b / (us * 1e-6) / 1e9, 1)
+            entry["frac_of_peak"] = round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        out[name] = entry
+    return out
 
 
 def main():
@@ -334,6 +494,7 @@ def main():
     log(f"timed {args.steps} steps: {ms * 1e3:.2f} us/step")
     rows_per_s = wl.rows / (ms * 1e-3)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
+    calls = per_call_times(wl, max(5, args.steps // 4)) if hasattr(wl, "calls") else None
     digest = _source_digest(*wl.sources)
     traffic = load_traffic(wl.counters, digest)
     cpu = None
@@ -359,6 +520,13 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes, "kernel_source_digest": digest},
         "cpu_baseline": cpu,
     }
+    if calls:
+        out["per_call"] = calls
+        dom = calls.get(wl.kernel.replace("_kernel", ""))
+        if dom:   # the dominant kernel timed on its own
+            us = dom["us"]
+            out["roofline"]["achieved"] = alg_bytes / (us * 1e-6) / 1e9
+            out["roofline"]["frac"] = out["roofline"]["achieved"] / PEAK_HBM_GBS
     out.update(wl.extra())
     print(json.dumps(out), flush=True)
 
