@@ -255,6 +255,37 @@ def test_softmax_renorm_fuzz(sv):
     log(f"softmax fuzz flagged rows: {flagged}")
 
 
+# bf16 rows held in registers: every register-count variant, unaligned rows,
+# a row whose most common value overflows a 16-bit histogram counter (redone by
+# the streamed algorithm), a key span too wide for the probability table, and
+# signed zeros at a top-k threshold.
+RR_CASES = [
+    (8193, None, ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 0, 0.6), (0.0, 0, 1.0))),
+    (40000, "ties", ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 7, 0.6), (0.0, 0, 1.0))),
+    (100003, None, ((1.0, 0, 1.0), (0.8, 20, 0.95), (1.2, 0, 0.8), (0.0, 0, 1.0))),
+    (129280, None, ((0.7, 0, 1.0), (0.8, 100, 1.0), (1.1, 0, 0.9), (0.9, 50, 0.5))),
+    (150001, None, ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 0, 0.6), (0.0, 0, 1.0))),
+    (80000, "mostly_zero", ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.0, 20000, 1.0), (1.2, 0, 0.3))),
+    (140000, "mostly_zero", ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.0, 20000, 0.99), (0.0, 0, 1.0))),
+    (50000, "wide", ((3e3, 0, 1.0), (1e4, 500, 0.9), (5e4, 0, 0.7), (2e3, 0, 1.0))),
+    (20000, "signed_zeros", ((1.0, 7000, 1.0), (0.5, 7000, 0.9), (2.0, 0, 0.5), (0.0, 0, 1.0))),
+]
+
+
+def test_softmax_register_resident_paths(sv):
+    flagged = 0
+    for i, (V, special, modes) in enumerate(RR_CASES):
+        c = fuzz_case(700 + i, 4, 1, V, "bf16", special=special)
+        Ts = np.array([m[0] for m in modes], np.float32)
+        ks = np.array([m[1] for m in modes], np.int32)
+        ps = np.array([m[2] for m in modes], np.float32)
+        log(f"register-resident softmax {i}: V={V} special={special}")
+        ref, fl = oracle.softmax_renorm(c["logits"], "bf16", Ts, ks, ps)
+        out = sv.softmax_renorm(dev_logits(c["logits"], "bf16"), dev(Ts), dev(ks), dev(ps))
+        flagged += assert_probs_match(out.cpu().numpy().astype(np.float64), ref, fl, (V, special))
+    log(f"register-resident softmax flagged rows: {flagged}")
+
+
 def test_softmax_renorm_optional_filters_and_subset(sv):
     torch = __import__("torch")
     B, npos, V = 5, 3, 2000

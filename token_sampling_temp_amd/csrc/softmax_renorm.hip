@@ -187,18 +187,10 @@ __device__ uint32_t radix_mass_key(const T* row, int64_t V, uint32_t kmin, float
     return prefix;
 }
 
+// One row streamed from global memory (every pass re-reads it).
 template <typename T>
-__global__ __launch_bounds__(kSmBlock) void softmax_renorm_kernel(
-    const T* __restrict__ logits, int64_t B, int npos, int64_t V, const float* __restrict__ temperature,
-    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, const int32_t* __restrict__ req_index,
-    float* __restrict__ out) {
-    __shared__ SmShared sh;
-    const int64_t b = req_index ? (int64_t)req_index[blockIdx.x] : (int64_t)blockIdx.x;
-    if (b < 0 || b >= B) return;
-    const int64_t r = (int64_t)b * npos + blockIdx.y;
-    const T* row = logits + r * V;
-    float* orow = out + r * V;
-    const float Tm = temperature[b];
+__device__ __forceinline__ void softmax_row_streamed(const T* __restrict__ row, float* __restrict__ orow, int64_t V,
+                                                     float Tm, int32_t k, float tp, SmShared& sh) {
     const int tid = threadIdx.x;
 
     if ((double)Tm < kGreedyTemperature) {
@@ -206,8 +198,6 @@ __global__ __launch_bounds__(kSmBlock) void softmax_renorm_kernel(
         for (int64_t i = tid; i < V; i += kSmBlock) orow[i] = (i == y) ? 1.0f : 0.0f;
         return;
     }
-    const int32_t k = top_k ? top_k[b] : 0;
-    const float tp = top_p ? top_p[b] : 1.0f;
 
     float lm = -INFINITY;
     row_foreach<kSmBlock, false>(row, V, [&](float v, int64_t) { lm = fmaxf(lm, v); });
@@ -243,26 +233,52 @@ __global__ __launch_bounds__(kSmBlock) void softmax_renorm_kernel(
     }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kSmBlock) void softmax_renorm_kernel(
+    const T* __restrict__ logits, int64_t B, int npos, int64_t V, const float* __restrict__ temperature,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, const int32_t* __restrict__ req_index,
+    float* __restrict__ out) {
+    __shared__ SmShared sh;
+    const int64_t b = req_index ? (int64_t)req_index[blockIdx.x] : (int64_t)blockIdx.x;
+    if (b < 0 || b >= B) return;
+    const int64_t r = (int64_t)b * npos + blockIdx.y;
+    softmax_row_streamed<T>(logits + r * V, out + r * V, V, temperature[b], top_k ? top_k[b] : 0,
+                            top_p ? top_p[b] : 1.0f, sh);
+}
+
 // ============================================================================
 // Register-resident variant for bf16 rows (V <= 1024 * 8 * NV): the row is
-// read from HBM once into registers (8*NV bf16 per thread, packed in pairs),
-// every selection pass runs over registers, and the output is written with
-// 16-byte stores.  Radix histograms are privatised 16 ways in LDS (lane & 15
-// picks the copy), so lanes of a wave that hit one digit rarely collide on one
-// address.  Top-p masses are 64-bit fixed point built exactly from the float
-// bits of w = exp2((z - m) * log2(e) / T) (floor to 2^-qs), so every sum is an
-// order-independent integer sum.
+// read from HBM once into registers as 16-bit order-preserving keys (8*NV
+// per thread, packed in pairs) and the output is written with 16-byte stores.
+//
+// Selection never touches the elements twice: one pass builds an LDS
+// histogram of all 65536 keys (16-bit counters, two per dword), and every
+// later step works on that histogram.  The weight of an element depends only
+// on its key, so a bin's count times its weight gives the bin's mass; top-k
+// and top-p are the same two-level (8-bit digit) radix selection as in the
+// streamed kernel, with the per-digit counts and 64-bit fixed-point masses
+// summed from the histogram instead of from the elements.  Fixed-point masses
+// are floor(w * 2^qs) built exactly from the float bits of
+// w = exp2((z - m) * log2(e) / T), so every sum is an order-independent
+// integer sum.  The output pass reads each element's probability from a
+// per-key table built in the same LDS once the histogram is no longer needed.
+//
+// A row in which one key occurs 65536 times or more overflows its 16-bit
+// counter; the sum of all counters then falls short of the element count, and
+// the row is redone by the streamed algorithm.
 // ============================================================================
 constexpr int kRrBlock = 1024;
-constexpr int kCopies = 16;
+constexpr int kKeys = 65536;
+constexpr int kHistWords = kKeys / 2;     // 16-bit counters, two per dword
+constexpr int kLutMax = kHistWords - 1;   // probability-table entries (slot 0 holds 0)
 
 // Keep the scheduler from interleaving the per-vector work of a fully
 // unrolled pass (which would keep every element's temporaries live at once).
 #define SV_VEC_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Make the register-resident row opaque to the optimiser at the start of a
-// pass, so values derived from it in one pass (unpacked halves, keys) are
-// recomputed instead of being kept live across passes.
+// pass, so values derived from it in one pass are recomputed instead of being
+// kept live across passes.
 template <int NV>
 __device__ __forceinline__ void launder(u32x4 (&w)[NV]) {
 #pragma unroll
@@ -270,11 +286,13 @@ __device__ __forceinline__ void launder(u32x4 (&w)[NV]) {
 }
 
 struct RrShared {
-    uint32_t hc[256 * kCopies];
-    unsigned long long hm[256 * kCopies];
-    uint32_t cc[256];              // copies folded per digit
-    unsigned long long cm[256];
-    float red_f[kRrBlock / kWave];
+    union {
+        uint32_t hist[kHistWords];   // key k: bits 16*(k&1).. of dword k>>1
+        float lut[kHistWords];       // then: lut[0] = 0, lut[1 + k - kmin] = probability of key k
+        SmShared sm;                 // or: the streamed algorithm's state (overflowed rows)
+    } u;
+    uint32_t cc[256];                // per-digit counts
+    unsigned long long cm[256];      // per-digit fixed-point masses
     double red_d[kRrBlock / kWave];
     int64_t red_i[kRrBlock / kWave];
     uint32_t sel_digit;
@@ -283,15 +301,48 @@ struct RrShared {
     uint64_t sel_mass;
 };
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Keys of the two bf16 halves of a packed pair: a non-negative bit pattern h
+// maps to h + 0x8000, a negative one to 0x10000 - h, so the keys order like
+// the values and -0 and +0 share the key 0x8000.
+__device__ __forceinline__ uint32_t keys_of_pair(uint32_t w) {
+    const u16x2 h = __builtin_bit_cast(u16x2, w);
+    const uint32_t neg = __builtin_bit_cast(uint32_t, (u16x2)(0) - h);
+    const uint32_t msk = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, w) >> (s16x2)(15));
+    const uint32_t pos = w ^ 0x80008000u;
+    return (msk & neg) | (~msk & pos);
+}
+
+// The value of key k (inverse of keys_of_pair).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    const uint32_t h = (k & 0x8000u) ? (k ^ 0x8000u) : ((0x10000u - k) & 0xFFFFu);
+    return __uint_as_float(h << 16);
+}
+
+// Largest key among the 8 keys of a register vector.
+__device__ __forceinline__ uint32_t vec_max_key(const u32x4 w) {
+    const uint32_t p = pk_max_u16(pk_max_u16(w.x, w.y), pk_max_u16(w.z, w.w));
+    return max(p & 0xFFFFu, p >> 16);
+}
+
+// Visit the 8 keys of register vector v: f(key, i) with i = 0..7 in
+// increasing element index.
+template <typename F>
+__device__ __forceinline__ void visit8(const u32x4 w, F&& f) {
+    f(w.x & 0xFFFFu, 0);
+    f(w.x >> 16, 1);
+    f(w.y & 0xFFFFu, 2);
+    f(w.y >> 16, 3);
+    f(w.z & 0xFFFFu, 4);
+    f(w.z >> 16, 5);
+    f(w.w & 0xFFFFu, 6);
+    f(w.w >> 16, 7);
+}
+
 // Raw buffer descriptor (gfx9 family third dword) over num_bytes bytes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
-}
-
-// 16-bit order-preserving key of a bf16 bit pattern; -0 and +0 share a key.
-__device__ __forceinline__ uint32_t bf16_key(uint32_t h) {
-    h = (h == 0x8000u) ? 0u : h;
-    return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
 }
 
 // floor(w * 2^qs) for w in [0, 1] (w a float), exactly, from its bits.
@@ -306,60 +357,33 @@ __device__ __forceinline__ uint64_t fixed_mass(float w, int qs) {
     return mt >> (-sh);
 }
 
-// Visit the 8 bf16 bit patterns of register vector v: f(h, i) with i = 0..7
-// in increasing element index.
-template <typename F>
-__device__ __forceinline__ void visit8(const u32x4 w, F&& f) {
-    f(w.x & 0xFFFFu, 0);
-    f(w.x >> 16, 1);
-    f(w.y & 0xFFFFu, 2);
-    f(w.y >> 16, 3);
-    f(w.z & 0xFFFFu, 4);
-    f(w.z >> 16, 5);
-    f(w.w & 0xFFFFu, 6);
-    f(w.w >> 16, 7);
-}
-
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
-
 // 2^x with the hardware instruction (results below 2^-126 may flush to zero,
-// i.e. probabilities under 1e-38 may read as 0).  Every pass uses this same
+// i.e. probabilities under 1e-38 may read as 0).  Every step uses this same
 // function, so a weight is identical wherever it is recomputed.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Wave 0: choose the digit from the privatised histograms (sum of the 16
-// copies per bin).  Lane l owns digits 255-4l .. 252-4l (descending).
-// Count mode (mass_mode false): first digit d from the top whose cumulative
-// count reaches rem.  Mass mode: first non-empty digit whose cumulative mass
-// (plus `above`) reaches target, else the lowest non-empty digit.  Written
-// to keep few registers live (the caller holds the row in registers).
-__device__ __forceinline__ uint32_t rr_bin_count(const RrShared& sh, int d) { return sh.cc[d]; }
-__device__ __forceinline__ uint64_t rr_bin_mass(const RrShared& sh, int d) { return sh.cm[d]; }
-
-// Threads 0..255 fold the 16 copies of their digit into cc / cm (caller syncs).
-__device__ __forceinline__ void rr_fold(RrShared& sh, bool mass) {
-    const int d = threadIdx.x;
-    if (d < 256) {
-        uint32_t c = 0;
-        uint64_t m = 0;
-#pragma unroll 2
-        for (int k = 0; k < kCopies; ++k) {
-            c += sh.hc[d * kCopies + ((k + d) & (kCopies - 1))];
-            if (mass) m += sh.hm[d * kCopies + ((k + d) & (kCopies - 1))];
-        }
-        sh.cc[d] = c;
-        if (mass) sh.cm[d] = m;
-    }
+__device__ __forceinline__ uint32_t hist_count(const RrShared& sh, uint32_t k) {
+    return (sh.u.hist[k >> 1] >> ((k & 1u) << 4)) & 0xFFFFu;
 }
 
+__device__ __forceinline__ void hist_add(RrShared& sh, uint32_t k) {
+    __hip_atomic_fetch_add(&sh.u.hist[k >> 1], 1u << ((k & 1u) << 4), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Wave 0: choose the digit from the 256 per-digit bins.  Lane l owns digits
+// 255-4l .. 252-4l (descending).  Count mode (mass_mode false): first digit d
+// from the top whose cumulative count reaches rem.  Mass mode: first non-empty
+// digit whose cumulative mass (plus `above`) reaches target, else the lowest
+// non-empty digit.
 __device__ void rr_select(RrShared& sh, bool mass_mode, uint32_t rem, uint64_t above, double target) {
     const int lane = threadIdx.x & (kWave - 1);
     const int d0 = 255 - 4 * lane;
     uint32_t lc = 0;
     uint64_t lm = 0;
     for (int e = 0; e < 4; ++e) {
-        lc += rr_bin_count(sh, d0 - e);
-        if (mass_mode) lm += rr_bin_mass(sh, d0 - e);
+        lc += sh.cc[d0 - e];
+        if (mass_mode) lm += sh.cm[d0 - e];
     }
     if (!mass_mode) {
         uint32_t incl = lc;
@@ -373,7 +397,7 @@ __device__ void rr_select(RrShared& sh, bool mass_mode, uint32_t rem, uint64_t a
         if (lane == ls) {
             uint32_t run = incl - lc;
             for (int e = 0; e < 4; ++e) {
-                const uint32_t c = rr_bin_count(sh, d0 - e);
+                const uint32_t c = sh.cc[d0 - e];
                 if (run + c >= rem) {
                     sh.sel_digit = (uint32_t)(d0 - e);
                     sh.sel_rem = rem - run;
@@ -397,8 +421,8 @@ __device__ void rr_select(RrShared& sh, bool mass_mode, uint32_t rem, uint64_t a
         if (lane == ls) {
             uint64_t run = incl - lm;
             for (int e = 0; e < 4; ++e) {
-                const uint32_t c = rr_bin_count(sh, d0 - e);
-                const uint64_t m = rr_bin_mass(sh, d0 - e);
+                const uint32_t c = sh.cc[d0 - e];
+                const uint64_t m = sh.cm[d0 - e];
                 if (c && (double)(above + run + m) >= target) {
                     sh.sel_digit = (uint32_t)(d0 - e);
                     sh.sel_above = above + run;
@@ -412,13 +436,13 @@ __device__ void rr_select(RrShared& sh, bool mass_mode, uint32_t rem, uint64_t a
         // rounding left the target above the total: keep everything present
         uint32_t lowest = 0xFFFFFFFFu;
         for (int e = 0; e < 4; ++e)
-            if (rr_bin_count(sh, d0 - e)) lowest = (uint32_t)(d0 - e);
+            if (sh.cc[d0 - e]) lowest = (uint32_t)(d0 - e);
         const uint32_t lo = wave_reduce(lowest, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
         uint64_t part = 0, at = 0;
         for (int e = 0; e < 4; ++e) {
             const uint32_t d = (uint32_t)(d0 - e);
             if (d >= lo) {
-                const uint64_t m = rr_bin_mass(sh, (int)d);
+                const uint64_t m = sh.cm[(int)d];
                 if (d > lo) part += m;
                 else at = m;
             }
@@ -433,11 +457,44 @@ __device__ void rr_select(RrShared& sh, bool mass_mode, uint32_t rem, uint64_t a
     }
 }
 
-__device__ __forceinline__ void rr_clear(RrShared& sh, bool mass) {
-    for (int i = threadIdx.x; i < 256 * kCopies; i += kRrBlock) {
-        sh.hc[i] = 0;
-        if (mass) sh.hm[i] = 0;
+// Per-digit counts and masses of the keys >= kmin of every upper digit, from
+// the histogram.  Wave w takes digits w, w+16, ...: the occupied keys of a
+// row sit in a few runs of neighbouring digits, which this spreads over the
+// waves.  Lane l of a wave owns keys 4l..4l+3 of the digit.  Returns this
+// thread's share of the total mass (lane 0 of each wave, zero elsewhere).
+__device__ __forceinline__ uint64_t rr_digit_masses(RrShared& sh, uint32_t kmin, float m, float scale, int qs) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint64_t total = 0;
+    for (int d = wave; d < 256; d += kRrBlock / kWave) {
+        uint32_t cs = 0;
+        uint64_t ms = 0;
+        if ((uint32_t)(d * 256 + 255) >= kmin) {
+            const uint32_t k0 = (uint32_t)(d * 256 + 4 * lane);
+            const uint2 h = reinterpret_cast<const uint2*>(sh.u.hist)[d * 64 + lane];
+            uint32_t c[4] = {h.x & 0xFFFFu, h.x >> 16, h.y & 0xFFFFu, h.y >> 16};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k0 + e < kmin) c[e] = 0;
+            if (__any((c[0] | c[1] | c[2] | c[3]) != 0)) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (c[e]) {
+                        const float wv = fast_exp2((key_to_float(k0 + e) - m) * scale);
+                        ms += (uint64_t)c[e] * fixed_mass(wv, qs);
+                        cs += c[e];
+                    }
+                }
+                ms = wave_reduce(ms, OpSumU64{});
+                cs = wave_reduce(cs, [](uint32_t a, uint32_t b) { return a + b; });
+            }
+        }
+        if (lane == 0) {
+            sh.cc[d] = cs;
+            sh.cm[d] = ms;
+            total += ms;
+        }
     }
+    return total;
 }
 
 template <int NV>
@@ -451,7 +508,7 @@ __global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
     const int64_t r = (int64_t)b * npos + blockIdx.y;
     const uint16_t* row = logits + r * V;
     float* orow = out + r * V;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int tid = threadIdx.x;
     const bool in_al = ((uintptr_t)row & 15u) == 0;
     const bool out_al = ((uintptr_t)orow & 15u) == 0;
     // Buffer descriptors over this row (range-checked by the hardware): one
@@ -460,45 +517,63 @@ __global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
     const __amdgpu_buffer_rsrc_t rout = make_rsrc(orow, (uint32_t)(V * 4));
     const int vfull = (int)(V / (kRrBlock * 8));   // vectors that are in range for every thread
     auto ebase = [&](int v) { return (v * kRrBlock + tid) * 8; };
+    const float Tm = temperature[b];
+    if ((double)Tm < kGreedyTemperature) {
+        // one-hot rows: the streamed argmax (reads the row once)
+        softmax_row_streamed<uint16_t>(row, orow, V, Tm, 0, 1.0f, sh.u.sm);
+        return;
+    }
 
-    // ---- load the row once (padding = bf16 -inf, which never changes a result)
+    // ---- load the row once (padding = bf16 -inf, key 0x0080, below every
+    // finite logit; its count is taken out of the histogram below); the first
+    // pass turns the bit patterns into keys in place
     u32x4 w[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
+        u32x4 raw;
         if (in_al && v < vfull) {
-            w[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, tid * 16, v * kRrBlock * 16, 0));
+            raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, tid * 16, v * kRrBlock * 16, 0));
         } else {
             const int e0 = ebase(v);
             uint32_t h[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = (e0 + i < V) ? (uint32_t)row[e0 + i] : 0xFF80u;
-            w[v].x = h[0] | (h[1] << 16);
-            w[v].y = h[2] | (h[3] << 16);
-            w[v].z = h[4] | (h[5] << 16);
-            w[v].w = h[6] | (h[7] << 16);
+            raw.x = h[0] | (h[1] << 16);
+            raw.y = h[2] | (h[3] << 16);
+            raw.z = h[4] | (h[5] << 16);
+            raw.w = h[6] | (h[7] << 16);
         }
+        w[v] = raw;
+    }
+    {
+        // clear the histogram while the loads are in flight
+        uint4* h4 = reinterpret_cast<uint4*>(sh.u.hist);
+#pragma unroll
+        for (int i = 0; i < kHistWords / 4 / kRrBlock; ++i) h4[i * kRrBlock + tid] = make_uint4(0, 0, 0, 0);
     }
     SV_VEC_FENCE();
-    const float Tm = temperature[b];
 
-    // ---- maximum
-    float lm = -INFINITY;
-launder<NV>(w);
+    // ---- keys, and their maximum
+    uint32_t lk = 0;
+    launder<NV>(w);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-        visit8(w[v], [&](uint32_t h, int) { lm = fmaxf(lm, bf16_bits_to_float(h)); });
-        SV_VEC_FENCE();
+        w[v].x = keys_of_pair(w[v].x);
+        w[v].y = keys_of_pair(w[v].y);
+        w[v].z = keys_of_pair(w[v].z);
+        w[v].w = keys_of_pair(w[v].w);
+        lk = max(lk, vec_max_key(w[v]));
     }
-    const float m = block_reduce<kRrBlock>(lm, OpMaxF{}, -INFINITY, sh.red_f);
+    const uint32_t mkey = (uint32_t)block_reduce<kRrBlock>((int64_t)lk, [](int64_t a, int64_t c) { return a > c ? a : c; },
+                                                           (int64_t)0, sh.red_i);
+    const float m = key_to_float(mkey);
 
     auto store8 = [&](int v, const float (&o)[8]) {
         if (out_al && v < vfull) {
             const u32x4 a = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
             const u32x4 c = {__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])};
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, a),
-                                                   rout, tid * 32, v * kRrBlock * 32, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, c),
-                                                   rout, tid * 32 + 16, v * kRrBlock * 32, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(a, rout, tid * 32, v * kRrBlock * 32, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(c, rout, tid * 32 + 16, v * kRrBlock * 32, 0);
         } else {
             const int e0 = ebase(v);
 #pragma unroll
@@ -507,144 +582,135 @@ launder<NV>(w);
         }
     };
 
-    const bool greedy = (double)Tm < kGreedyTemperature;
-    int y32 = -1;
-    if (greedy) {
-        // lowest index holding the maximum (branch-free 32-bit minimum)
-        int cand = 0x7FFFFFFF;
-        launder<NV>(w);
+    // ---- key histogram (the block_reduce above ordered the clear before it)
+    launder<NV>(w);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            visit8(w[v], [&](uint32_t h, int i) {
-                const int idx = ebase(v) + i;
-                cand = min(cand, (bf16_bits_to_float(h) == m && idx < V) ? idx : 0x7FFFFFFF);
-            });
-            SV_VEC_FENCE();
-        }
-        y32 = (int)block_reduce<kRrBlock>((int64_t)cand, OpMinI64{}, (int64_t)INT64_MAX, sh.red_i);
+    for (int v = 0; v < NV; ++v) {
+        visit8(w[v], [&](uint32_t k, int) { hist_add(sh, k); });
+        SV_VEC_FENCE();
     }
+    __syncthreads();
+
+    // ---- per-digit counts (thread t sums keys 64t..64t+63 of digit t/4); the
+    // total shows whether a 16-bit counter overflowed
+    {
+        const uint4* h4 = reinterpret_cast<const uint4*>(sh.u.hist) + tid * 8;
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 q = h4[i];
+            c += (q.x & 0xFFFFu) + (q.x >> 16) + (q.y & 0xFFFFu) + (q.y >> 16);
+            c += (q.z & 0xFFFFu) + (q.z >> 16) + (q.w & 0xFFFFu) + (q.w >> 16);
+        }
+        uint32_t cd = c + __shfl_xor(c, 1, kWave);
+        cd += __shfl_xor(cd, 2, kWave);
+        if ((tid & 3) == 0) sh.cc[tid >> 2] = cd;
+        const int64_t total = block_reduce<kRrBlock>((int64_t)c, [](int64_t a, int64_t d) { return a + d; },
+                                                     (int64_t)0, sh.red_i);
+        if (total != (int64_t)NV * 8 * kRrBlock) {
+            __syncthreads();
+            softmax_row_streamed<uint16_t>(row, orow, V, Tm, top_k ? top_k[b] : 0, top_p ? top_p[b] : 1.0f,
+                                           sh.u.sm);
+            return;
+        }
+        const uint32_t npad = (uint32_t)((int64_t)NV * 8 * kRrBlock - V);
+        __syncthreads();
+        if (tid == 0 && npad) {
+            sh.u.hist[0x80u >> 1] -= npad;   // key 0x0080 (bf16 -inf) sits in the low half
+            sh.cc[0] -= npad;
+        }
+        __syncthreads();
+    }
+
+    const int32_t k = top_k ? top_k[b] : 0;
+    const float tp = top_p ? top_p[b] : 1.0f;
     const float scale = kLog2e / Tm;
     uint32_t kmin = 0;
-    float inv = 1.0f;
-    if (!greedy) {
-        const int32_t k = top_k ? top_k[b] : 0;
-        const float tp = top_p ? top_p[b] : 1.0f;
-        const int copy = lane & (kCopies - 1);
 
-        // ---- top-k: k-th largest key (two 8-bit digits), all ties kept
-        if (k > 0 && (int64_t)k < V) {
-            uint32_t prefix = 0, rem = (uint32_t)k;
-            for (int shift = 8; shift >= 0; shift -= 8) {
-                rr_clear(sh, false);
-                __syncthreads();
-    launder<NV>(w);
-    #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    visit8(w[v], [&](uint32_t h, int) {
-                        const uint32_t key = bf16_key(h);
-                        if (shift == 8 || (key >> 8) == prefix)
-                            atomicAdd(&sh.hc[((key >> shift) & 255u) * kCopies + copy], 1u);
-                    });
-                    SV_VEC_FENCE();
-                }
-                __syncthreads();
-                rr_fold(sh, false);
-                __syncthreads();
-                if (tid < kWave) rr_select(sh, false, rem, 0, 0.0);
-                __syncthreads();
-                prefix = (prefix << 8) | sh.sel_digit;
-                rem = sh.sel_rem;
-            }
-            kmin = prefix;
-        }
+    // ---- top-k: k-th largest key (two 8-bit digits), all ties kept
+    if (k > 0 && (int64_t)k < V) {
+        if (tid < kWave) rr_select(sh, false, (uint32_t)k, 0, 0.0);
+        __syncthreads();
+        const uint32_t hi = sh.sel_digit, rem = sh.sel_rem;
+        __syncthreads();
+        if (tid < 256) sh.cc[tid] = hist_count(sh, hi * 256 + tid);
+        __syncthreads();
+        if (tid < kWave) rr_select(sh, false, rem, 0, 0.0);
+        __syncthreads();
+        kmin = (hi << 8) | sh.sel_digit;
+    }
 
-        // ---- top-p over the kept keys; fixed-point masses
-        const int lg = V > 1 ? 64 - __clzll((unsigned long long)(V - 1)) : 0;
-        const int qs = 62 - lg;
-        double S = 1.0;
-        if (tp < 1.0f) {
-            uint32_t prefix = 0;
-            uint64_t above = 0, total = 0;
-            double target = 0.0;
-            for (int shift = 8; shift >= 0; shift -= 8) {
-                rr_clear(sh, true);
-                __syncthreads();
-    launder<NV>(w);
-    #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    uint32_t any = 0;
-                    visit8(w[v], [&](uint32_t h, int) { any |= (bf16_key(h) >= kmin) ? 1u : 0u; });
-                    if (__any(any)) {
-                        visit8(w[v], [&](uint32_t h, int) {
-                            const uint32_t key = bf16_key(h);
-                            if (key >= kmin && (shift == 8 || (key >> 8) == prefix)) {
-                                const float wv = fast_exp2((bf16_bits_to_float(h) - m) * scale);
-                                const uint32_t d = ((key >> shift) & 255u) * kCopies + copy;
-                                atomicAdd(&sh.hc[d], 1u);
-                                const uint64_t wq = fixed_mass(wv, qs);
-                                if (wq) atomicAdd(&sh.hm[d], (unsigned long long)wq);
-                            }
-                        });
-                    }
-                    SV_VEC_FENCE();
-                }
-                __syncthreads();
-                rr_fold(sh, true);
-                __syncthreads();
-                if (shift == 8) {
-                    // the first level's histogram holds every kept key: its total is the top-k mass
-                    uint64_t part = 0;
-                    for (int i = tid; i < 256; i += kRrBlock) part += sh.cm[i];
-                    total = block_reduce<kRrBlock>(part, OpSumU64{}, (uint64_t)0,
-                                                   reinterpret_cast<uint64_t*>(sh.red_i));
-                    target = (double)tp * (double)total;
-                }
-                if (tid < kWave) rr_select(sh, true, 0, above, target);
-                __syncthreads();
-                prefix = (prefix << 8) | sh.sel_digit;
-                above = sh.sel_above;
-                if (shift == 0) S = (double)(above + sh.sel_mass) * ldexp(1.0, -qs);
-            }
-            kmin = prefix;
-        } else {
-            double ps = 0.0;
-    launder<NV>(w);
-    #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                uint32_t any = 0;
-                visit8(w[v], [&](uint32_t h, int) { any |= (bf16_key(h) >= kmin) ? 1u : 0u; });
-                if (__any(any)) {
-                    visit8(w[v], [&](uint32_t h, int) {
-                        if (bf16_key(h) >= kmin) ps += (double)fast_exp2((bf16_bits_to_float(h) - m) * scale);
-                    });
-                }
-                SV_VEC_FENCE();
-            }
-            S = block_reduce<kRrBlock>(ps, OpSumD{}, 0.0, sh.red_d);
+    // ---- top-p over the kept keys; S = sum of the kept weights
+    const int lg = V > 1 ? 64 - __clzll((unsigned long long)(V - 1)) : 0;
+    const int qs = 62 - lg;
+    double S;
+    if (tp < 1.0f) {
+        const uint64_t part = rr_digit_masses(sh, kmin, m, scale, qs);
+        const uint64_t total = block_reduce<kRrBlock>(part, OpSumU64{}, (uint64_t)0,
+                                                      reinterpret_cast<uint64_t*>(sh.red_i));
+        const double target = (double)tp * (double)total;
+        if (tid < kWave) rr_select(sh, true, 0, 0, target);
+        __syncthreads();
+        const uint32_t hi = sh.sel_digit;
+        const uint64_t above = sh.sel_above;
+        __syncthreads();
+        if (tid < 256) {
+            const uint32_t key = hi * 256 + tid;
+            const uint32_t c = key >= kmin ? hist_count(sh, key) : 0u;
+            sh.cc[tid] = c;
+            sh.cm[tid] = c ? (uint64_t)c * fixed_mass(fast_exp2((key_to_float(key) - m) * scale), qs) : 0;
         }
-        inv = (float)(1.0 / S);
+        __syncthreads();
+        if (tid < kWave) rr_select(sh, true, 0, above, target);
+        __syncthreads();
+        kmin = (hi << 8) | sh.sel_digit;
+        S = (double)(sh.sel_above + sh.sel_mass) * ldexp(1.0, -qs);
+    } else {
+        // sum over the histogram: wave w takes digits w, w+16, ... (as above)
+        const int lane = tid & (kWave - 1);
+        double ps = 0.0;
+        for (int d = tid / kWave; d < 256; d += kRrBlock / kWave) {
+            if ((uint32_t)(d * 256 + 255) < kmin) continue;
+            const uint32_t k0 = (uint32_t)(d * 256 + 4 * lane);
+            const uint2 h = reinterpret_cast<const uint2*>(sh.u.hist)[d * 64 + lane];
+            const uint32_t c[4] = {h.x & 0xFFFFu, h.x >> 16, h.y & 0xFFFFu, h.y >> 16};
+            if (!__any((c[0] | c[1] | c[2] | c[3]) != 0)) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c[e] && k0 + e >= kmin) ps += (double)c[e] * (double)fast_exp2((key_to_float(k0 + e) - m) * scale);
+        }
+        S = block_reduce<kRrBlock>(ps, OpSumD{}, 0.0, sh.red_d);
+    }
+    const float inv = (float)(1.0 / S);
+
+    // ---- probability table over keys kmin..mkey (replaces the histogram)
+    const uint32_t span = mkey - kmin;   // table holds span + 1 keys
+    const bool table = span < (uint32_t)kLutMax;
+    __syncthreads();
+    if (table) {
+        for (uint32_t j = tid; j <= span; j += kRrBlock)
+            sh.u.lut[1 + j] = fast_exp2((key_to_float(kmin + j) - m) * scale) * inv;
+        if (tid == 0) sh.u.lut[0] = 0.0f;
+        __syncthreads();
     }
 
     // ---- write
-launder<NV>(w);
+    const int koff = 1 - (int)kmin;
+    launder<NV>(w);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         float o[8];
-        uint32_t any = 0;
-        if (greedy) {
-            const int e0 = ebase(v);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (e0 + i == y32) ? 1.0f : 0.0f;
-        } else {
-        visit8(w[v], [&](uint32_t h, int) { any |= (bf16_key(h) >= kmin) ? 1u : 0u; });
-        if (__any(any)) {
-            visit8(w[v], [&](uint32_t h, int i) {
-                o[i] = (bf16_key(h) >= kmin) ? fast_exp2((bf16_bits_to_float(h) - m) * scale) * inv : 0.0f;
-            });
+        if (__any(vec_max_key(w[v]) >= kmin)) {
+            if (table) {
+                visit8(w[v], [&](uint32_t key, int i) { o[i] = sh.u.lut[max((int)key + koff, 0)]; });
+            } else {
+                visit8(w[v], [&](uint32_t key, int i) {
+                    o[i] = (key >= kmin) ? fast_exp2((key_to_float(key) - m) * scale) * inv : 0.0f;
+                });
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = 0.0f;
-        }
         }
         store8(v, o);
         SV_VEC_FENCE();

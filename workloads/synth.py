@@ -259,7 +259,10 @@ def fuzz_case(seed: int, B: int, D: int, V: int, dtype: str = "f32", sigma: floa
     so rows hold repeated maxima), "zeros" (all-zero logits and probability
     rows), "onehot" (one-hot target and draft rows), "disjoint" (draft and
     target supports disjoint), "equal" (draft rows equal to target rows),
-    "invalid_ids" (some draft ids outside [0, V)).
+    "invalid_ids" (some draft ids outside [0, V)), "mostly_zero" (nine in ten
+    logits exactly zero, so one value fills most of a row), "wide" (logits
+    uniform over [-3e4, 3e4]), "signed_zeros" (logits drawn from -1, -0.0,
+    +0.0 and 1).
     """
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([1000, seed, B, D, V])))
     N = D + 1
@@ -268,6 +271,12 @@ def fuzz_case(seed: int, B: int, D: int, V: int, dtype: str = "f32", sigma: floa
         z = np.round(z).astype(np.float32)
     if special == "zeros":
         z = np.zeros_like(z)
+    if special == "mostly_zero":
+        z = np.where(rng.random(z.shape) < 0.9, np.float32(0.0), z).astype(np.float32)
+    if special == "wide":
+        z = rng.uniform(-3e4, 3e4, size=z.shape).astype(np.float32)
+    if special == "signed_zeros":
+        z = rng.choice(np.array([-1.0, -0.0, 0.0, 1.0], np.float32), size=z.shape, p=[0.3, 0.2, 0.2, 0.3])
     if dtype == "bf16":
         zs = f32_to_bf16_bits(z)
         zd = bf16_bits_to_f32(zs).astype(np.float64)
