@@ -11,6 +11,8 @@
 //     largest key whose upper mass reaches top_p times the top-k mass.
 // Then out = w / sum(kept w), zero elsewhere.  T < 1e-5 writes a one-hot at
 // the lowest-index argmax.
+#include <atomic>
+
 #include "sv_argmax.hpp"
 #include "sv_launch.hpp"
 
@@ -251,23 +253,28 @@ __global__ __launch_bounds__(kSmBlock) void softmax_renorm_kernel(
 // read from HBM once into registers as 16-bit order-preserving keys (8*NV
 // per thread, packed in pairs) and the output is written with 16-byte stores.
 //
-// Selection never touches the elements twice: one pass builds an LDS
-// histogram of all 65536 keys (16-bit counters, two per dword), and every
-// later step works on that histogram.  The weight of an element depends only
-// on its key, so a bin's count times its weight gives the bin's mass; top-k
-// and top-p are the same two-level (8-bit digit) radix selection as in the
-// streamed kernel, with the per-digit counts and 64-bit fixed-point masses
-// summed from the histogram instead of from the elements.  Fixed-point masses
-// are floor(w * 2^qs) built exactly from the float bits of
-// w = exp2((z - m) * log2(e) / T), so every sum is an order-independent
-// integer sum.  The output pass reads each element's probability from a
-// per-key table built in the same LDS once the histogram is no longer needed.
+// Selection never touches the elements twice: while the row is arriving, each
+// vector is turned into keys and counted into an LDS histogram of all 65536
+// keys (16-bit counters), and every later step works on that histogram.  The
+// weight of an element depends only on its key, so a bin's count times its
+// weight gives the bin's mass; top-k and top-p are the same two-level (8-bit
+// digit) radix selection as in the streamed kernel, with the per-digit counts
+// and 64-bit fixed-point masses summed from the histogram instead of from the
+// elements.  Fixed-point masses are floor(w * 2^qs) built exactly from the
+// float bits of w = exp2((z - m) * log2(e) / T), so every sum is an
+// order-independent integer sum.  The output pass reads each element's
+// probability from a per-key table built in the same LDS once the histogram
+// is no longer needed.
+//
+// The kernel is persistent: one workgroup per compute unit walks the rows, so
+// the loads of a row are issued right behind the stores of the previous one.
 //
 // A row in which one key occurs 65536 times or more overflows its 16-bit
 // counter; the sum of all counters then falls short of the element count, and
-// the row is redone by the streamed algorithm.
+// the row is redone by the streamed algorithm (as are one-hot rows).
 // ============================================================================
 constexpr int kRrBlock = 1024;
+constexpr int kRrWaves = kRrBlock / kWave;
 constexpr int kKeys = 65536;
 constexpr int kHistWords = kKeys / 2;     // 16-bit counters, two per dword
 constexpr int kLutMax = kHistWords - 1;   // probability-table entries (slot 0 holds 0)
@@ -289,12 +296,11 @@ struct RrShared {
     union {
         uint32_t hist[kHistWords];   // key k: bits 16*(k&1).. of dword k>>1
         float lut[kHistWords];       // then: lut[0] = 0, lut[1 + k - kmin] = probability of key k
-        SmShared sm;                 // or: the streamed algorithm's state (overflowed rows)
+        SmShared sm;                 // or: the streamed algorithm's state
     } u;
     uint32_t cc[256];                // per-digit counts
     unsigned long long cm[256];      // per-digit fixed-point masses
-    double red_d[kRrBlock / kWave];
-    int64_t red_i[kRrBlock / kWave];
+    uint64_t red[kRrWaves];          // per-wave partials of a block reduction
     uint32_t sel_digit;
     uint32_t sel_rem;
     uint64_t sel_above;
@@ -371,49 +377,73 @@ __device__ __forceinline__ void hist_add(RrShared& sh, uint32_t k) {
                            __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Block-wide reduction of a 32- or 64-bit value (every thread receives it).
+template <typename T, typename Op>
+__device__ __forceinline__ T rr_block_reduce(RrShared& sh, int tid, T v, Op op) {
+    v = wave_allreduce(v, op);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) {
+        uint64_t u = 0;
+        __builtin_memcpy(&u, &v, sizeof(T));
+        sh.red[tid / kWave] = u;
+    }
+    __syncthreads();
+    T r;
+    __builtin_memcpy(&r, &sh.red[0], sizeof(T));
+#pragma unroll
+    for (int i = 1; i < kRrWaves; ++i) {
+        T x;
+        __builtin_memcpy(&x, &sh.red[i], sizeof(T));
+        r = op(r, x);
+    }
+    return r;
+}
+
+struct OpAddU32 {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct OpMaxU32 {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+
 // Wave 0: choose the digit from the 256 per-digit bins.  Lane l owns digits
 // 255-4l .. 252-4l (descending).  Count mode (mass_mode false): first digit d
 // from the top whose cumulative count reaches rem.  Mass mode: first non-empty
 // digit whose cumulative mass (plus `above`) reaches target, else the lowest
 // non-empty digit.
-__device__ void rr_select(RrShared& sh, bool mass_mode, uint32_t rem, uint64_t above, double target) {
-    const int lane = threadIdx.x & (kWave - 1);
+__device__ void rr_select(RrShared& sh, int tid, bool mass_mode, uint32_t rem, uint64_t above, double target) {
+    const int lane = tid & (kWave - 1);
     const int d0 = 255 - 4 * lane;
-    uint32_t lc = 0;
-    uint64_t lm = 0;
+    uint32_t c[4], lc = 0;
+#pragma unroll
     for (int e = 0; e < 4; ++e) {
-        lc += sh.cc[d0 - e];
-        if (mass_mode) lm += sh.cm[d0 - e];
+        c[e] = sh.cc[d0 - e];
+        lc += c[e];
     }
     if (!mass_mode) {
-        uint32_t incl = lc;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t v = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += v;
-        }
+        const uint32_t incl = wave_inclusive_sum(lc, lane);
         const uint64_t ball = __ballot(incl >= rem);
         const int ls = __ffsll((unsigned long long)ball) - 1;
         if (lane == ls) {
             uint32_t run = incl - lc;
             for (int e = 0; e < 4; ++e) {
-                const uint32_t c = sh.cc[d0 - e];
-                if (run + c >= rem) {
+                if (run + c[e] >= rem) {
                     sh.sel_digit = (uint32_t)(d0 - e);
                     sh.sel_rem = rem - run;
                     break;
                 }
-                run += c;
+                run += c[e];
             }
         }
         return;
     }
-    uint64_t incl = lm;
+    uint64_t m[4], lm = 0;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint64_t v = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += v;
+    for (int e = 0; e < 4; ++e) {
+        m[e] = sh.cm[d0 - e];
+        lm += m[e];
     }
+    const uint64_t incl = wave_inclusive_sum(lm, lane);
     // a lane holds the answer iff it has a non-empty digit and its inclusive mass reaches the target
     const uint64_t ball = __ballot(lc > 0 && (double)(above + incl) >= target);
     if (ball) {
@@ -421,34 +451,31 @@ __device__ void rr_select(RrShared& sh, bool mass_mode, uint32_t rem, uint64_t a
         if (lane == ls) {
             uint64_t run = incl - lm;
             for (int e = 0; e < 4; ++e) {
-                const uint32_t c = sh.cc[d0 - e];
-                const uint64_t m = sh.cm[d0 - e];
-                if (c && (double)(above + run + m) >= target) {
+                if (c[e] && (double)(above + run + m[e]) >= target) {
                     sh.sel_digit = (uint32_t)(d0 - e);
                     sh.sel_above = above + run;
-                    sh.sel_mass = m;
+                    sh.sel_mass = m[e];
                     break;
                 }
-                run += m;
+                run += m[e];
             }
         }
     } else {
         // rounding left the target above the total: keep everything present
         uint32_t lowest = 0xFFFFFFFFu;
+#pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (sh.cc[d0 - e]) lowest = (uint32_t)(d0 - e);
-        const uint32_t lo = wave_reduce(lowest, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+            if (c[e]) lowest = (uint32_t)(d0 - e);
+        const uint32_t lo = wave_allreduce(lowest, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
         uint64_t part = 0, at = 0;
+#pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t d = (uint32_t)(d0 - e);
-            if (d >= lo) {
-                const uint64_t m = sh.cm[(int)d];
-                if (d > lo) part += m;
-                else at = m;
-            }
+            if (d > lo) part += m[e];
+            if (d == lo) at = m[e];
         }
-        const uint64_t above_lo = wave_reduce(part, OpSumU64{});
-        const uint64_t at_lo = wave_reduce(at, OpSumU64{});
+        const uint64_t above_lo = wave_allreduce(part, OpSumU64{});
+        const uint64_t at_lo = wave_allreduce(at, OpSumU64{});
         if (lane == 0) {
             sh.sel_digit = lo;
             sh.sel_above = above + above_lo;
@@ -457,24 +484,31 @@ __device__ void rr_select(RrShared& sh, bool mass_mode, uint32_t rem, uint64_t a
     }
 }
 
-// Per-digit counts and masses of the keys >= kmin of every upper digit, from
-// the histogram.  Wave w takes digits w, w+16, ...: the occupied keys of a
-// row sit in a few runs of neighbouring digits, which this spreads over the
-// waves.  Lane l of a wave owns keys 4l..4l+3 of the digit.  Returns this
-// thread's share of the total mass (lane 0 of each wave, zero elsewhere).
-__device__ __forceinline__ uint64_t rr_digit_masses(RrShared& sh, uint32_t kmin, float m, float scale, int qs) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+// Per-digit counts and masses of the keys >= kmin, from the histogram.  Wave
+// w takes digits w, w+16, ...: the occupied keys of a row sit in a few runs
+// of neighbouring digits, which this spreads over the waves.  Lane l of a
+// wave owns keys 4l..4l+3 of the digit.  Returns the wave's total mass in
+// lane 0 and zero in the other lanes.
+__device__ __forceinline__ uint64_t rr_digit_masses(RrShared& sh, int tid, uint32_t kmin, float m, float scale,
+                                                    int qs) {
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint2* h2 = reinterpret_cast<const uint2*>(sh.u.hist);
     uint64_t total = 0;
-    for (int d = wave; d < 256; d += kRrBlock / kWave) {
-        uint32_t cs = 0;
-        uint64_t ms = 0;
-        if ((uint32_t)(d * 256 + 255) >= kmin) {
+#pragma unroll 1
+    for (int g = 0; g < 256 / kRrWaves; g += 4) {
+        uint2 h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = h2[(wave + kRrWaves * (g + j)) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = wave + kRrWaves * (g + j);
             const uint32_t k0 = (uint32_t)(d * 256 + 4 * lane);
-            const uint2 h = reinterpret_cast<const uint2*>(sh.u.hist)[d * 64 + lane];
-            uint32_t c[4] = {h.x & 0xFFFFu, h.x >> 16, h.y & 0xFFFFu, h.y >> 16};
+            uint32_t c[4] = {h[j].x & 0xFFFFu, h[j].x >> 16, h[j].y & 0xFFFFu, h[j].y >> 16};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (k0 + e < kmin) c[e] = 0;
+            uint32_t cs = 0;
+            uint64_t ms = 0;
             if (__any((c[0] | c[1] | c[2] | c[3]) != 0)) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -484,137 +518,123 @@ __device__ __forceinline__ uint64_t rr_digit_masses(RrShared& sh, uint32_t kmin,
                         cs += c[e];
                     }
                 }
-                ms = wave_reduce(ms, OpSumU64{});
-                cs = wave_reduce(cs, [](uint32_t a, uint32_t b) { return a + b; });
+                ms = wave_allreduce(ms, OpSumU64{});
+                cs = wave_allreduce(cs, OpAddU32{});
             }
-        }
-        if (lane == 0) {
-            sh.cc[d] = cs;
-            sh.cm[d] = ms;
+            if (lane == 0) {
+                sh.cc[d] = cs;
+                sh.cm[d] = ms;
+            }
             total += ms;
         }
     }
-    return total;
+    return lane == 0 ? total : 0;
 }
 
+// Sum over the histogram of count * weight for keys >= kmin (double), wave
+// w taking digits w, w+16, ... as above; returns this lane's share.
+__device__ __forceinline__ double rr_kept_weight(const RrShared& sh, int tid, uint32_t kmin, float m, float scale) {
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint2* h2 = reinterpret_cast<const uint2*>(sh.u.hist);
+    double ps = 0.0;
+#pragma unroll 1
+    for (int g = 0; g < 256 / kRrWaves; g += 4) {
+        uint2 h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = h2[(wave + kRrWaves * (g + j)) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = wave + kRrWaves * (g + j);
+            if ((uint32_t)(d * 256 + 255) < kmin) continue;
+            const uint32_t k0 = (uint32_t)(d * 256 + 4 * lane);
+            const uint32_t c[4] = {h[j].x & 0xFFFFu, h[j].x >> 16, h[j].y & 0xFFFFu, h[j].y >> 16};
+            if (!__any((c[0] | c[1] | c[2] | c[3]) != 0)) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c[e] && k0 + e >= kmin)
+                    ps += (double)c[e] * (double)fast_exp2((key_to_float(k0 + e) - m) * scale);
+        }
+    }
+    return ps;
+}
+
+// One row whose input and output are 16-byte aligned, with V a multiple of
+// 8: every 16-byte vector lies wholly inside or wholly past the end of the
+// row, and all vectors move with buffer loads and stores, whose range check
+// returns zeros for, and drops, the ones past the end.  Returns false, with
+// nothing written, if a histogram counter overflowed.
 template <int NV>
-__global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
-    const uint16_t* __restrict__ logits, int64_t B, int npos, int64_t V, const float* __restrict__ temperature,
-    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, const int32_t* __restrict__ req_index,
-    float* __restrict__ out) {
-    __shared__ RrShared sh;
-    const int64_t b = req_index ? (int64_t)req_index[blockIdx.x] : (int64_t)blockIdx.x;
-    if (b < 0 || b >= B) return;
-    const int64_t r = (int64_t)b * npos + blockIdx.y;
-    const uint16_t* row = logits + r * V;
-    float* orow = out + r * V;
-    const int tid = threadIdx.x;
-    const bool in_al = ((uintptr_t)row & 15u) == 0;
-    const bool out_al = ((uintptr_t)orow & 15u) == 0;
-    // Buffer descriptors over this row (range-checked by the hardware): one
-    // per-thread VGPR offset, the per-vector offset is a scalar.
+__device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict__ row, float* __restrict__ orow,
+                                       int64_t V, float Tm, int32_t k, float tp) {
+    // the thread index is made opaque per row, so nothing derived from it is
+    // hoisted out of the row loop and held in registers across rows
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const __amdgpu_buffer_rsrc_t rin = make_rsrc(row, (uint32_t)(V * 2));
     const __amdgpu_buffer_rsrc_t rout = make_rsrc(orow, (uint32_t)(V * 4));
-    const int vfull = (int)(V / (kRrBlock * 8));   // vectors that are in range for every thread
+    const int vfull = (int)(V / (kRrBlock * 8));   // vectors in range for every thread
     auto ebase = [&](int v) { return (v * kRrBlock + tid) * 8; };
-    const float Tm = temperature[b];
-    if ((double)Tm < kGreedyTemperature) {
-        // one-hot rows: the streamed argmax (reads the row once)
-        softmax_row_streamed<uint16_t>(row, orow, V, Tm, 0, 1.0f, sh.u.sm);
-        return;
-    }
 
-    // ---- load the row once (padding = bf16 -inf, key 0x0080, below every
-    // finite logit; its count is taken out of the histogram below); the first
-    // pass turns the bit patterns into keys in place
+    // ---- issue the row's loads
     u32x4 w[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        u32x4 raw;
-        if (in_al && v < vfull) {
-            raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, tid * 16, v * kRrBlock * 16, 0));
-        } else {
-            const int e0 = ebase(v);
-            uint32_t h[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = (e0 + i < V) ? (uint32_t)row[e0 + i] : 0xFF80u;
-            raw.x = h[0] | (h[1] << 16);
-            raw.y = h[2] | (h[3] << 16);
-            raw.z = h[4] | (h[5] << 16);
-            raw.w = h[6] | (h[7] << 16);
-        }
-        w[v] = raw;
-    }
+    for (int v = 0; v < NV; ++v)
+        w[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, tid * 16, v * kRrBlock * 16, 0));
+    // ---- clear the histogram (the previous row's table reads are done first)
+    __syncthreads();
     {
-        // clear the histogram while the loads are in flight
         uint4* h4 = reinterpret_cast<uint4*>(sh.u.hist);
 #pragma unroll
         for (int i = 0; i < kHistWords / 4 / kRrBlock; ++i) h4[i * kRrBlock + tid] = make_uint4(0, 0, 0, 0);
     }
-    SV_VEC_FENCE();
-
-    // ---- keys, and their maximum
-    uint32_t lk = 0;
-    launder<NV>(w);
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        w[v].x = keys_of_pair(w[v].x);
-        w[v].y = keys_of_pair(w[v].y);
-        w[v].z = keys_of_pair(w[v].z);
-        w[v].w = keys_of_pair(w[v].w);
-        lk = max(lk, vec_max_key(w[v]));
-    }
-    const uint32_t mkey = (uint32_t)block_reduce<kRrBlock>((int64_t)lk, [](int64_t a, int64_t c) { return a > c ? a : c; },
-                                                           (int64_t)0, sh.red_i);
-    const float m = key_to_float(mkey);
-
-    auto store8 = [&](int v, const float (&o)[8]) {
-        if (out_al && v < vfull) {
-            const u32x4 a = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
-            const u32x4 c = {__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])};
-            __builtin_amdgcn_raw_buffer_store_b128(a, rout, tid * 32, v * kRrBlock * 32, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(c, rout, tid * 32 + 16, v * kRrBlock * 32, 0);
-        } else {
-            const int e0 = ebase(v);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (e0 + i < V) orow[e0 + i] = o[i];
-        }
-    };
-
-    // ---- key histogram (the block_reduce above ordered the clear before it)
-    launder<NV>(w);
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        visit8(w[v], [&](uint32_t k, int) { hist_add(sh, k); });
-        SV_VEC_FENCE();
-    }
     __syncthreads();
 
-    // ---- per-digit counts (thread t sums keys 64t..64t+63 of digit t/4); the
-    // total shows whether a 16-bit counter overflowed
-    {
-        const uint4* h4 = reinterpret_cast<const uint4*>(sh.u.hist) + tid * 8;
-        uint32_t c = 0;
+    // ---- as each vector arrives: keys, running maximum, histogram (vectors
+    // past the end of the row become bf16 -inf, key 0x0080, below every
+    // finite logit; their count is taken out of the histogram below)
+    uint32_t lk = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 q = h4[i];
-            c += (q.x & 0xFFFFu) + (q.x >> 16) + (q.y & 0xFFFFu) + (q.y >> 16);
-            c += (q.z & 0xFFFFu) + (q.z >> 16) + (q.w & 0xFFFFu) + (q.w >> 16);
+    for (int v = 0; v < NV; ++v) {
+        u32x4 x = w[v];
+        if (v >= vfull && ebase(v) >= V) x = u32x4{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+        x.x = keys_of_pair(x.x);
+        x.y = keys_of_pair(x.y);
+        x.z = keys_of_pair(x.z);
+        x.w = keys_of_pair(x.w);
+        lk = max(lk, vec_max_key(x));
+        visit8(x, [&](uint32_t key, int) { hist_add(sh, key); });
+        w[v] = x;
+        SV_VEC_FENCE();
+    }
+    const uint32_t mkey = rr_block_reduce(sh, tid, lk, OpMaxU32{});   // its barriers also end the histogram
+    const float m = key_to_float(mkey);
+
+    // ---- per-digit counts: uint4 j = i*1024 + tid holds keys 8j..8j+7 of
+    // digit j/32, so each half-wave sums one digit; the total shows whether a
+    // 16-bit counter overflowed
+    {
+        const uint4* h4 = reinterpret_cast<const uint4*>(sh.u.hist);
+        const int lane = tid & (kWave - 1);
+        uint32_t all = 0;
+#pragma unroll
+        for (int i = 0; i < kHistWords / 4 / kRrBlock; ++i) {
+            const uint4 q = h4[i * kRrBlock + tid];
+            uint32_t c = (q.x & 0xFFFFu) + (q.x >> 16) + (q.y & 0xFFFFu) + (q.y >> 16) + (q.z & 0xFFFFu) +
+                         (q.z >> 16) + (q.w & 0xFFFFu) + (q.w >> 16);
+            all += c;
+            // sum over each group of 32 lanes: within rows, then rows 0+1 and 2+3
+            c += dpp_u32<0xB1>(c);
+            c += dpp_u32<0x4E>(c);
+            c += dpp_u32<0x141>(c);
+            c += dpp_u32<0x140>(c);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)c, 0) + (uint32_t)__builtin_amdgcn_readlane((int)c, 16);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)c, 32) + (uint32_t)__builtin_amdgcn_readlane((int)c, 48);
+            if (lane == 0) sh.cc[(i * kRrBlock + tid) / 32] = lo;
+            if (lane == 32) sh.cc[(i * kRrBlock + tid) / 32] = hi;
         }
-        uint32_t cd = c + __shfl_xor(c, 1, kWave);
-        cd += __shfl_xor(cd, 2, kWave);
-        if ((tid & 3) == 0) sh.cc[tid >> 2] = cd;
-        const int64_t total = block_reduce<kRrBlock>((int64_t)c, [](int64_t a, int64_t d) { return a + d; },
-                                                     (int64_t)0, sh.red_i);
-        if (total != (int64_t)NV * 8 * kRrBlock) {
-            __syncthreads();
-            softmax_row_streamed<uint16_t>(row, orow, V, Tm, top_k ? top_k[b] : 0, top_p ? top_p[b] : 1.0f,
-                                           sh.u.sm);
-            return;
-        }
+        const uint32_t total = rr_block_reduce(sh, tid, all, OpAddU32{});
+        if (total != (uint32_t)(NV * 8 * kRrBlock)) return false;
         const uint32_t npad = (uint32_t)((int64_t)NV * 8 * kRrBlock - V);
-        __syncthreads();
         if (tid == 0 && npad) {
             sh.u.hist[0x80u >> 1] -= npad;   // key 0x0080 (bf16 -inf) sits in the low half
             sh.cc[0] -= npad;
@@ -622,20 +642,18 @@ __global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
         __syncthreads();
     }
 
-    const int32_t k = top_k ? top_k[b] : 0;
-    const float tp = top_p ? top_p[b] : 1.0f;
     const float scale = kLog2e / Tm;
     uint32_t kmin = 0;
 
     // ---- top-k: k-th largest key (two 8-bit digits), all ties kept
     if (k > 0 && (int64_t)k < V) {
-        if (tid < kWave) rr_select(sh, false, (uint32_t)k, 0, 0.0);
+        if (tid < kWave) rr_select(sh, tid, false, (uint32_t)k, 0, 0.0);
         __syncthreads();
         const uint32_t hi = sh.sel_digit, rem = sh.sel_rem;
         __syncthreads();
         if (tid < 256) sh.cc[tid] = hist_count(sh, hi * 256 + tid);
         __syncthreads();
-        if (tid < kWave) rr_select(sh, false, rem, 0, 0.0);
+        if (tid < kWave) rr_select(sh, tid, false, rem, 0, 0.0);
         __syncthreads();
         kmin = (hi << 8) | sh.sel_digit;
     }
@@ -645,11 +663,9 @@ __global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
     const int qs = 62 - lg;
     double S;
     if (tp < 1.0f) {
-        const uint64_t part = rr_digit_masses(sh, kmin, m, scale, qs);
-        const uint64_t total = block_reduce<kRrBlock>(part, OpSumU64{}, (uint64_t)0,
-                                                      reinterpret_cast<uint64_t*>(sh.red_i));
+        const uint64_t total = rr_block_reduce(sh, tid, rr_digit_masses(sh, tid, kmin, m, scale, qs), OpSumU64{});
         const double target = (double)tp * (double)total;
-        if (tid < kWave) rr_select(sh, true, 0, 0, target);
+        if (tid < kWave) rr_select(sh, tid, true, 0, 0, target);
         __syncthreads();
         const uint32_t hi = sh.sel_digit;
         const uint64_t above = sh.sel_above;
@@ -661,30 +677,17 @@ __global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
             sh.cm[tid] = c ? (uint64_t)c * fixed_mass(fast_exp2((key_to_float(key) - m) * scale), qs) : 0;
         }
         __syncthreads();
-        if (tid < kWave) rr_select(sh, true, 0, above, target);
+        if (tid < kWave) rr_select(sh, tid, true, 0, above, target);
         __syncthreads();
         kmin = (hi << 8) | sh.sel_digit;
         S = (double)(sh.sel_above + sh.sel_mass) * ldexp(1.0, -qs);
     } else {
-        // sum over the histogram: wave w takes digits w, w+16, ... (as above)
-        const int lane = tid & (kWave - 1);
-        double ps = 0.0;
-        for (int d = tid / kWave; d < 256; d += kRrBlock / kWave) {
-            if ((uint32_t)(d * 256 + 255) < kmin) continue;
-            const uint32_t k0 = (uint32_t)(d * 256 + 4 * lane);
-            const uint2 h = reinterpret_cast<const uint2*>(sh.u.hist)[d * 64 + lane];
-            const uint32_t c[4] = {h.x & 0xFFFFu, h.x >> 16, h.y & 0xFFFFu, h.y >> 16};
-            if (!__any((c[0] | c[1] | c[2] | c[3]) != 0)) continue;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (c[e] && k0 + e >= kmin) ps += (double)c[e] * (double)fast_exp2((key_to_float(k0 + e) - m) * scale);
-        }
-        S = block_reduce<kRrBlock>(ps, OpSumD{}, 0.0, sh.red_d);
+        S = rr_block_reduce(sh, tid, rr_kept_weight(sh, tid, kmin, m, scale), OpSumD{});
     }
     const float inv = (float)(1.0 / S);
 
     // ---- probability table over keys kmin..mkey (replaces the histogram)
-    const uint32_t span = mkey - kmin;   // table holds span + 1 keys
+    const uint32_t span = mkey - kmin;   // the table holds span + 1 keys
     const bool table = span < (uint32_t)kLutMax;
     __syncthreads();
     if (table) {
@@ -712,8 +715,67 @@ __global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = 0.0f;
         }
-        store8(v, o);
+        const u32x4 a = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+        const u32x4 c = {__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(a, rout, tid * 32, v * kRrBlock * 32, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(c, rout, tid * 32 + 16, v * kRrBlock * 32, 0);
         SV_VEC_FENCE();
+    }
+    return true;
+}
+
+// Persistent: workgroup g handles rows g, g + gridDim.x, ... of the
+// n_req * npos rows (request-major).  Rows the register-resident path does
+// not take (one-hot rows, unaligned rows, overflowed counters) are queued in
+// LDS and redone by the streamed algorithm after the loop, so that code is
+// not part of the loop that keeps a row in registers.
+constexpr int kDeferMax = 512;
+
+struct RrKernelShared {
+    RrShared rr;
+    int64_t defer[kDeferMax];
+    uint32_t ndefer;
+};
+
+template <int NV>
+__global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
+    const uint16_t* __restrict__ logits, int64_t B, int npos, int64_t V, const float* __restrict__ temperature,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, const int32_t* __restrict__ req_index,
+    int64_t n_req, float* __restrict__ out) {
+    __shared__ RrKernelShared ks;
+    const int64_t n_rows = n_req * npos;
+    if (threadIdx.x == 0) ks.ndefer = 0;
+    auto locate = [&](int64_t item, int64_t& b, int64_t& r) {
+        const int64_t q = item / npos;
+        b = req_index ? (int64_t)req_index[q] : q;
+        r = b * npos + (item - q * npos);
+        return b >= 0 && b < B;
+    };
+    for (int64_t item = blockIdx.x; item < n_rows; item += gridDim.x) {
+        int64_t b, r;
+        if (!locate(item, b, r)) continue;
+        const uint16_t* row = logits + r * V;
+        float* orow = out + r * V;
+        const float Tm = temperature[b];
+        bool done = false;
+        if ((double)Tm >= kGreedyTemperature && (((uintptr_t)row | (uintptr_t)orow) & 15u) == 0 && (V & 7) == 0)
+            done = rr_row<NV>(ks.rr, row, orow, V, Tm, top_k ? top_k[b] : 0, top_p ? top_p[b] : 1.0f);
+        if (!done && threadIdx.x == 0) {
+            const uint32_t i = ks.ndefer++;
+            if (i < (uint32_t)kDeferMax) ks.defer[i] = item;
+        }
+    }
+    __syncthreads();
+    const uint32_t nd = ks.ndefer;
+    // more deferred rows than the queue holds: redo every row of this workgroup
+    const int64_t n_redo = nd <= (uint32_t)kDeferMax ? (int64_t)nd : (n_rows - blockIdx.x + gridDim.x - 1) / gridDim.x;
+    for (int64_t i = 0; i < n_redo; ++i) {
+        const int64_t item = nd <= (uint32_t)kDeferMax ? ks.defer[i] : blockIdx.x + i * gridDim.x;
+        int64_t b, r;
+        if (!locate(item, b, r)) continue;
+        __syncthreads();
+        softmax_row_streamed<uint16_t>(logits + r * V, out + r * V, V, temperature[b], top_k ? top_k[b] : 0,
+                                       top_p ? top_p[b] : 1.0f, ks.rr.u.sm);
     }
 }
 
@@ -721,11 +783,24 @@ __global__ __launch_bounds__(kRrBlock) void softmax_renorm_rr_kernel(
 constexpr int kRrMaxNV = 20;
 
 template <int NV>
-static void launch_rr(dim3 grid, hipStream_t stream, const uint16_t* logits, int64_t B, int npos, int64_t V,
+static void launch_rr(unsigned grid, hipStream_t stream, const uint16_t* logits, int64_t B, int npos, int64_t V,
                       const float* temperature, const int32_t* top_k, const float* top_p, const int32_t* req_index,
-                      float* out) {
-    hipLaunchKernelGGL(softmax_renorm_rr_kernel<NV>, grid, dim3(kRrBlock), 0, stream, logits, B, npos, V,
-                       temperature, top_k, top_p, req_index, out);
+                      int64_t n_req, float* out) {
+    hipLaunchKernelGGL(softmax_renorm_rr_kernel<NV>, dim3(grid), dim3(kRrBlock), 0, stream, logits, B, npos, V,
+                       temperature, top_k, top_p, req_index, n_req, out);
+}
+
+// Compute units of the current device (cached per device; 256 if unknown).
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t npos, int64_t V,
@@ -734,16 +809,19 @@ hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64
                                  hipStream_t stream) {
     const dim3 grid((unsigned)n_req, (unsigned)npos), block(kSmBlock);
     if (dtype == kDtypeBF16 && V <= (int64_t)kRrBlock * 8 * kRrMaxNV) {
+        // one persistent workgroup per compute unit (the LDS footprint allows no more)
+        const int64_t rows = n_req * npos;
+        const unsigned g = (unsigned)(rows < (int64_t)device_cus() ? rows : (int64_t)device_cus());
         const int64_t nv = (V + kRrBlock * 8 - 1) / (kRrBlock * 8);
         const uint16_t* lg = static_cast<const uint16_t*>(logits);
         const int np = (int)npos;
-        if (nv <= 1) launch_rr<1>(grid, stream, lg, B, np, V, temperature, top_k, top_p, req_index, probs_out);
-        else if (nv <= 2) launch_rr<2>(grid, stream, lg, B, np, V, temperature, top_k, top_p, req_index, probs_out);
-        else if (nv <= 4) launch_rr<4>(grid, stream, lg, B, np, V, temperature, top_k, top_p, req_index, probs_out);
-        else if (nv <= 8) launch_rr<8>(grid, stream, lg, B, np, V, temperature, top_k, top_p, req_index, probs_out);
-        else if (nv <= 12) launch_rr<12>(grid, stream, lg, B, np, V, temperature, top_k, top_p, req_index, probs_out);
-        else if (nv <= 16) launch_rr<16>(grid, stream, lg, B, np, V, temperature, top_k, top_p, req_index, probs_out);
-        else launch_rr<20>(grid, stream, lg, B, np, V, temperature, top_k, top_p, req_index, probs_out);
+        if (nv <= 1) launch_rr<1>(g, stream, lg, B, np, V, temperature, top_k, top_p, req_index, n_req, probs_out);
+        else if (nv <= 2) launch_rr<2>(g, stream, lg, B, np, V, temperature, top_k, top_p, req_index, n_req, probs_out);
+        else if (nv <= 4) launch_rr<4>(g, stream, lg, B, np, V, temperature, top_k, top_p, req_index, n_req, probs_out);
+        else if (nv <= 8) launch_rr<8>(g, stream, lg, B, np, V, temperature, top_k, top_p, req_index, n_req, probs_out);
+        else if (nv <= 12) launch_rr<12>(g, stream, lg, B, np, V, temperature, top_k, top_p, req_index, n_req, probs_out);
+        else if (nv <= 16) launch_rr<16>(g, stream, lg, B, np, V, temperature, top_k, top_p, req_index, n_req, probs_out);
+        else launch_rr<20>(g, stream, lg, B, np, V, temperature, top_k, top_p, req_index, n_req, probs_out);
         return hipGetLastError();
     }
     if (dtype == kDtypeBF16)

@@ -84,6 +84,84 @@ __device__ __forceinline__ T wave_reduce(T v, Op op) {
     return v;
 }
 
+// ----------------------------------------------------------------------------
+// Cross-lane steps on the DPP network (register to register, no LDS round
+// trip).  Every lane of the wave must be active.  Control codes: quad_perm
+// [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
+// row_mirror = 0x140, row_shr:n = 0x110 + n.
+// ----------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+// Like dpp_u32, but a lane whose source lies outside its row reads 0.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_or0_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_move(T v) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const uint64_t r = (uint64_t)dpp_u32<CTRL>((uint32_t)u) | ((uint64_t)dpp_u32<CTRL>((uint32_t)(u >> 32)) << 32);
+        return __builtin_bit_cast(T, r);
+    }
+}
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_move_or0(T v) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, dpp_or0_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const uint64_t r =
+            (uint64_t)dpp_or0_u32<CTRL>((uint32_t)u) | ((uint64_t)dpp_or0_u32<CTRL>((uint32_t)(u >> 32)) << 32);
+        return __builtin_bit_cast(T, r);
+    }
+}
+template <typename T>
+__device__ __forceinline__ T read_lane(T v, int lane) {
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const uint64_t r = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane) << 32);
+        return __builtin_bit_cast(T, r);
+    }
+}
+
+// Reduction over the 64 lanes with a fixed association order (butterfly in
+// each row of 16 lanes, then the four row results in lane order); the result
+// is wave-uniform.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op) {
+    v = op(v, dpp_move<0xB1>(v));
+    v = op(v, dpp_move<0x4E>(v));
+    v = op(v, dpp_move<0x141>(v));
+    v = op(v, dpp_move<0x140>(v));
+    return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
+}
+
+// Inclusive prefix sum over lanes 0..63 (lane l receives v_0 + ... + v_l);
+// `lane` is this thread's lane number.
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_sum(T v, int lane) {
+    v += dpp_move_or0<0x111>(v);
+    v += dpp_move_or0<0x112>(v);
+    v += dpp_move_or0<0x114>(v);
+    v += dpp_move_or0<0x118>(v);
+    const T r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
+    T add = 0;
+    if (lane >= 16) add += r0;
+    if (lane >= 32) add += r1;
+    if (lane >= 48) add += r2;
+    return v + add;
+}
+
 struct OpMaxF {
     __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
 };
