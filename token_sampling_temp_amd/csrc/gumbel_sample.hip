@@ -4,8 +4,12 @@
 //
 // Row j of request b: s_v = z_v / T + G_v, G_v = -ln(-ln u_v), u_v the uniform
 // of Philox word v of stream (seed_b, offset_b + 32 j); the sample is the
-// lowest-index maximum of s (float scores, packed (key, index) maximum).
-// Thread work unit = 4 consecutive vocabulary entries = one Philox block.
+// lowest-index maximum of s.  Thread work unit = 4 consecutive vocabulary
+// entries = one Philox block.
+//
+// The scores are float: z / T as z * (1/T), and both logarithms from the
+// hardware base-2 logarithm times ln 2 (a few ulp from correctly rounded
+// values; only a near tie of the two best scores can tell them apart).
 #include "sv_argmax.hpp"
 #include "sv_launch.hpp"
 
@@ -13,11 +17,39 @@ namespace sv {
 
 constexpr int kGbBlock = 1024;
 
-__device__ __forceinline__ uint64_t gumbel_key(float z, float T, uint32_t w, int64_t idx) {
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Philox4x32-10 block `block` of stream (seed, subseq) with each 32x32-bit
+// product formed once as a 64-bit value (one multiply instruction per
+// product instead of separate low and high halves).
+__device__ __forceinline__ uint4 philox_block_mad(uint64_t seed, uint64_t subseq, uint64_t block) {
+    uint32_t c0 = (uint32_t)block, c1 = (uint32_t)(block >> 32);
+    uint32_t c2 = (uint32_t)subseq, c3 = (uint32_t)(subseq >> 32);
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0;
+        c1 = (uint32_t)p1;
+        c2 = n2;
+        c3 = (uint32_t)p0;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+// z / T + G for Philox word w: u = (2 (w >> 9) + 1) 2^-24, -ln u and
+// -ln(-ln u) through the hardware log2.
+__device__ __forceinline__ float gumbel_score(float z, float invT, uint32_t w) {
     const float u = uniform_of(w);
-    const float g = -logf(-logf(u));
-    const float s = z / T + g;
-    return pack_key_index(float_key(s), idx);
+    const float nl = __builtin_amdgcn_logf(u) * -kLn2;   // -ln u > 0
+    return fmaf(__builtin_amdgcn_logf(nl), -kLn2, z * invT);
 }
 
 template <typename T>
@@ -51,26 +83,43 @@ __device__ __forceinline__ void load_group4<uint16_t>(const uint16_t* row, int64
 }
 
 template <int BLOCK, typename T>
-__device__ int64_t row_gumbel(const T* row, int64_t V, float Tm, uint64_t seed, uint64_t subseq,
+__device__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed, uint64_t subseq,
                               ArgmaxShared<BLOCK>& sh) {
     const bool aligned = ((uintptr_t)row % (4 * sizeof(T))) == 0;
-    const int64_t ngroups = (V + 3) / 4;
-    uint64_t best = 0;
-    for (int64_t g = threadIdx.x; g < ngroups; g += BLOCK) {
-        const int64_t v0 = g * 4;
+    const int Vi = (int)V;   // V < 2^31
+    const int ngroups = (Vi + 3) / 4;
+    // this thread's best score and its index; elements are visited in
+    // increasing index order, so a strict comparison keeps the lowest index
+    float best = -INFINITY;
+    int bi = (int)threadIdx.x * 4 < Vi ? (int)threadIdx.x * 4 : -1;
+    for (int g = threadIdx.x; g < ngroups; g += BLOCK) {
+        const int v0 = g * 4;
         float f[4];
         load_group4<T>(row, v0, V, aligned, f);
-        const uint4 w = philox_block(seed, subseq, (uint64_t)g);
+        const uint4 w = philox_block_mad(seed, subseq, (uint64_t)g);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        if (v0 + 3 < Vi) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (v0 + e < V) {
-                const uint64_t k = gumbel_key(f[e], Tm, ws[e], v0 + e);
-                best = k > best ? k : best;
+            for (int e = 0; e < 4; ++e) {
+                const float sc = gumbel_score(f[e], invT, ws[e]);
+                if (sc > best) {
+                    best = sc;
+                    bi = v0 + e;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sc = gumbel_score(f[e], invT, ws[e]);
+                if (v0 + e < Vi && sc > best) {
+                    best = sc;
+                    bi = v0 + e;
+                }
             }
         }
     }
-    const uint64_t m = block_reduce<BLOCK>(best, OpMaxU64{}, (uint64_t)0, sh.red_u);
+    const uint64_t key = bi < 0 ? 0 : pack_key_index(float_key(best), (int64_t)bi);
+    const uint64_t m = block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
     return packed_index(m);
 }
 
@@ -87,13 +136,14 @@ __global__ __launch_bounds__(kGbBlock) void gumbel_sample_kernel(
     const int N = D + 1;
     const float Tm = temperature[b];
     const bool greedy = (double)Tm < kGreedyTemperature;
+    const float invT = 1.0f / Tm;
     const uint64_t sd = seed[b], off = offset[b];
     const bool all_rows = sampled_out != nullptr;
     int L = -1;
     for (int j = 0; j < N; ++j) {
         const T* row = logits + ((int64_t)b * N + j) * V;
         const int64_t y = greedy ? row_argmax<kGbBlock, true>(row, V, sh)
-                                 : row_gumbel<kGbBlock>(row, V, Tm, sd, off + kRngSlotSpan * (uint64_t)j, sh);
+                                 : row_gumbel<kGbBlock>(row, V, invT, sd, off + kRngSlotSpan * (uint64_t)j, sh);
         if (threadIdx.x == 0) s_y[j] = (int32_t)y;
         if (L < 0 && (j == D || draft_ids[(int64_t)b * D + j] != (int32_t)y)) {
             L = j;
