@@ -178,6 +178,20 @@ def test_chain_reject_unaligned_rows(sv):
         assert_chain_match(np_i(acc), np_i(alen), ref, range(B), ("unaligned", shift))
 
 
+def test_chain_reject_one_workgroup_per_request(sv):
+    """Batches large enough that each request gets one workgroup (chunk sums
+    kept in LDS), on aligned rows with a partial last round, odd V, and the
+    degenerate-row fallbacks."""
+    for B, D, V, special in ((260, 5, 20000, None), (300, 3, 5003, None), (258, 2, 4096, "zeros"),
+                             (257, 4, 12288, "disjoint")):
+        c = fuzz_case(500 + V, B, D, V, "f32", special=special)
+        log(f"chain one workgroup per request: B={B} D={D} V={V} special={special}")
+        ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
+        acc, alen = sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]),
+                                    dev(c["seed"]), dev(c["offset"]))
+        assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, V, special))
+
+
 def test_chain_reject_request_subset_and_determinism(sv):
     B, D, V = 9, 4, 3001
     c = fuzz_case(91, B, D, V, "f32")

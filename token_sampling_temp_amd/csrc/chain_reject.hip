@@ -2,28 +2,33 @@
 //
 // Work split: each request's row is cut into C segments and every (request,
 // segment) pair is one 256-thread workgroup; C is chosen so the grid holds
-// about five resident workgroups per CU, so a batch fills the chip whatever
-// its accept pattern.
+// about one workgroup per CU (a large batch gets one workgroup per request).
 //
 // 1. Probe (every workgroup of a request, redundantly; the lines are shared
 //    in L2): thread i < D loads p_i(x_i), q_i(x_i) and the Philox uniform u_i
 //    and decides u_i * q < p exactly in double; thread D takes the final
 //    uniform.  L = first rejected position (D if none).
 // 2. Segment pass: r_v = max(0, p_L[v] - q_L[v]) (or p_D[v] for the bonus) is
-//    summed in double per 1024-entry chunk; waves stream their chunks with two
-//    rounds of 16-byte loads in flight, and publish one sum per chunk.
-// 3. The last workgroup of the request to finish (device-scope atomic counter,
-//    reset afterwards; no cache-flushing fences) prefix-sums the chunk sums in
-//    order, finds the chunk holding u_f * R, re-reads it and finishes with a
-//    64-lane scan.  Zero-mass entries are never selected.  Sums use fixed
-//    reduction trees, so results are reproducible run to run.
+//    summed in double per 1024-entry chunk; waves stream their chunks with
+//    several rounds of 16-byte loads in flight, one sum per chunk.
+// 3. A workgroup that owns the whole row keeps its chunk sums in LDS.
+//    Otherwise the sums are published and the last workgroup of the request
+//    to finish (device-scope atomic counter, reset afterwards; no
+//    cache-flushing fences) collects them.  The locating workgroup
+//    prefix-sums the chunk sums in order, finds the chunk holding u_f * R,
+//    re-reads it and finishes with a 64-lane scan.  Zero-mass entries are
+//    never selected.  Sums use fixed reduction trees, so results are
+//    reproducible run to run.
 // 4. Degenerate rows (residual mass not positive) fall back to a draw from the
 //    target row by the same workgroup, then to floor(u_f * V).
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
 
 #ifndef SV_CHAIN_TARGET_WGS
-#define SV_CHAIN_TARGET_WGS 1024   // ~4 resident 256-thread workgroups per CU on 256 CUs
+#define SV_CHAIN_TARGET_WGS 256    // one 256-thread workgroup per CU on 256 CUs
+#endif
+#ifndef SV_CHAIN_DEPTH
+#define SV_CHAIN_DEPTH 2           // rounds of loads in flight per wave
 #endif
 #ifndef SV_CHAIN_NT
 #define SV_CHAIN_NT 1              // stream rows with non-temporal loads
@@ -31,7 +36,10 @@
 
 namespace sv {
 
-constexpr int kChainBlock = 256;
+#ifndef SV_CHAIN_BLOCK
+#define SV_CHAIN_BLOCK 256
+#endif
+constexpr int kChainBlock = SV_CHAIN_BLOCK;
 constexpr int kChainWaves = kChainBlock / kWave;
 constexpr int64_t kChunk = 1024;   // entries per wave-round; one partial sum each
 constexpr int kFallbackChunks = 512;
@@ -86,16 +94,10 @@ __device__ __forceinline__ void load_run(const float* row, int64_t base, int64_t
     }
 }
 
-// Inclusive 64-lane scan (Hillis-Steele, fixed association order).
+// Inclusive 64-lane scan (DPP, fixed association order).
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const T u = __shfl_up(v, off, kWave);
-        if (lane >= off) v += u;
-    }
-    return v;
+    return wave_inclusive_sum(v, (int)(threadIdx.x & (kWave - 1)));
 }
 
 // Search NSUB sub-tiles (64 lanes x 4 entries each; index order sub-tile,
@@ -124,7 +126,7 @@ __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if (rval(pf[k][e], qf[k][e], resid) > 0.0) mylast = base + (k * kWave + lane) * 4 + e;
-    lastpos = wave_reduce(mylast, [](int64_t a, int64_t b) { return a > b ? a : b; });
+    lastpos = wave_allreduce(mylast, [](int64_t a, int64_t b) { return a > b ? a : b; });
     total = 0.0;
     if (force_last) return -1;
 #pragma unroll
@@ -134,8 +136,7 @@ __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int
         for (int e = 0; e < 4; ++e) r[e] = rval(pf[k][e], qf[k][e], resid);
         const double s = ((r[0] + r[1]) + r[2]) + r[3];
         const double incl = wave_incl_scan(s);
-        double excl = __shfl_up(incl, 1, kWave);
-        if (lane == 0) excl = 0.0;
+        const double excl = wave_shift_up1(incl);
         const uint64_t hit = __ballot(run + incl > T && s > 0.0);
         if (hit) {
             const int ls = __ffsll((unsigned long long)hit) - 1;
@@ -154,9 +155,9 @@ __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int
                 }
                 if (cand < 0) cand = i0 + last_e;
             }
-            return __shfl(cand, ls, kWave);
+            return read_lane(cand, ls);
         }
-        const double tot = __shfl(incl, kWave - 1, kWave);
+        const double tot = read_lane(incl, kWave - 1);
         run += tot;
         total += tot;
     }
@@ -176,7 +177,8 @@ __device__ int wave_pick(int n, Get get, double& R, double uf, double& base, int
     double lt = 0.0;
     for (int i = i0; i < i1; ++i) lt += get(i);
     const double incl = wave_incl_scan(lt);
-    R = __shfl(incl, kWave - 1, kWave);
+    const double ex = wave_shift_up1(incl);
+    R = read_lane(incl, kWave - 1);
     base = 0.0;
     force_last = 0;
     if (!(R > 0.0)) return -1;
@@ -185,8 +187,6 @@ __device__ int wave_pick(int n, Get get, double& R, double uf, double& base, int
     int pick = -1;
     if (ball) {
         const int ls = __ffsll((unsigned long long)ball) - 1;
-        double ex = __shfl_up(incl, 1, kWave);
-        if (lane == 0) ex = 0.0;
         if (lane == ls) {
             double run = ex;
             int lastp = -1;
@@ -207,14 +207,14 @@ __device__ int wave_pick(int n, Get get, double& R, double uf, double& base, int
                 force_last = 1;
             }
         }
-        pick = __shfl(pick, ls, kWave);
-        base = __shfl(base, ls, kWave);
-        force_last = __shfl(force_last, ls, kWave);
+        pick = read_lane(pick, ls);
+        base = read_lane(base, ls);
+        force_last = read_lane(force_last, ls);
     } else {
         int lp = -1;
         for (int i = i0; i < i1; ++i)
             if (get(i) > 0.0) lp = i;
-        pick = wave_reduce(lp, [](int a, int b) { return a > b ? a : b; });
+        pick = wave_allreduce(lp, [](int a, int b) { return a > b ? a : b; });
         force_last = 1;
     }
     return pick;
@@ -241,7 +241,7 @@ __device__ int64_t draw_row_single(const float* pr, int64_t V, double uf, ChainS
                 acc += ((r[0] + r[1]) + r[2]) + r[3];
             }
         }
-        acc = wave_reduce(acc, OpSumD{});
+        acc = wave_allreduce(acc, OpSumD{});
         if (lane == 0) sh.chunk[c] = acc;
     }
     __syncthreads();
@@ -288,52 +288,85 @@ __device__ __forceinline__ double read_partial(double* src) {
     return __longlong_as_double((long long)v);
 }
 
-// Segment pass for a workgroup whose chunks are all in bounds and 16-byte
-// aligned: straight-line unconditional loads so that the next round's loads
-// stay in flight while the current round is summed.  Returns, on lane r, the
-// sum of round r's chunk of this wave.
-template <bool RESID>
-__device__ __forceinline__ double stream_chunks_fast(const float* pr, const float* qr, int64_t chunk0, int R) {
+// Segment pass for rows that are 16-byte aligned with V a multiple of 4 (and
+// V < 2^29, so every offset fits 32 bits).  Rounds whose four chunks lie
+// wholly inside the row stream with plain 16-byte loads and DEPTH rounds in
+// flight (consume a slot, refill it); the remaining rounds use buffer loads
+// with the row as the range, so chunks past the end read as zeros.  Returns,
+// on lane r, the sum of round r's chunk of this wave.
+template <bool RESID, int DEPTH>
+__device__ __forceinline__ double stream_chunks_fast(const float* pr, const float* qr, int64_t V, int64_t chunk0,
+                                                     int R) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    constexpr int64_t kStride = (int64_t)kChainWaves * kChunk;   // between a wave's consecutive chunks
-    const float* pb0 = pr + (chunk0 + wid) * kChunk + lane * 4;
-    const float* qb0 = RESID ? qr + (chunk0 + wid) * kChunk + lane * 4 : nullptr;
-    u32x4 pa[4], qa[4], pbf[4], qbf[4];
-    auto ld = [&](int r, u32x4 (&pv)[4], u32x4 (&qv)[4]) {
-        const float* pp = pb0 + (int64_t)r * kStride;
+    constexpr bool kNT = SV_CHAIN_NT != 0;
+    const int64_t lane_off = (int64_t)wid * kChunk + lane * 4;   // floats
+    u32x4 pv[DEPTH][4], qv[DEPTH][4];
+    auto ld = [&](int slot, int r) {
+        const float* pp = pr + (chunk0 + (int64_t)r * kChainWaves) * kChunk + lane_off;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pv[k] = load_vec<SV_CHAIN_NT != 0>(pp + k * kWave * 4, 0);
+        for (int k = 0; k < 4; ++k) pv[slot][k] = load_vec<kNT>(pp + k * kWave * 4, 0);
         if constexpr (RESID) {
-            const float* qq = qb0 + (int64_t)r * kStride;
+            const float* qq = qr + (chunk0 + (int64_t)r * kChainWaves) * kChunk + lane_off;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) qv[k] = load_vec<SV_CHAIN_NT != 0>(qq + k * kWave * 4, 0);
+            for (int k = 0; k < 4; ++k) qv[slot][k] = load_vec<kNT>(qq + k * kWave * 4, 0);
         }
     };
     double mine = 0.0;
-    auto sum = [&](int r, const u32x4 (&pv)[4], const u32x4 (&qv)[4]) {
+    auto sum = [&](const u32x4 (&p4)[4], const u32x4 (&q4)[4], int r) {
         double acc = 0.0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             float pf[4], qf[4] = {0.f, 0.f, 0.f, 0.f};
-            unpack(pv[k], pf);
-            if constexpr (RESID) unpack(qv[k], qf);
+            unpack(p4[k], pf);
+            if constexpr (RESID) unpack(q4[k], qf);
             double s4 = 0.0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) s4 += rval(pf[e], qf[e], RESID);
             acc += s4;
         }
-        acc = wave_reduce(acc, OpSumD{});
+        acc = wave_allreduce(acc, OpSumD{});
         if (lane == r) mine = acc;
     };
-    ld(0, pa, qa);
-    int r = 0;
-    for (; r + 1 < R; r += 2) {
-        ld(r + 1, pbf, qbf);
-        sum(r, pa, qa);
-        if (r + 2 < R) ld(r + 2, pa, qa);
-        sum(r + 1, pbf, qbf);
+    // rounds [0, rp) are wholly in range and a multiple of DEPTH
+    const int64_t nfull = V / kChunk;
+    int64_t rf = (nfull - chunk0) / kChainWaves;
+    rf = rf < 0 ? 0 : (rf > R ? R : rf);
+    const int rp = (int)(rf - rf % DEPTH);
+    if (rp > 0) {
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) ld(j, j);
+        int r0 = 0;
+        for (; r0 + DEPTH < rp; r0 += DEPTH) {
+#pragma unroll
+            for (int j = 0; j < DEPTH; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                sum(pv[j], qv[j], r0 + j);
+                __builtin_amdgcn_sched_barrier(0);
+                ld(j, r0 + j + DEPTH);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) sum(pv[j], qv[j], r0 + j);
     }
-    if (r < R) sum(r, pa, qa);
+    // remaining rounds: range-checked buffer loads
+    if (rp < R) {
+        constexpr int kAux = SV_CHAIN_NT ? 2 : 0;   // non-temporal
+        const __amdgpu_buffer_rsrc_t rsp = make_rsrc(pr, (uint32_t)(V * 4));
+        const __amdgpu_buffer_rsrc_t rsq = make_rsrc(RESID ? qr : pr, (uint32_t)(V * 4));
+        const uint32_t vo = (uint32_t)(lane_off * 4);
+        for (int r = rp; r < R; ++r) {
+            const uint32_t so = (uint32_t)((chunk0 + (int64_t)r * kChainWaves) * kChunk * 4);
+            u32x4 p4[4], q4[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                p4[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsp, vo + k * kWave * 16, so, kAux));
+                q4[k] = RESID ? __builtin_bit_cast(
+                                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsq, vo + k * kWave * 16, so, kAux))
+                              : u32x4{0u, 0u, 0u, 0u};
+            }
+            sum(p4, q4, r);
+        }
+    }
     return mine;
 }
 
@@ -394,9 +427,9 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     // keeps round r's chunk sum.
     const int64_t chunk0 = (int64_t)c * R * kChainWaves;
     double mine = 0.0;
-    if (aligned && (chunk0 + (int64_t)R * kChainWaves) * kChunk <= V) {
-        if (resid) mine = stream_chunks_fast<true>(pr, qr, chunk0, R);
-        else mine = stream_chunks_fast<false>(pr, qr, chunk0, R);
+    if (aligned && (V & 3) == 0 && V < ((int64_t)1 << 29)) {
+        if (resid) mine = stream_chunks_fast<true, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
+        else mine = stream_chunks_fast<false, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
     } else {
         float pa[4][4], qa[4][4], pb[4][4], qb[4][4];
         auto load_chunk = [&](int r, float (&pf)[4][4], float (&qf)[4][4]) {
@@ -418,7 +451,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
                     acc += s4;
                 }
             }
-            acc = wave_reduce(acc, OpSumD{});
+            acc = wave_allreduce(acc, OpSumD{});
             if (lane == r) mine = acc;
         };
         load_chunk(0, pa, qa);
@@ -429,25 +462,53 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
             if (r + 1 < R) sum_chunk(r + 1, pb, qb);
         }
     }
+    // One workgroup for the whole row: its chunk sums go straight to LDS.
+    // Otherwise they are published and the request's last workgroup locates.
+    const bool sums_in_lds = nchunks <= kFallbackChunks;
+    const bool solo = C == 1 && sums_in_lds;
     {
         const int64_t ch = chunk0 + (int64_t)lane * kChainWaves + wid;
-        if (lane < R && ch < nchunks) publish_partial(&partial[slot * nchunks + ch], mine);
+        if (lane < R && ch < nchunks) {
+            if (solo) sh.chunk[ch] = mine;
+            else publish_partial(&partial[slot * nchunks + ch], mine);
+        }
     }
     __syncthreads();
-    if (tid == 0)
-        sh.last = (__hip_atomic_fetch_add(&counter[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   (uint32_t)(C - 1)) ? 1 : 0;
-    __syncthreads();
-    if (!sh.last) return;
+    if (!solo) {
+        if (tid == 0)
+            sh.last = (__hip_atomic_fetch_add(&counter[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (uint32_t)(C - 1)) ? 1 : 0;
+        __syncthreads();
+        if (!sh.last) return;
+    }
 
-    // ---- 3. locate (the request's last workgroup; wave 0)
+    // ---- 3. locate (the request's last workgroup).  Published chunk sums are
+    // first copied to LDS by every thread at once (one round trip), then wave
+    // 0 picks the chunk and searches it.
     const double uf = (double)sh.code * 0x1p-24;
+    double* part = partial + slot * nchunks;
+    if (sums_in_lds && !solo) {
+        constexpr int kPer = (kFallbackChunks + kChainBlock - 1) / kChainBlock;
+        double v[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int64_t i = tid + (int64_t)k * kChainBlock;
+            v[k] = i < nchunks ? read_partial(&part[i]) : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int64_t i = tid + (int64_t)k * kChainBlock;
+            if (i < nchunks) sh.chunk[i] = v[k];
+        }
+        __syncthreads();
+    }
     if (wid == 0) {
-        double* part = partial + slot * nchunks;
         double R_tot, base;
         int force_last;
-        const int cstar = wave_pick((int)nchunks, [&](int i) { return read_partial(&part[i]); }, R_tot, uf,
-                                    base, force_last);
+        const int cstar =
+            sums_in_lds ? wave_pick((int)nchunks, [&](int i) { return sh.chunk[i]; }, R_tot, uf, base, force_last)
+                        : wave_pick((int)nchunks, [&](int i) { return read_partial(&part[i]); }, R_tot, uf, base,
+                                    force_last);
         int64_t y = -1;
         if (cstar >= 0) {
             int64_t lastpos;
@@ -471,7 +532,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     if (tid == 0) {
         accept_len[b] = L;
         // ready for the next call on this workspace (kernel boundary orders it)
-        __hip_atomic_store(&counter[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!solo) __hip_atomic_store(&counter[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

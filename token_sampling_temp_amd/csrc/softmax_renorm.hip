@@ -346,11 +346,6 @@ __device__ __forceinline__ void visit8(const u32x4 w, F&& f) {
     f(w.w >> 16, 7);
 }
 
-// Raw buffer descriptor (gfx9 family third dword) over num_bytes bytes.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
-}
-
 // floor(w * 2^qs) for w in [0, 1] (w a float), exactly, from its bits.
 __device__ __forceinline__ uint64_t fixed_mass(float w, int qs) {
     const uint32_t bits = __float_as_uint(w);

@@ -84,6 +84,12 @@ __device__ __forceinline__ T wave_reduce(T v, Op op) {
     return v;
 }
 
+// Raw buffer descriptor (gfx9 family third dword) over num_bytes bytes.  Loads
+// through it return zeros, and stores are dropped, at offsets past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+}
+
 // ----------------------------------------------------------------------------
 // Cross-lane steps on the DPP network (register to register, no LDS round
 // trip).  Every lane of the wave must be active.  Control codes: quad_perm
@@ -144,6 +150,12 @@ __device__ __forceinline__ T wave_allreduce(T v, Op op) {
     v = op(v, dpp_move<0x141>(v));
     v = op(v, dpp_move<0x140>(v));
     return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
+}
+
+// Lane l receives lane l-1's value; lane 0 receives 0 (wave_shr:1).
+template <typename T>
+__device__ __forceinline__ T wave_shift_up1(T v) {
+    return dpp_move_or0<0x138>(v);
 }
 
 // Inclusive prefix sum over lanes 0..63 (lane l receives v_0 + ... + v_l);
