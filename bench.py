@@ -238,7 +238,7 @@ class GreedyWorkload:
 
 class TopkToppWorkload:
     name = "topk_topp_chain"
-    kernel = "softmax_renorm_kernel"
+    kernel = "softmax_renorm_rr_kernel"
     sources = ("softmax_renorm.hip", "sv_argmax.hpp", "sv_common.hpp")
     counters = "softmax_renorm_topk_topp_counters.txt"
     dtype = "bf16"
@@ -319,7 +319,7 @@ class TopkToppWorkload:
 class MixedWorkload:
     """B=1024 D=7 V=129280 bf16 logits, 256 requests per mode, each mode through req_index."""
     name = "mixed"
-    kernel = "softmax_renorm_kernel"
+    kernel = "softmax_renorm_rr_kernel"
     sources = ("softmax_renorm.hip", "sv_argmax.hpp", "sv_common.hpp")
     counters = "softmax_renorm_mixed_counters.txt"
     dtype = "bf16"
