@@ -31,8 +31,10 @@
  *   rejection_sampling_one_model docstring).
  * - stream is a hipStream_t passed as void*; NULL is the default stream.
  *   Calls are asynchronous; nothing is read back to the host.  The library
- *   never synchronises.  The softmax/top-k/top-p and greedy paths use no
- *   device memory besides the arguments.
+ *   never synchronises.  specverify_softmax_renorm, specverify_greedy_verify
+ *   and specverify_gumbel_sample use no device memory besides their
+ *   arguments; specverify_chain_reject keeps a library-owned workspace (see
+ *   there).
  * - Host-side validation runs before any HIP call.  Return codes:
  *   SPECVERIFY_OK, SPECVERIFY_INVALID_ARGUMENT (nothing launched),
  *   SPECVERIFY_UNSUPPORTED (current device is not gfx950),
@@ -113,6 +115,17 @@ int specverify_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t 
  * The draw is y = min{ j : sum_{v<=j} r_v > u_f * R }, R = sum r, with
  * double-precision sums in ascending index order; an empty r falls back to
  * the target row, and an all-zero target row to floor(u_f * V).
+ *
+ * Memory: when a request's row is split over several workgroups (small
+ * batches), they hand their partial sums over through a workspace the
+ * library owns, one per (device, stream): one 32-bit counter per request and
+ * one double per 1024 vocabulary entries per request.  It is allocated with
+ * hipMalloc on the first call that needs more than the current one (grown
+ * geometrically; replaced buffers are kept until the process ends) and its
+ * counters are zeroed once with hipMemsetAsync on the call's stream; every
+ * kernel leaves them at zero.  Calls on one stream use it in stream order;
+ * calls on different streams use different workspaces.  A failed allocation
+ * returns SPECVERIFY_HIP_ERROR with nothing launched.
  */
 int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids,
                             const float* target_probs, const uint64_t* seed,
