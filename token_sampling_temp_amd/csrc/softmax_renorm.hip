@@ -268,6 +268,9 @@ __global__ __launch_bounds__(kSmBlock) void softmax_renorm_kernel(
 //
 // The kernel is persistent: one workgroup per compute unit walks the rows, so
 // the loads of a row are issued right behind the stores of the previous one.
+// Threads of a row exchange data only through LDS, so its barriers order LDS
+// alone: the stores of the previous row and the loads of this one stay in
+// flight across them.
 //
 // A row in which one key occurs 65536 times or more overflows its 16-bit
 // counter; the sum of all counters then falls short of the element count, and
@@ -376,13 +379,13 @@ __device__ __forceinline__ void hist_add(RrShared& sh, uint32_t k) {
 template <typename T, typename Op>
 __device__ __forceinline__ T rr_block_reduce(RrShared& sh, int tid, T v, Op op) {
     v = wave_allreduce(v, op);
-    __syncthreads();
+    lds_barrier();
     if ((tid & (kWave - 1)) == 0) {
         uint64_t u = 0;
         __builtin_memcpy(&u, &v, sizeof(T));
         sh.red[tid / kWave] = u;
     }
-    __syncthreads();
+    lds_barrier();
     T r;
     __builtin_memcpy(&r, &sh.red[0], sizeof(T));
 #pragma unroll
@@ -576,13 +579,13 @@ __device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict_
     for (int v = 0; v < NV; ++v)
         w[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, tid * 16, v * kRrBlock * 16, 0));
     // ---- clear the histogram (the previous row's table reads are done first)
-    __syncthreads();
+    lds_barrier();
     {
         uint4* h4 = reinterpret_cast<uint4*>(sh.u.hist);
 #pragma unroll
         for (int i = 0; i < kHistWords / 4 / kRrBlock; ++i) h4[i * kRrBlock + tid] = make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- as each vector arrives: keys, running maximum, histogram (vectors
     // past the end of the row become bf16 -inf, key 0x0080, below every
@@ -634,7 +637,7 @@ __device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict_
             sh.u.hist[0x80u >> 1] -= npad;   // key 0x0080 (bf16 -inf) sits in the low half
             sh.cc[0] -= npad;
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     const float scale = kLog2e / Tm;
@@ -643,13 +646,13 @@ __device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict_
     // ---- top-k: k-th largest key (two 8-bit digits), all ties kept
     if (k > 0 && (int64_t)k < V) {
         if (tid < kWave) rr_select(sh, tid, false, (uint32_t)k, 0, 0.0);
-        __syncthreads();
+        lds_barrier();
         const uint32_t hi = sh.sel_digit, rem = sh.sel_rem;
-        __syncthreads();
+        lds_barrier();
         if (tid < 256) sh.cc[tid] = hist_count(sh, hi * 256 + tid);
-        __syncthreads();
+        lds_barrier();
         if (tid < kWave) rr_select(sh, tid, false, rem, 0, 0.0);
-        __syncthreads();
+        lds_barrier();
         kmin = (hi << 8) | sh.sel_digit;
     }
 
@@ -661,19 +664,19 @@ __device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict_
         const uint64_t total = rr_block_reduce(sh, tid, rr_digit_masses(sh, tid, kmin, m, scale, qs), OpSumU64{});
         const double target = (double)tp * (double)total;
         if (tid < kWave) rr_select(sh, tid, true, 0, 0, target);
-        __syncthreads();
+        lds_barrier();
         const uint32_t hi = sh.sel_digit;
         const uint64_t above = sh.sel_above;
-        __syncthreads();
+        lds_barrier();
         if (tid < 256) {
             const uint32_t key = hi * 256 + tid;
             const uint32_t c = key >= kmin ? hist_count(sh, key) : 0u;
             sh.cc[tid] = c;
             sh.cm[tid] = c ? (uint64_t)c * fixed_mass(fast_exp2((key_to_float(key) - m) * scale), qs) : 0;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < kWave) rr_select(sh, tid, true, 0, above, target);
-        __syncthreads();
+        lds_barrier();
         kmin = (hi << 8) | sh.sel_digit;
         S = (double)(sh.sel_above + sh.sel_mass) * ldexp(1.0, -qs);
     } else {
@@ -684,12 +687,12 @@ __device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict_
     // ---- probability table over keys kmin..mkey (replaces the histogram)
     const uint32_t span = mkey - kmin;   // the table holds span + 1 keys
     const bool table = span < (uint32_t)kLutMax;
-    __syncthreads();
+    lds_barrier();
     if (table) {
         for (uint32_t j = tid; j <= span; j += kRrBlock)
             sh.u.lut[1 + j] = fast_exp2((key_to_float(kmin + j) - m) * scale) * inv;
         if (tid == 0) sh.u.lut[0] = 0.0f;
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- write

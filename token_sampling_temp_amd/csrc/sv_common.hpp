@@ -90,6 +90,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
 }
 
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS
+// operations, not for its outstanding global loads and stores (a plain
+// __syncthreads() waits for those too).  For code whose threads exchange
+// data only through LDS.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ----------------------------------------------------------------------------
 // Cross-lane steps on the DPP network (register to register, no LDS round
 // trip).  Every lane of the wave must be active.  Control codes: quad_perm
