@@ -281,6 +281,7 @@ constexpr int kRrWaves = kRrBlock / kWave;
 constexpr int kKeys = 65536;
 constexpr int kHistWords = kKeys / 2;     // 16-bit counters, two per dword
 constexpr int kLutMax = kHistWords - 1;   // probability-table entries (slot 0 holds 0)
+constexpr int kDirectSpan = 4096;         // key spans selected by one wave
 
 // Keep the scheduler from interleaving the per-vector work of a fully
 // unrolled pass (which would keep every element's temporaries live at once).
@@ -556,6 +557,120 @@ __device__ __forceinline__ double rr_kept_weight(const RrShared& sh, int tid, ui
     return ps;
 }
 
+// Wave 0: the k-th largest key (1 <= k < number of elements) into
+// sh.sel_digit.  Digits are summed from the maximum's digit downwards until
+// their count reaches k; inside that digit, the largest key whose count of
+// keys at or above it (within the digit, plus the digits above) reaches k.
+__device__ __noinline__ void rr_kth_key(RrShared& sh, int lane, uint32_t mkey, uint32_t k) {
+    const uint2* h2 = reinterpret_cast<const uint2*>(sh.u.hist);
+    uint32_t rem = k;
+    int d = (int)(mkey >> 8);
+    uint32_t c[4];
+    uint32_t own;
+    for (;;) {
+        const uint2 h = h2[d * 64 + lane];
+        c[0] = h.x & 0xFFFFu;
+        c[1] = h.x >> 16;
+        c[2] = h.y & 0xFFFFu;
+        c[3] = h.y >> 16;
+        own = c[0] + c[1] + c[2] + c[3];
+        const uint32_t tot = wave_allreduce(own, OpAddU32{});
+        if (tot >= rem || d == 0) break;
+        rem -= tot;
+        --d;
+    }
+    const uint32_t incl = wave_inclusive_sum(own, lane);
+    const uint32_t above = read_lane(incl, kWave - 1) - incl;   // keys of the higher lanes
+    if (lane == 0) sh.sel_digit = 0;   // (not reached when the counts are consistent)
+    if (above < rem && above + own >= rem) {
+        uint32_t run = above;
+        int e = 3;
+        for (; e > 0; --e) {
+            run += c[e];
+            if (run >= rem) break;
+        }
+        sh.sel_digit = (uint32_t)(d * 256 + 4 * lane + e);
+    }
+}
+
+// Wave 0, key span kmin..mkey of at most kDirectSpan keys: top-p on the
+// fixed-point masses count * floor(w * 2^qs), taken in descending key order:
+// the first non-empty key whose cumulative mass reaches top_p times the span's
+// mass (the lowest non-empty key if rounding leaves the target above the
+// total).  sh.sel_digit = that key, sh.sel_mass = the mass at or above it.
+// Lane l owns the l-th block of ceil(span / 64) keys from the top.
+__device__ __noinline__ void rr_topp_direct(RrShared& sh, int lane, uint32_t kmin, uint32_t mkey, float m,
+                                            float scale, int qs, float tp) {
+    const int span = (int)(mkey - kmin) + 1;
+    const int kpl = (span + kWave - 1) / kWave;
+    auto mass_of = [&](uint32_t key, uint32_t& cnt) -> uint64_t {
+        cnt = hist_count(sh, key);
+        return cnt ? (uint64_t)cnt * fixed_mass(fast_exp2((key_to_float(key) - m) * scale), qs) : 0;
+    };
+    uint64_t lm = 0;
+    uint32_t lc = 0;
+    for (int j = 0; j < kpl; ++j) {
+        const int i = lane * kpl + j;
+        if (i < span) {
+            uint32_t cnt;
+            lm += mass_of(mkey - (uint32_t)i, cnt);
+            lc += cnt;
+        }
+    }
+    const uint64_t incl = wave_inclusive_sum(lm, lane);
+    const uint64_t total = read_lane(incl, kWave - 1);
+    const double target = (double)tp * (double)total;
+    const uint64_t ball = __ballot(lc > 0 && (double)incl >= target);
+    if (ball) {
+        const int ls = __ffsll((unsigned long long)ball) - 1;
+        if (lane == ls) {
+            uint64_t run = incl - lm;
+            for (int j = 0; j < kpl; ++j) {
+                const int i = lane * kpl + j;
+                if (i >= span) break;
+                uint32_t cnt;
+                const uint64_t mk = mass_of(mkey - (uint32_t)i, cnt);
+                if (cnt && (double)(run + mk) >= target) {
+                    sh.sel_digit = mkey - (uint32_t)i;
+                    sh.sel_mass = run + mk;
+                    break;
+                }
+                run += mk;
+            }
+        }
+    } else {
+        // rounding left the target above the total: keep everything present
+        int last = -1;
+        for (int j = 0; j < kpl; ++j) {
+            const int i = lane * kpl + j;
+            if (i < span && hist_count(sh, mkey - (uint32_t)i)) last = i;
+        }
+        const int lo = wave_allreduce(last, [](int x, int y) { return x > y ? x : y; });
+        if (lane == 0) {
+            sh.sel_digit = mkey - (uint32_t)lo;
+            sh.sel_mass = total;
+        }
+    }
+}
+
+// Wave 0: sum of count * w over the keys kmin..mkey (span at most
+// kDirectSpan), in double; every lane returns the same value.
+__device__ __noinline__ double rr_span_weight(const RrShared& sh, int lane, uint32_t kmin, uint32_t mkey, float m,
+                                              float scale) {
+    const int span = (int)(mkey - kmin) + 1;
+    const int kpl = (span + kWave - 1) / kWave;
+    double ps = 0.0;
+    for (int j = 0; j < kpl; ++j) {
+        const int i = lane * kpl + j;
+        if (i < span) {
+            const uint32_t key = mkey - (uint32_t)i;
+            const uint32_t cnt = hist_count(sh, key);
+            if (cnt) ps += (double)cnt * (double)fast_exp2((key_to_float(key) - m) * scale);
+        }
+    }
+    return wave_allreduce(ps, OpSumD{});
+}
+
 // One row whose input and output are 16-byte aligned, with V a multiple of
 // 8: every 16-byte vector lies wholly inside or wholly past the end of the
 // row, and all vectors move with buffer loads and stores, whose range check
@@ -607,60 +722,49 @@ __device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict_
     const uint32_t mkey = rr_block_reduce(sh, tid, lk, OpMaxU32{});   // its barriers also end the histogram
     const float m = key_to_float(mkey);
 
-    // ---- per-digit counts: uint4 j = i*1024 + tid holds keys 8j..8j+7 of
-    // digit j/32, so each half-wave sums one digit; the total shows whether a
-    // 16-bit counter overflowed
-    {
+    // ---- overflow check (possible only when the row's slots number 65536 or
+    // more): the 16-bit counters must add up to the slot count
+    if (NV * 8 * kRrBlock > 65535) {
         const uint4* h4 = reinterpret_cast<const uint4*>(sh.u.hist);
-        const int lane = tid & (kWave - 1);
         uint32_t all = 0;
 #pragma unroll
         for (int i = 0; i < kHistWords / 4 / kRrBlock; ++i) {
             const uint4 q = h4[i * kRrBlock + tid];
-            uint32_t c = (q.x & 0xFFFFu) + (q.x >> 16) + (q.y & 0xFFFFu) + (q.y >> 16) + (q.z & 0xFFFFu) +
-                         (q.z >> 16) + (q.w & 0xFFFFu) + (q.w >> 16);
-            all += c;
-            // sum over each group of 32 lanes: within rows, then rows 0+1 and 2+3
-            c += dpp_u32<0xB1>(c);
-            c += dpp_u32<0x4E>(c);
-            c += dpp_u32<0x141>(c);
-            c += dpp_u32<0x140>(c);
-            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)c, 0) + (uint32_t)__builtin_amdgcn_readlane((int)c, 16);
-            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)c, 32) + (uint32_t)__builtin_amdgcn_readlane((int)c, 48);
-            if (lane == 0) sh.cc[(i * kRrBlock + tid) / 32] = lo;
-            if (lane == 32) sh.cc[(i * kRrBlock + tid) / 32] = hi;
+            all += (q.x & 0xFFFFu) + (q.x >> 16) + (q.y & 0xFFFFu) + (q.y >> 16) + (q.z & 0xFFFFu) + (q.z >> 16) +
+                   (q.w & 0xFFFFu) + (q.w >> 16);
         }
         const uint32_t total = rr_block_reduce(sh, tid, all, OpAddU32{});
         if (total != (uint32_t)(NV * 8 * kRrBlock)) return false;
+    }
+    {
         const uint32_t npad = (uint32_t)((int64_t)NV * 8 * kRrBlock - V);
-        if (tid == 0 && npad) {
-            sh.u.hist[0x80u >> 1] -= npad;   // key 0x0080 (bf16 -inf) sits in the low half
-            sh.cc[0] -= npad;
-        }
+        if (tid == 0 && npad) sh.u.hist[0x80u >> 1] -= npad;   // key 0x0080 (bf16 -inf) sits in the low half
         lds_barrier();
     }
 
     const float scale = kLog2e / Tm;
     uint32_t kmin = 0;
 
-    // ---- top-k: k-th largest key (two 8-bit digits), all ties kept
+    // ---- top-k: k-th largest key, all ties kept (wave 0 walks the digits
+    // down from the maximum's)
     if (k > 0 && (int64_t)k < V) {
-        if (tid < kWave) rr_select(sh, tid, false, (uint32_t)k, 0, 0.0);
+        if (tid < kWave) rr_kth_key(sh, tid, mkey, (uint32_t)k);
         lds_barrier();
-        const uint32_t hi = sh.sel_digit, rem = sh.sel_rem;
-        lds_barrier();
-        if (tid < 256) sh.cc[tid] = hist_count(sh, hi * 256 + tid);
-        lds_barrier();
-        if (tid < kWave) rr_select(sh, tid, false, rem, 0, 0.0);
-        lds_barrier();
-        kmin = (hi << 8) | sh.sel_digit;
+        kmin = sh.sel_digit;
     }
 
-    // ---- top-p over the kept keys; S = sum of the kept weights
+    // ---- top-p over the kept keys; S = sum of the kept weights.  A key span
+    // kmin..mkey of at most kDirectSpan keys is handled by wave 0 alone.
     const int lg = V > 1 ? 64 - __clzll((unsigned long long)(V - 1)) : 0;
     const int qs = 62 - lg;
+    const bool direct = mkey - kmin < (uint32_t)kDirectSpan;
     double S;
-    if (tp < 1.0f) {
+    if (tp < 1.0f && direct) {
+        if (tid < kWave) rr_topp_direct(sh, tid, kmin, mkey, m, scale, qs, tp);
+        lds_barrier();
+        kmin = sh.sel_digit;
+        S = (double)sh.sel_mass * ldexp(1.0, -qs);
+    } else if (tp < 1.0f) {
         const uint64_t total = rr_block_reduce(sh, tid, rr_digit_masses(sh, tid, kmin, m, scale, qs), OpSumU64{});
         const double target = (double)tp * (double)total;
         if (tid < kWave) rr_select(sh, tid, true, 0, 0, target);
@@ -679,6 +783,13 @@ __device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict_
         lds_barrier();
         kmin = (hi << 8) | sh.sel_digit;
         S = (double)(sh.sel_above + sh.sel_mass) * ldexp(1.0, -qs);
+    } else if (direct) {
+        if (tid < kWave) {
+            const double ws = rr_span_weight(sh, tid, kmin, mkey, m, scale);
+            if (tid == 0) sh.sel_above = __builtin_bit_cast(uint64_t, ws);
+        }
+        lds_barrier();
+        S = __builtin_bit_cast(double, sh.sel_above);
     } else {
         S = rr_block_reduce(sh, tid, rr_kept_weight(sh, tid, kmin, m, scale), OpSumD{});
     }
