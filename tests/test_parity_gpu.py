@@ -269,16 +269,20 @@ def test_softmax_renorm_fuzz(sv):
     log(f"softmax fuzz flagged rows: {flagged}")
 
 
-# bf16 rows held in registers: every register-count variant, unaligned rows,
+# bf16 rows held in registers: every register-count variant (V a multiple of
+# 8), rows of odd V (redone by the streamed algorithm),
 # a row whose most common value overflows a 16-bit histogram counter (redone by
 # the streamed algorithm), a key span too wide for the probability table, and
 # signed zeros at a top-k threshold.
 RR_CASES = [
+    (4096, "ties", ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 0, 0.6), (0.7, 3, 1.0))),
+    (8200, None, ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 0, 0.6), (0.0, 0, 1.0))),
     (8193, None, ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 0, 0.6), (0.0, 0, 1.0))),
     (40000, "ties", ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 7, 0.6), (0.0, 0, 1.0))),
-    (100003, None, ((1.0, 0, 1.0), (0.8, 20, 0.95), (1.2, 0, 0.8), (0.0, 0, 1.0))),
+    (100000, None, ((1.0, 0, 1.0), (0.8, 20, 0.95), (1.2, 0, 0.8), (0.0, 0, 1.0))),
+    (100003, None, ((1.0, 0, 1.0), (0.8, 20, 0.95), (1.2, 0, 0.8), (0.9, 0, 0.7))),
     (129280, None, ((0.7, 0, 1.0), (0.8, 100, 1.0), (1.1, 0, 0.9), (0.9, 50, 0.5))),
-    (150001, None, ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 0, 0.6), (0.0, 0, 1.0))),
+    (150000, None, ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.2, 0, 0.6), (0.5, 30000, 0.99))),
     (80000, "mostly_zero", ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.0, 20000, 1.0), (1.2, 0, 0.3))),
     (140000, "mostly_zero", ((1.0, 0, 1.0), (0.8, 100, 0.9), (1.0, 20000, 0.99), (0.0, 0, 1.0))),
     (50000, "wide", ((3e3, 0, 1.0), (1e4, 500, 0.9), (5e4, 0, 0.7), (2e3, 0, 1.0))),

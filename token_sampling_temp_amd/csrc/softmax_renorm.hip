@@ -256,15 +256,19 @@ __global__ __launch_bounds__(kSmBlock) void softmax_renorm_kernel(
 // Selection never touches the elements twice: while the row is arriving, each
 // vector is turned into keys and counted into an LDS histogram of all 65536
 // keys (16-bit counters), and every later step works on that histogram.  The
-// weight of an element depends only on its key, so a bin's count times its
-// weight gives the bin's mass; top-k and top-p are the same two-level (8-bit
-// digit) radix selection as in the streamed kernel, with the per-digit counts
-// and 64-bit fixed-point masses summed from the histogram instead of from the
-// elements.  Fixed-point masses are floor(w * 2^qs) built exactly from the
-// float bits of w = exp2((z - m) * log2(e) / T), so every sum is an
-// order-independent integer sum.  The output pass reads each element's
-// probability from a per-key table built in the same LDS once the histogram
-// is no longer needed.
+// weight of an element depends only on its key, so a key's count times its
+// weight gives its mass.  Top-k: one wave sums digits (the key's upper 8 bits)
+// down from the maximum's digit until the count reaches k, then finds the key
+// inside that digit.  Top-p: the mass of all kept keys (a block-wide pass),
+// then one wave walks digits down from the maximum's until the cumulative
+// mass reaches top_p times it, and finds the key inside that digit (when the
+// kept keys span at most kDirectSpan values, one wave does all of it over the
+// span).  Masses are 64-bit fixed point, floor(w * 2^qs) built exactly from
+// the float bits of w = exp2((z - m) * log2(e) / T), so every sum is an
+// order-independent integer sum and the selected keys are the same as those
+// of the streamed kernel's radix selection on the same masses.  The output
+// pass reads each element's probability from a per-key table built in the
+// same LDS once the histogram is no longer needed.
 //
 // The kernel is persistent: one workgroup per compute unit walks the rows, so
 // the loads of a row are issued right behind the stores of the previous one.
@@ -302,13 +306,10 @@ struct RrShared {
         float lut[kHistWords];       // then: lut[0] = 0, lut[1 + k - kmin] = probability of key k
         SmShared sm;                 // or: the streamed algorithm's state
     } u;
-    uint32_t cc[256];                // per-digit counts
-    unsigned long long cm[256];      // per-digit fixed-point masses
     uint64_t red[kRrWaves];          // per-wave partials of a block reduction
-    uint32_t sel_digit;
-    uint32_t sel_rem;
-    uint64_t sel_above;
-    uint64_t sel_mass;
+    uint32_t sel_digit;              // selected key (top-k, top-p)
+    uint64_t sel_above;              // a wave-0 result handed to the block
+    uint64_t sel_mass;               // mass at or above the top-p key
 };
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
@@ -404,131 +405,6 @@ struct OpAddU32 {
 struct OpMaxU32 {
     __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
 };
-
-// Wave 0: choose the digit from the 256 per-digit bins.  Lane l owns digits
-// 255-4l .. 252-4l (descending).  Count mode (mass_mode false): first digit d
-// from the top whose cumulative count reaches rem.  Mass mode: first non-empty
-// digit whose cumulative mass (plus `above`) reaches target, else the lowest
-// non-empty digit.
-__device__ void rr_select(RrShared& sh, int tid, bool mass_mode, uint32_t rem, uint64_t above, double target) {
-    const int lane = tid & (kWave - 1);
-    const int d0 = 255 - 4 * lane;
-    uint32_t c[4], lc = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        c[e] = sh.cc[d0 - e];
-        lc += c[e];
-    }
-    if (!mass_mode) {
-        const uint32_t incl = wave_inclusive_sum(lc, lane);
-        const uint64_t ball = __ballot(incl >= rem);
-        const int ls = __ffsll((unsigned long long)ball) - 1;
-        if (lane == ls) {
-            uint32_t run = incl - lc;
-            for (int e = 0; e < 4; ++e) {
-                if (run + c[e] >= rem) {
-                    sh.sel_digit = (uint32_t)(d0 - e);
-                    sh.sel_rem = rem - run;
-                    break;
-                }
-                run += c[e];
-            }
-        }
-        return;
-    }
-    uint64_t m[4], lm = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        m[e] = sh.cm[d0 - e];
-        lm += m[e];
-    }
-    const uint64_t incl = wave_inclusive_sum(lm, lane);
-    // a lane holds the answer iff it has a non-empty digit and its inclusive mass reaches the target
-    const uint64_t ball = __ballot(lc > 0 && (double)(above + incl) >= target);
-    if (ball) {
-        const int ls = __ffsll((unsigned long long)ball) - 1;
-        if (lane == ls) {
-            uint64_t run = incl - lm;
-            for (int e = 0; e < 4; ++e) {
-                if (c[e] && (double)(above + run + m[e]) >= target) {
-                    sh.sel_digit = (uint32_t)(d0 - e);
-                    sh.sel_above = above + run;
-                    sh.sel_mass = m[e];
-                    break;
-                }
-                run += m[e];
-            }
-        }
-    } else {
-        // rounding left the target above the total: keep everything present
-        uint32_t lowest = 0xFFFFFFFFu;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (c[e]) lowest = (uint32_t)(d0 - e);
-        const uint32_t lo = wave_allreduce(lowest, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
-        uint64_t part = 0, at = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t d = (uint32_t)(d0 - e);
-            if (d > lo) part += m[e];
-            if (d == lo) at = m[e];
-        }
-        const uint64_t above_lo = wave_allreduce(part, OpSumU64{});
-        const uint64_t at_lo = wave_allreduce(at, OpSumU64{});
-        if (lane == 0) {
-            sh.sel_digit = lo;
-            sh.sel_above = above + above_lo;
-            sh.sel_mass = at_lo;
-        }
-    }
-}
-
-// Per-digit counts and masses of the keys >= kmin, from the histogram.  Wave
-// w takes digits w, w+16, ...: the occupied keys of a row sit in a few runs
-// of neighbouring digits, which this spreads over the waves.  Lane l of a
-// wave owns keys 4l..4l+3 of the digit.  Returns the wave's total mass in
-// lane 0 and zero in the other lanes.
-__device__ __forceinline__ uint64_t rr_digit_masses(RrShared& sh, int tid, uint32_t kmin, float m, float scale,
-                                                    int qs) {
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint2* h2 = reinterpret_cast<const uint2*>(sh.u.hist);
-    uint64_t total = 0;
-#pragma unroll 1
-    for (int g = 0; g < 256 / kRrWaves; g += 4) {
-        uint2 h[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) h[j] = h2[(wave + kRrWaves * (g + j)) * 64 + lane];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d = wave + kRrWaves * (g + j);
-            const uint32_t k0 = (uint32_t)(d * 256 + 4 * lane);
-            uint32_t c[4] = {h[j].x & 0xFFFFu, h[j].x >> 16, h[j].y & 0xFFFFu, h[j].y >> 16};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (k0 + e < kmin) c[e] = 0;
-            uint32_t cs = 0;
-            uint64_t ms = 0;
-            if (__any((c[0] | c[1] | c[2] | c[3]) != 0)) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (c[e]) {
-                        const float wv = fast_exp2((key_to_float(k0 + e) - m) * scale);
-                        ms += (uint64_t)c[e] * fixed_mass(wv, qs);
-                        cs += c[e];
-                    }
-                }
-                ms = wave_allreduce(ms, OpSumU64{});
-                cs = wave_allreduce(cs, OpAddU32{});
-            }
-            if (lane == 0) {
-                sh.cc[d] = cs;
-                sh.cm[d] = ms;
-            }
-            total += ms;
-        }
-    }
-    return lane == 0 ? total : 0;
-}
 
 // Sum over the histogram of count * weight for keys >= kmin (double), wave
 // w taking digits w, w+16, ... as above; returns this lane's share.
@@ -671,6 +547,97 @@ __device__ __noinline__ double rr_span_weight(const RrShared& sh, int lane, uint
     return wave_allreduce(ps, OpSumD{});
 }
 
+// This thread's share of the fixed-point mass of the keys >= kmin (all
+// threads; wave w reads digits w, w+16, ..., lane l keys 4l..4l+3 of each).
+__device__ __noinline__ uint64_t rr_total_mass(const RrShared& sh, int tid, uint32_t kmin, float m, float scale,
+                                                  int qs) {
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint2* h2 = reinterpret_cast<const uint2*>(sh.u.hist);
+    uint64_t ms = 0;
+#pragma unroll 1
+    for (int g = 0; g < 256 / kRrWaves; g += 4) {
+        uint2 h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = h2[(wave + kRrWaves * (g + j)) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = wave + kRrWaves * (g + j);
+            const uint32_t k0 = (uint32_t)(d * 256 + 4 * lane);
+            const uint32_t c[4] = {h[j].x & 0xFFFFu, h[j].x >> 16, h[j].y & 0xFFFFu, h[j].y >> 16};
+            if (!__any((c[0] | c[1] | c[2] | c[3]) != 0)) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c[e] && k0 + e >= kmin)
+                    ms += (uint64_t)c[e] * fixed_mass(fast_exp2((key_to_float(k0 + e) - m) * scale), qs);
+        }
+    }
+    return ms;
+}
+
+// Wave 0, any key span: top-p given the total fixed-point mass of the keys
+// >= kmin.  Digits are visited from the maximum's digit downwards; the first
+// non-empty digit whose cumulative mass reaches top_p * total holds the
+// threshold, which is the first non-empty key of that digit (from the top)
+// whose cumulative mass reaches it.  If rounding leaves the target above the
+// total, the threshold is the lowest non-empty key.  sh.sel_digit = the
+// threshold key, sh.sel_mass = the mass at or above it.  The masses are the
+// same expressions as in rr_total_mass.
+__device__ __noinline__ void rr_topp_topdown(RrShared& sh, int lane, uint32_t kmin, uint32_t mkey, float m,
+                                             float scale, int qs, float tp, uint64_t total) {
+    const uint2* h2 = reinterpret_cast<const uint2*>(sh.u.hist);
+    const double target = (double)tp * (double)total;
+    uint64_t above = 0;
+    int lowest = -1;   // lowest non-empty key seen
+    for (int d = (int)(mkey >> 8); d >= (int)(kmin >> 8); --d) {
+        const uint2 h = h2[d * 64 + lane];
+        const uint32_t k0 = (uint32_t)(d * 256 + 4 * lane);
+        uint32_t c[4] = {h.x & 0xFFFFu, h.x >> 16, h.y & 0xFFFFu, h.y >> 16};
+        uint64_t mk[4];
+        uint64_t lm = 0;
+        uint32_t lc = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (k0 + e < kmin) c[e] = 0;
+            mk[e] = c[e] ? (uint64_t)c[e] * fixed_mass(fast_exp2((key_to_float(k0 + e) - m) * scale), qs) : 0;
+            lm += mk[e];
+            lc += c[e];
+        }
+        const uint32_t dc = wave_allreduce(lc, OpAddU32{});
+        if (dc == 0) continue;
+        // keys of this digit in descending order: lane 63 first, e = 3 first
+        const uint64_t incl = wave_inclusive_sum(lm, lane);
+        const uint64_t dm = read_lane(incl, kWave - 1);
+        const uint64_t higher = dm - incl;   // mass of the keys in higher lanes
+        int lo = -1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (c[e] && lo < 0) lo = (int)(k0 + e);
+        lowest = wave_allreduce(lo < 0 ? 0x7FFFFFFF : lo, [](int x, int y) { return x < y ? x : y; });
+        if ((double)(above + dm) >= target) {
+            const uint64_t ball = __ballot(lc > 0 && (double)(above + higher + lm) >= target);
+            const int ls = 63 - __builtin_clzll((unsigned long long)ball);   // highest lane = highest keys
+            if (lane == ls) {
+                uint64_t run = above + higher;
+                for (int e = 3; e >= 0; --e) {
+                    if (c[e] && (double)(run + mk[e]) >= target) {
+                        sh.sel_digit = k0 + e;
+                        sh.sel_mass = run + mk[e];
+                        break;
+                    }
+                    run += mk[e];
+                }
+            }
+            return;
+        }
+        above += dm;
+    }
+    // rounding left the target above the total: keep everything present
+    if (lane == 0) {
+        sh.sel_digit = (uint32_t)lowest;
+        sh.sel_mass = total;
+    }
+}
+
 // One row whose input and output are 16-byte aligned, with V a multiple of
 // 8: every 16-byte vector lies wholly inside or wholly past the end of the
 // row, and all vectors move with buffer loads and stores, whose range check
@@ -765,24 +732,11 @@ __device__ __forceinline__ bool rr_row(RrShared& sh, const uint16_t* __restrict_
         kmin = sh.sel_digit;
         S = (double)sh.sel_mass * ldexp(1.0, -qs);
     } else if (tp < 1.0f) {
-        const uint64_t total = rr_block_reduce(sh, tid, rr_digit_masses(sh, tid, kmin, m, scale, qs), OpSumU64{});
-        const double target = (double)tp * (double)total;
-        if (tid < kWave) rr_select(sh, tid, true, 0, 0, target);
+        const uint64_t total = rr_block_reduce(sh, tid, rr_total_mass(sh, tid, kmin, m, scale, qs), OpSumU64{});
+        if (tid < kWave) rr_topp_topdown(sh, tid, kmin, mkey, m, scale, qs, tp, total);
         lds_barrier();
-        const uint32_t hi = sh.sel_digit;
-        const uint64_t above = sh.sel_above;
-        lds_barrier();
-        if (tid < 256) {
-            const uint32_t key = hi * 256 + tid;
-            const uint32_t c = key >= kmin ? hist_count(sh, key) : 0u;
-            sh.cc[tid] = c;
-            sh.cm[tid] = c ? (uint64_t)c * fixed_mass(fast_exp2((key_to_float(key) - m) * scale), qs) : 0;
-        }
-        lds_barrier();
-        if (tid < kWave) rr_select(sh, tid, true, 0, above, target);
-        lds_barrier();
-        kmin = (hi << 8) | sh.sel_digit;
-        S = (double)(sh.sel_above + sh.sel_mass) * ldexp(1.0, -qs);
+        kmin = sh.sel_digit;
+        S = (double)sh.sel_mass * ldexp(1.0, -qs);
     } else if (direct) {
         if (tid < kWave) {
             const double ws = rr_span_weight(sh, tid, kmin, mkey, m, scale);
