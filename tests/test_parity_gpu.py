@@ -192,6 +192,48 @@ def test_chain_reject_one_workgroup_per_request(sv):
         assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, V, special))
 
 
+def test_chain_reject_large_batches(sv):
+    """Batches of long rows, with rows split over several workgroups (partial
+    sums published, last workgroup locates) and with one workgroup per
+    request: a ragged last chunk, up to 1024 requests, all-bonus and
+    all-residual batches, degenerate rows, and a request subset with skipped
+    and repeated indices."""
+    cases = ((64, 5, 65536, None), (300, 3, 16424, None), (1024, 3, 4096, None), (130, 4, 32768, "zeros"),
+             (110, 2, 40000, "equal"), (140, 2, 30000, "disjoint"), (70, 7, 60000, None), (160, 0, 65536, None))
+    flagged = 0
+    for B, D, V, special in cases:
+        c = fuzz_case(900 + B + V, B, D, V, "f32", special=special)
+        log(f"chain large batch: B={B} D={D} V={V} special={special}")
+        ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
+        acc, acc_full = guarded_i32((B, D + 1))
+        alen, alen_full = guarded_i32((B,))
+        sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]), dev(c["seed"]),
+                        dev(c["offset"]), out=(acc, alen))
+        flagged += assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, V, special))
+        assert guard_intact(acc_full, B * (D + 1)) and guard_intact(alen_full, B)
+        if special == "equal":
+            assert np.all(np_i(alen) == D)
+        if special == "disjoint":
+            assert np.all(np_i(alen) == 0)
+    # request subset: skipped (-1, B) and repeated entries
+    B, D, V = 400, 4, 20000
+    c = fuzz_case(977, B, D, V, "f32")
+    rng = np.random.default_rng(5)
+    reqs = rng.permutation(B)[:300].astype(np.int32)
+    reqs[10], reqs[20], reqs[30] = -1, B, reqs[40]
+    log(f"chain large batch subset: B={B} D={D} V={V} n_req={len(reqs)}")
+    ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
+    acc = __import__("torch").full((B, D + 1), SENTINEL, dtype=__import__("torch").int32, device="cuda")
+    alen = __import__("torch").full((B,), SENTINEL, dtype=__import__("torch").int32, device="cuda")
+    sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]), dev(c["seed"]),
+                    dev(c["offset"]), req_index=dev(reqs), out=(acc, alen))
+    done = sorted({int(r) for r in reqs if 0 <= r < B})
+    flagged += assert_chain_match(np_i(acc), np_i(alen), ref, done, "large batch subset")
+    rest = np.setdiff1d(np.arange(B), done)
+    assert np.all(np_i(acc)[rest] == SENTINEL) and np.all(np_i(alen)[rest] == SENTINEL)
+    log(f"chain large batch flagged requests: {flagged}")
+
+
 def test_chain_reject_request_subset_and_determinism(sv):
     B, D, V = 9, 4, 3001
     c = fuzz_case(91, B, D, V, "f32")
