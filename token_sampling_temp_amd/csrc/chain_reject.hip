@@ -5,9 +5,10 @@
 // about one workgroup per CU (a large batch gets one workgroup per request).
 //
 // 1. Probe (every workgroup of a request, redundantly; the lines are shared
-//    in L2): thread i < D loads p_i(x_i), q_i(x_i) and the Philox uniform u_i
-//    and decides u_i * q < p exactly in double; thread D takes the final
-//    uniform.  L = first rejected position (D if none).
+//    in L2): lane i < D of wave 0 loads p_i(x_i), q_i(x_i), forms the Philox
+//    uniform u_i while those loads are in flight and decides u_i * q < p
+//    exactly in double; lane D takes the final uniform.  L = first rejected
+//    position (D if none), from a ballot.
 // 2. Segment pass: r_v = max(0, p_L[v] - q_L[v]) (or p_D[v] for the bonus) is
 //    summed in double per 1024-entry chunk; waves stream their chunks with
 //    several rounds of 16-byte loads in flight, one sum per chunk.
@@ -46,7 +47,6 @@ constexpr int kFallbackChunks = 512;
 
 struct ChainShared {
     double chunk[kFallbackChunks];
-    int acc[kMaxDraft];
     uint32_t code;
     int L;
     int last;
@@ -370,6 +370,8 @@ __device__ __forceinline__ double stream_chunks_fast(const float* pr, const floa
     return mine;
 }
 
+// kDraft: D > 0 (the probe loads draft ids and probabilities).
+template <bool kDraft>
 __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const float* __restrict__ q, const int32_t* __restrict__ x, const float* __restrict__ p,
     const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
@@ -388,31 +390,33 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const int N = D + 1;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
 
-    // ---- 1. probe
+    // ---- 1. probe (wave 0): lane i < D tests position i, lane D draws u_f.
+    // The loads at the draft ids are issued before the Philox rounds, so the
+    // rounds overlap their round trip; the first reject comes from a ballot.
     if (tid <= D) {
-        const uint32_t w = philox_word(seed[b], offset[b], (uint64_t)tid);
-        if (tid < D) {
-            const int32_t xi = x[b * D + tid];
-            bool ok = false;
-            if (xi >= 0 && (int64_t)xi < V) {
-                const float a = p[(b * N + tid) * V + xi];
-                const float cq = q[(b * D + tid) * V + xi];
-                ok = (double)uniform_of(w) * (double)cq < (double)a;
-            }
-            sh.acc[tid] = ok ? 1 : 0;
+        uint32_t w;
+        bool ok = false;
+        if constexpr (kDraft) {
+            // lanes 0 and 1 (both active: D >= 1) fetch seed and offset with
+            // the id loads; lane D repeats lane D-1's loads (in bounds), so no
+            // lane branches and the Philox rounds overlap the draft-probability
+            // round trip
+            const uint64_t so = ((tid & 1) ? offset : seed)[b];
+            const int ic = tid < D ? tid : D - 1;
+            const int32_t xi = x[b * D + ic];
+            const bool inr = tid < D && xi >= 0 && (int64_t)xi < V;
+            const int64_t xc = inr ? (int64_t)xi : 0;
+            const float a = p[(b * N + ic) * V + xc];
+            const float cq = q[(b * D + ic) * V + xc];
+            __builtin_amdgcn_sched_barrier(0);
+            w = philox_word(read_lane(so, 0), read_lane(so, 1), (uint64_t)tid);
+            ok = inr && (double)uniform_of(w) * (double)cq < (double)a;
         } else {
-            sh.code = uniform_code(w);
+            w = philox_word(seed[b], offset[b], (uint64_t)tid);
         }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int L = D;
-        for (int i = 0; i < D; ++i)
-            if (!sh.acc[i]) {
-                L = i;
-                break;
-            }
-        sh.L = L;
+        if (tid == D) sh.code = uniform_code(w);
+        const uint64_t rej = __ballot(tid < D && !ok);
+        if (tid == 0) sh.L = rej ? __ffsll((unsigned long long)rej) - 1 : D;
     }
     __syncthreads();
     const int L = sh.L;
@@ -562,9 +566,10 @@ hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_id
     const int64_t per_xcd = (total + 7) / 8;
     const int64_t grid = per_xcd * 8;
     if (grid > 2147483647LL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(chain_reject_kernel, dim3((unsigned)grid), dim3(kChainBlock), 0, stream, draft_probs,
-                       draft_ids, target_probs, seed, offset, B, D, V, req_index, n_req, C, R, per_xcd, accepted,
-                       accept_len, partial, counter);
+    auto* kernel = D > 0 ? chain_reject_kernel<true> : chain_reject_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kChainBlock), 0, stream, draft_probs, draft_ids,
+                       target_probs, seed, offset, B, D, V, req_index, n_req, C, R, per_xcd, accepted, accept_len,
+                       partial, counter);
     return hipGetLastError();
 }
 
