@@ -20,9 +20,12 @@ __global__ __launch_bounds__(kGreedyBlock) void greedy_verify_kernel(
     int32_t* __restrict__ predict, int32_t* __restrict__ accept_index, int32_t* __restrict__ argmax_out) {
     __shared__ ArgmaxShared<kGreedyBlock> sh;
     __shared__ int32_t s_y[kMaxDraft + 1];
+    __shared__ int32_t s_x[kMaxDraft];
     const int64_t b = req_index ? (int64_t)req_index[blockIdx.x] : (int64_t)blockIdx.x;
     if (b < 0 || b >= B) return;
     const int N = D + 1;
+    // draft ids fetched up front (visible after the first row's reduction)
+    if (threadIdx.x < D) s_x[threadIdx.x] = draft_ids[(int64_t)b * D + threadIdx.x];
     const bool all_rows = argmax_out != nullptr;
     int L = -1;
     int rows = 0;
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(kGreedyBlock) void greedy_verify_kernel(
         const int64_t y = row_argmax<kGreedyBlock, true>(row, V, sh);
         if (threadIdx.x == 0) s_y[j] = (int32_t)y;
         rows = j + 1;
-        if (L < 0 && (j == D || draft_ids[(int64_t)b * D + j] != (int32_t)y)) {
+        if (L < 0 && (j == D || s_x[j] != (int32_t)y)) {
             L = j;
             if (!all_rows) break;
         }
