@@ -25,4 +25,5 @@ from .verify import (  # noqa: F401
     residual_draw,
     softmax_renorm,
     temperature_softmax,
+    verify_fused,
 )

@@ -254,6 +254,69 @@ def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, requests=No
     return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
 
 
+# --------------------------------------------------------------------------- fused target rows + chain rejection
+def verify_fused(logits, dtype, temperature, top_k, top_p, draft_probs, draft_ids, seed, offset, requests=None):
+    """Target rows from logits, then chain rejection, as one call.
+
+    tokenspeed flashinfer.py, ``verify``: the target probabilities are the
+    temperature softmax of the logits followed by top-k and then top-p
+    renormalisation, and the chain verify consumes them; TensorRT-LLM's
+    fused sampling ops are the pages' reason to compute both without
+    materialising the probabilities.  Definition: row j of request b is
+    ``renorm_row(z_bj, T_b, k_b, top_p_b)`` (float64) and the outputs are
+    ``chain_reject_core`` on those rows with the request's draft probs, draft
+    ids and uniforms.  Only rows 0..L are needed, and only those are
+    computed.
+
+    Returns the ``chain_reject`` dictionary.  Here ``flag_pos`` also covers
+    the decisions a float32 implementation takes from differently rounded
+    target probabilities: a near-threshold accept test at position i (from i
+    on), a top-p boundary flag on a row j <= L (from j on), and a near CDF
+    boundary (from L on).
+    """
+    B, N, V = np.shape(logits)
+    D = N - 1
+    x = np.asarray(draft_ids)
+    tokens = np.full((B, N), -2, dtype=np.int64)
+    L = np.full(B, -2, dtype=np.int64)
+    flag_pos = np.full(B, N, dtype=np.int64)
+    near_accept = np.full(B, -1, dtype=np.int64)
+    reqs = range(B) if requests is None else [int(r) for r in requests]
+    for b in reqs:
+        z = decode_logits(logits[b], dtype)
+        k = 0 if top_k is None else int(top_k[b])
+        tp = 1.0 if top_p is None else float(top_p[b])
+        T = float(temperature[b])
+        ua, uf, code = chain_uniforms(int(seed[b]), int(offset[b]), D)
+        rows, row_flag = [], []
+        # rows 0..L: row j is needed once positions 0..j-1 are accepted
+        for j in range(N):
+            pj, fj = renorm_row(z[j], T, k, tp)
+            rows.append(pj)
+            row_flag.append(fj)
+            if j < D:
+                xj = int(x[b, j])
+                if not (0 <= xj < V and float(ua[j]) * float(draft_probs[b, j, xj]) < pj[xj]):
+                    break
+        P = np.zeros((N, V))
+        P[:len(rows)] = np.array(rows)
+        res = chain_reject_core(draft_probs[b], x[b], P, ua, uf, code)
+        tokens[b] = res["tokens"]
+        L[b] = res["L"]
+        fp = N
+        if res["near_cdf"]:
+            fp = res["L"]
+        if res["near_accept"] is not None:
+            near_accept[b] = res["near_accept"]
+            fp = min(fp, res["near_accept"])
+        for j in range(res["L"] + 1):
+            if row_flag[j]:
+                fp = min(fp, j)
+                break
+        flag_pos[b] = fp
+    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
+
+
 # --------------------------------------------------------------------------- greedy verify
 def greedy_verify(logits, dtype, draft_ids, requests=None):
     """Greedy chain verify.
