@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large_vocab_chain_reject",
-                    choices=["large_vocab_chain_reject", "topk_topp_chain", "greedy", "mixed"])
+                    choices=["large_vocab_chain_reject", "topk_topp_chain", "greedy", "mixed", "mixed_fused"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -113,7 +113,7 @@ class ChainWorkload:
     """B=256 D=5 V=128256 chain rejection on float32 probabilities."""
     name = "large_vocab_chain_reject"
     kernel = "chain_reject_kernel"
-    sources = ("chain_reject.hip", "sv_common.hpp")
+    sources = ("chain_reject.hip", "sv_draw.hpp", "sv_common.hpp")
     counters = "chain_reject_large_vocab_counters.txt"
     dtype = "f32"
 
@@ -239,7 +239,7 @@ class GreedyWorkload:
 class TopkToppWorkload:
     name = "topk_topp_chain"
     kernel = "softmax_renorm_rr_kernel"
-    sources = ("softmax_renorm.hip", "sv_argmax.hpp", "sv_common.hpp")
+    sources = ("softmax_renorm.hip", "sv_softmax.hpp", "sv_argmax.hpp", "sv_common.hpp")
     counters = "softmax_renorm_topk_topp_counters.txt"
     dtype = "bf16"
 
@@ -320,7 +320,7 @@ class MixedWorkload:
     """B=1024 D=7 V=129280 bf16 logits, 256 requests per mode, each mode through req_index."""
     name = "mixed"
     kernel = "softmax_renorm_rr_kernel"
-    sources = ("softmax_renorm.hip", "sv_argmax.hpp", "sv_common.hpp")
+    sources = ("softmax_renorm.hip", "sv_softmax.hpp", "sv_argmax.hpp", "sv_common.hpp")
     counters = "softmax_renorm_mixed_counters.txt"
     dtype = "bf16"
 
@@ -435,7 +435,49 @@ class MixedWorkload:
                 "sample": f"{n} requests (random order over all modes), {el:.1f}s single-threaded numpy"}
 
 
-WORKLOADS = {c.name: c for c in (ChainWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload)}
+class MixedFusedWorkload(MixedWorkload):
+    """The mixed batch with its top-k and top-p requests through the fused call
+    (target rows from logits and chain rejection in one launch, no probabilities
+    stored): greedy_verify, gumbel_sample, verify_fused."""
+    name = "mixed_fused"
+    kernel = "verify_fused_kernel"
+    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_common.hpp")
+    counters = "verify_fused_mixed_counters.txt"
+
+    def __init__(self, dev, replicas):
+        super().__init__(dev, replicas)
+        self.calls = {"greedy_verify": self.greedy, "gumbel_sample": self.gumbel, "verify_fused": self.fused}
+
+    def fused(self, i=0):
+        self.sv.verify_fused(self.z, self.T, self.q, self.x, self.seed, self.off, top_k=self.k, top_p=self.p,
+                             req_index=self.filt_idx, out=(self.acc, self.alen))
+
+    def step(self, i):
+        self.greedy(i)
+        self.gumbel(i)
+        self.fused(i)
+
+    def algorithmic_bytes(self):
+        from workloads import MODE_GREEDY, MODE_TEMPERATURE
+        self.step(0)
+        L = self.alen.cpu().numpy().astype(np.int64)
+        self.L = L
+        D, V = self.D, self.V
+        g = self.idx_host[MODE_GREEDY]
+        t = self.idx_host[MODE_TEMPERATURE]
+        f = self.filt_host
+        # logit rows 0..L, the draft row q_L on a rejection, q at the ids probed
+        self.bytes_by_call = {
+            "greedy_verify": float(((L[g] + 1) * V * 2).sum()),
+            "gumbel_sample": float(((L[t] + 1) * V * 2).sum()),
+            "verify_fused": float(((L[f] + 1) * V * 2 + np.where(L[f] < D, 4 * V, 0)
+                                   + PROBE_GRANULE * np.minimum(L[f] + 1, D)).sum()),
+        }
+        return self.bytes_by_call["verify_fused"]
+
+
+WORKLOADS = {c.name: c for c in (ChainWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
+                                 MixedFusedWorkload)}
 
 
 def per_call_times(wl, steps):

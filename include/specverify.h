@@ -31,10 +31,10 @@
  *   rejection_sampling_one_model docstring).
  * - stream is a hipStream_t passed as void*; NULL is the default stream.
  *   Calls are asynchronous; nothing is read back to the host.  The library
- *   never synchronises.  specverify_softmax_renorm, specverify_greedy_verify
- *   and specverify_gumbel_sample use no device memory besides their
- *   arguments; specverify_chain_reject keeps a library-owned workspace (see
- *   there).
+ *   never synchronises.  specverify_softmax_renorm, specverify_greedy_verify,
+ *   specverify_gumbel_sample and specverify_verify_fused use no device memory
+ *   besides their arguments; specverify_chain_reject keeps a library-owned
+ *   workspace (see there).
  * - Host-side validation runs before any HIP call.  Return codes:
  *   SPECVERIFY_OK, SPECVERIFY_INVALID_ARGUMENT (nothing launched),
  *   SPECVERIFY_UNSUPPORTED (current device is not gfx950),
@@ -189,6 +189,38 @@ int specverify_gumbel_sample(const void* target_logits, int dtype, const float* 
                              const uint64_t* offset, int64_t B, int64_t D, int64_t V,
                              const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
                              int32_t* accept_length, int32_t* sampled_out, void* stream);
+
+/*
+ * Fused verify: target rows from logits, then chain rejection, in one call.
+ *
+ * Passage: "tokenspeed sampling/backends/flashinfer.py",
+ * FlashInferSamplingBackend.verify -- the target probabilities are the
+ * temperature softmax followed by top-k and then top-p renormalisation, and
+ * the chain verify consumes them; the page's aim of keeping the verify hot
+ * path to two kernels and "TensorRT-LLM" fused sampling ops motivate one
+ * launch that never writes the probabilities.
+ *
+ * target_logits   [B, D+1, V] dtype
+ * temperature     [B] float; top_k [B] int32 or NULL; top_p [B] float or NULL
+ *                 (the meanings of specverify_softmax_renorm)
+ * draft_probs     [B, D, V] float (may be NULL when D == 0)
+ * draft_ids       [B, D] int32 (may be NULL when D == 0)
+ * seed, offset    [B] uint64
+ * accepted_tokens [B, D+1] int32   output
+ * accept_length   [B] int32        output
+ *
+ * Equivalent to specverify_softmax_renorm on the logits followed by
+ * specverify_chain_reject on its output (same tokens whenever that output
+ * buffer is 16-byte aligned), except that only logit rows 0..L of a request
+ * are read and no probability is stored.  V <= 524288.  Uses no device
+ * memory besides its arguments.
+ */
+int specverify_verify_fused(const void* target_logits, int dtype, const float* temperature,
+                            const int32_t* top_k, const float* top_p, const float* draft_probs,
+                            const int32_t* draft_ids, const uint64_t* seed, const uint64_t* offset,
+                            int64_t B, int64_t D, int64_t V, const int32_t* req_index,
+                            int64_t n_req, int32_t* accepted_tokens, int32_t* accept_length,
+                            void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* specverify_status_string(int status);

@@ -98,6 +98,25 @@ def test_greedy_and_gumbel_and_softmax_invalid_arguments():
     assert L.specverify_softmax_renorm(None, 1, 0, 2, 10, None, None, None, None, 0, None, None) == 0
 
 
+def test_verify_fused_invalid_arguments():
+    L = sv.lib()
+    # (logits, dtype, T, top_k, top_p, q, x, seed, offset, B, D, V, req_index, n_req, acc, alen, stream)
+    assert L.specverify_verify_fused(P, 3, P, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert "dtype=3" in L.specverify_last_error().decode()
+    assert L.specverify_verify_fused(P, 1, None, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert "temperature" in L.specverify_last_error().decode()
+    assert L.specverify_verify_fused(P, 1, P, None, None, None, P, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert "draft_probs" in L.specverify_last_error().decode()
+    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 17, 10, None, 4, P, P, None) == 1
+    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 3, 600000, None, 4, P, P, None) == 1
+    assert "exceeds" in L.specverify_last_error().decode()
+    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, None, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert "seed" in L.specverify_last_error().decode()
+    # n_req = 0 is a no-op that touches no device
+    assert L.specverify_verify_fused(None, 0, None, None, None, None, None, None, None, 4, 3, 10, P, 0, None, None,
+                                     None) == 0
+
+
 def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     z = torch.zeros(2, 3, 8)

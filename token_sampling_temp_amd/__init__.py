@@ -35,6 +35,7 @@ SYMBOLS = (
     "specverify_chain_reject",
     "specverify_greedy_verify",
     "specverify_gumbel_sample",
+    "specverify_verify_fused",
     "specverify_status_string",
     "specverify_last_error",
     "specverify_version",
@@ -66,8 +67,9 @@ def lib() -> ctypes.CDLL:
     L.specverify_chain_reject.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
     L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
+    L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
     for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_greedy_verify",
-                 "specverify_gumbel_sample"):
+                 "specverify_gumbel_sample", "specverify_verify_fused"):
         getattr(L, name).restype = ctypes.c_int
     L.specverify_status_string.argtypes = [ctypes.c_int]
     L.specverify_status_string.restype = ctypes.c_char_p
@@ -190,6 +192,43 @@ def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=N
         _ptr(draft_probs), _ptr(draft_ids), _ptr(target_probs), _ptr(seed), _ptr(offset), B, D, V,
         _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
     _check("specverify_chain_reject", st)
+    return acc, alen
+
+
+def verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None, top_p=None,
+                 req_index=None, out=None):
+    """Target rows from logits (softmax, top-k, top-p) then chain rejection, in one launch;
+    returns (accepted_tokens [B, D+1] int32, accept_length [B] int32)."""
+    torch = _torch()
+    _need(target_logits, "target_logits", (torch.float32, torch.bfloat16), None, 3)
+    dev = target_logits.device
+    B, N, V = target_logits.shape
+    D = N - 1
+    _need(temperature, "temperature", (torch.float32,), dev, 1)
+    if top_k is not None:
+        _need(top_k, "top_k", (torch.int32,), dev, 1)
+    if top_p is not None:
+        _need(top_p, "top_p", (torch.float32,), dev, 1)
+    for name, t in (("temperature", temperature), ("top_k", top_k), ("top_p", top_p)):
+        if t is not None and t.shape[0] != B:
+            raise ValueError(f"{name} must have shape [{B}]")
+    _need(draft_probs, "draft_probs", (torch.float32,), dev, 3)
+    _need(draft_ids, "draft_ids", (torch.int32,), dev, 2)
+    if tuple(draft_probs.shape) != (B, D, V) or tuple(draft_ids.shape) != (B, D):
+        raise ValueError(f"draft_probs must be [{B},{D},{V}] and draft_ids [{B},{D}]")
+    _u64(seed, "seed", B, dev)
+    _u64(offset, "offset", B, dev)
+    req_index, n_req = _req(req_index, B, dev)
+    if out is None:
+        acc = torch.empty((B, N), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        acc, alen = out
+    st = lib().specverify_verify_fused(
+        _ptr(target_logits), _logit_dtype(target_logits), _ptr(temperature), _ptr(top_k), _ptr(top_p),
+        _ptr(draft_probs), _ptr(draft_ids), _ptr(seed), _ptr(offset), B, D, V, _ptr(req_index), n_req, _ptr(acc),
+        _ptr(alen), _stream_ptr(dev))
+    _check("specverify_verify_fused", st)
     return acc, alen
 
 

@@ -240,6 +240,35 @@ int specverify_gumbel_sample(const void* target_logits, int dtype, const float* 
                                                  sampled_out, static_cast<hipStream_t>(stream)));
 }
 
+int specverify_verify_fused(const void* target_logits, int dtype, const float* temperature, const int32_t* top_k,
+                            const float* top_p, const float* draft_probs, const int32_t* draft_ids,
+                            const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D, int64_t V,
+                            const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
+                            int32_t* accept_length, void* stream) {
+    const char* fn = "specverify_verify_fused";
+    SV_TRY(check_dtype(fn, dtype));
+    SV_TRY(check_draft(fn, D));
+    SV_TRY(check_sizes(fn, B, D + 1, V, req_index, n_req, 4));
+    if (V > sv::verify_fused_max_vocab())
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: V=%lld exceeds %lld", fn, (long long)V,
+                    (long long)sv::verify_fused_max_vocab());
+    if (n_req == 0) return SPECVERIFY_OK;
+    SV_REQUIRE(target_logits, "target_logits");
+    SV_REQUIRE(temperature, "temperature");
+    if (D > 0) {
+        SV_REQUIRE(draft_probs, "draft_probs");
+        SV_REQUIRE(draft_ids, "draft_ids");
+    }
+    SV_REQUIRE(seed, "seed");
+    SV_REQUIRE(offset, "offset");
+    SV_REQUIRE(accepted_tokens, "accepted_tokens");
+    SV_REQUIRE(accept_length, "accept_length");
+    SV_TRY(check_device());
+    return launched(fn, sv::launch_verify_fused(target_logits, dtype, temperature, top_k, top_p, draft_probs,
+                                                draft_ids, seed, offset, B, (int)D, V, req_index, n_req,
+                                                accepted_tokens, accept_length, static_cast<hipStream_t>(stream)));
+}
+
 const char* specverify_status_string(int status) {
     switch (status) {
         case SPECVERIFY_OK: return "SPECVERIFY_OK";

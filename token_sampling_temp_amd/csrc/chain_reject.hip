@@ -22,7 +22,7 @@
 //    reproducible run to run.
 // 4. Degenerate rows (residual mass not positive) fall back to a draw from the
 //    target row by the same workgroup, then to floor(u_f * V).
-#include "sv_common.hpp"
+#include "sv_draw.hpp"
 #include "sv_launch.hpp"
 
 #ifndef SV_CHAIN_TARGET_WGS
@@ -63,10 +63,6 @@ __device__ __forceinline__ void load4(const float* row, int64_t idx, int64_t V, 
     }
 }
 
-__device__ __forceinline__ double rval(float pv, float qv, bool resid) {
-    return resid ? fmax(0.0, (double)pv - (double)qv) : (double)pv;
-}
-
 template <bool NT>
 __device__ __forceinline__ void lane_r4(const float* pr, const float* qr, bool resid, int64_t V, bool aligned,
                                         int64_t idx, double (&r)[4]) {
@@ -92,12 +88,6 @@ __device__ __forceinline__ void load_run(const float* row, int64_t base, int64_t
 #pragma unroll
         for (int k = 0; k < NSUB; ++k) load4<NT>(row, base + (k * kWave + lane) * 4, V, aligned, f[k]);
     }
-}
-
-// Inclusive 64-lane scan (DPP, fixed association order).
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v) {
-    return wave_inclusive_sum(v, (int)(threadIdx.x & (kWave - 1)));
 }
 
 // Search NSUB sub-tiles (64 lanes x 4 entries each; index order sub-tile,
@@ -162,62 +152,6 @@ __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int
         total += tot;
     }
     return -1;
-}
-
-// Wave 0 of the block: given 'n' ordered non-negative masses m[0..n) (read
-// through `get`), total R and target T = uf * R, find the first index whose
-// running mass exceeds T (only positive entries qualify).  Returns the index
-// and the mass before it; force_last is set when rounding left T beyond every
-// positive entry (then the index is the last positive one).
-template <typename Get>
-__device__ int wave_pick(int n, Get get, double& R, double uf, double& base, int& force_last) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int g = (n + kWave - 1) / kWave;
-    const int i0 = min(n, lane * g), i1 = min(n, i0 + g);
-    double lt = 0.0;
-    for (int i = i0; i < i1; ++i) lt += get(i);
-    const double incl = wave_incl_scan(lt);
-    const double ex = wave_shift_up1(incl);
-    R = read_lane(incl, kWave - 1);
-    base = 0.0;
-    force_last = 0;
-    if (!(R > 0.0)) return -1;
-    const double T = uf * R;
-    const uint64_t ball = __ballot(incl > T && lt > 0.0);
-    int pick = -1;
-    if (ball) {
-        const int ls = __ffsll((unsigned long long)ball) - 1;
-        if (lane == ls) {
-            double run = ex;
-            int lastp = -1;
-            for (int i = i0; i < i1; ++i) {
-                const double si = get(i);
-                if (si > 0.0) {
-                    lastp = i;
-                    if (run + si > T) {
-                        pick = i;
-                        base = run;
-                        break;
-                    }
-                }
-                run += si;
-            }
-            if (pick < 0) {
-                pick = lastp;
-                force_last = 1;
-            }
-        }
-        pick = read_lane(pick, ls);
-        base = read_lane(base, ls);
-        force_last = read_lane(force_last, ls);
-    } else {
-        int lp = -1;
-        for (int i = i0; i < i1; ++i)
-            if (get(i) > 0.0) lp = i;
-        pick = wave_allreduce(lp, [](int a, int b) { return a > b ? a : b; });
-        force_last = 1;
-    }
-    return pick;
 }
 
 // Single-workgroup inverse-CDF draw over a whole row (only for the

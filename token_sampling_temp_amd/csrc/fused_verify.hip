@@ -1,0 +1,416 @@
+// Fused verify: target probabilities from logits (temperature softmax, then
+// top-k, then top-p renormalisation) and chain rejection of a linear draft in
+// one launch, without writing the probabilities.
+//
+// One 1024-thread workgroup per request walks the target rows j = 0..D in
+// order.  For row j it computes the row's statistics with the softmax kernels'
+// own row algorithms (register-resident for bf16 rows that fit, streamed
+// otherwise, the argmax for one-hot rows), evaluates p_j at the draft id x_j
+// and stops at the first rejection, so only logit rows 0..L are read.  The
+// residual max(0, p_L - q_L) (or the bonus row p_D) is then drawn by inverse
+// CDF over ascending vocabulary index: double sums per 1024-entry chunk,
+// prefix over the chunk sums, search inside the chosen chunk.  Probability
+// values, chunk sums, their order and the search are those of softmax_renorm
+// followed by chain_reject (with a 16-byte aligned probability buffer), so the
+// two paths return the same tokens.
+#include <atomic>
+#include <type_traits>
+
+#include "sv_draw.hpp"
+#include "sv_launch.hpp"
+#include "sv_softmax.hpp"
+
+namespace sv {
+
+constexpr int kFvBlock = 1024;
+static_assert(kFvBlock == kRrBlock && kFvBlock == kSmBlock, "one block size for every row algorithm");
+constexpr int kFvWaves = kFvBlock / kWave;
+constexpr int64_t kFvChunk = 1024;   // entries per chunk sum
+constexpr int kFvMaxChunks = 512;    // V <= 524288
+
+struct FusedShared {
+    RrShared rr;                  // histogram / probability table / streamed and argmax state
+    double chunk[kFvMaxChunks];   // chunk sums of the drawn row
+    int32_t xs[kMaxDraft];        // draft ids
+    float qx[kMaxDraft];          // q_i(x_i), 0 for an id outside [0, V)
+    uint32_t zx[kMaxDraft];       // bits of the logit z_i(x_i)
+    uint32_t code[kMaxDraft + 1]; // uniform codes: accept tests 0..D-1, final draw D
+    int acc;
+    int64_t y;
+};
+
+// How one row's probabilities are evaluated.
+enum : int { kProbOneHot = 0, kProbTable = 1, kProbRrExp = 2, kProbStreamed = 3 };
+struct RowProb {
+    int mode;
+    float m, scale, inv;
+    uint32_t kmin;
+    int64_t y;   // one-hot index
+};
+
+__device__ __forceinline__ float raw_value(uint16_t h) { return bf16_to_float(h); }
+__device__ __forceinline__ float raw_value(float f) { return f; }
+
+// Probability of entry idx whose logit has the bits `raw`: the value the
+// softmax kernels write for it under the same statistics.
+template <typename T>
+__device__ __forceinline__ float row_prob(const RowProb rp, const RrShared& sh, T raw, int64_t idx) {
+    if (rp.mode == kProbOneHot) return idx == rp.y ? 1.0f : 0.0f;
+    if constexpr (sizeof(T) == 2) {
+        if (rp.mode == kProbTable || rp.mode == kProbRrExp) {
+            const uint32_t key = keys_of_pair((uint32_t)raw) & 0xFFFFu;
+            if (rp.mode == kProbTable) return sh.u.lut[max((int)key + 1 - (int)rp.kmin, 0)];
+            return key >= rp.kmin ? fast_exp2((key_to_float(key) - rp.m) * rp.scale) * rp.inv : 0.0f;
+        }
+    }
+    const float v = raw_value(raw);
+    return logit_key<T>(v) >= rp.kmin ? exp2f((v - rp.m) * rp.scale) * rp.inv : 0.0f;
+}
+
+// Four consecutive logits starting at idx (a multiple of 4); entries past V
+// read as 0 bits (their probability is forced to 0 by the caller).
+template <typename T>
+__device__ __forceinline__ void load_raw4(const T* row, int64_t idx, int64_t V, bool vec_ok, T (&r)[4]) {
+    if (vec_ok && idx + 3 < V) {
+        if constexpr (sizeof(T) == 2) {
+            const uint2 u = *reinterpret_cast<const uint2*>(row + idx);
+            r[0] = (uint16_t)(u.x & 0xFFFFu);
+            r[1] = (uint16_t)(u.x >> 16);
+            r[2] = (uint16_t)(u.y & 0xFFFFu);
+            r[3] = (uint16_t)(u.y >> 16);
+        } else {
+            const float4 f = *reinterpret_cast<const float4*>(row + idx);
+            r[0] = f.x;
+            r[1] = f.y;
+            r[2] = f.z;
+            r[3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = idx + e < V ? row[idx + e] : T{};
+    }
+}
+
+__device__ __forceinline__ void load_q4(const float* row, int64_t idx, int64_t V, bool vec_ok, float (&f)[4]) {
+    if (vec_ok && idx + 3 < V) {
+        unpack(load_vec<false>(row + idx, 0), f);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = idx + e < V ? row[idx + e] : 0.0f;
+    }
+}
+
+// Inverse-CDF draw of one index from r_v = max(0, p_v - q_v) (resid) or p_v,
+// p given by rp on the logit row zr.  Whole workgroup; returns -1 when the
+// weights have no positive mass.  Chunk c of 1024 entries is summed by one
+// wave as four sub-tiles of 64 lanes x 4 consecutive entries (lane sums of
+// four, then the sub-tiles in order, then the 64 lanes), wave 0 picks the
+// chunk holding u_f * R and scans it in index order.
+template <typename T, bool RESID>
+__device__ __forceinline__ int64_t fused_draw(FusedShared& sh, const RowProb rp, const T* __restrict__ zr,
+                              const float* __restrict__ qr, int64_t V, double uf) {
+    constexpr bool resid = RESID;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const bool zvec = (uintptr_t)zr % (4 * sizeof(T)) == 0;
+    const bool qvec = !resid || (uintptr_t)qr % 16 == 0;
+    const int nch = (int)((V + kFvChunk - 1) / kFvChunk);
+    auto weights = [&](int64_t idx, double (&r)[4]) {
+        T z[4];
+        float qf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        load_raw4<T>(zr, idx, V, zvec, z);
+        if constexpr (RESID) load_q4(qr, idx, V, qvec, qf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float pv = idx + e < V ? row_prob<T>(rp, sh.rr, z[e], idx + e) : 0.0f;
+            r[e] = rval(pv, qf[e], resid);
+        }
+    };
+    // acc = sum over sub-tiles k (in order) of the lane's sum of four
+    auto publish = [&](double acc, int c) {
+        acc = wave_allreduce(acc, OpSumD{});
+        if (lane == 0) sh.chunk[c] = acc;
+    };
+    // chunks wholly inside the row, with aligned rows: unconditional vector
+    // loads, two chunks of a wave in flight (wave w takes w, w + 16, ...)
+    const int nfull = (int)(V / kFvChunk);
+    int cdone = 0;   // chunks below this are summed
+    if (zvec && qvec) {
+        typedef typename std::conditional<sizeof(T) == 2, uint2, float4>::type ZV;
+        ZV zb[2][4];
+        u32x4 qb[2][4];
+        const int nr = nfull > wid ? (nfull - wid + kFvWaves - 1) / kFvWaves : 0;
+        auto ld = [&](int slot, int r) {
+            const int64_t base = (int64_t)(wid + r * kFvWaves) * kFvChunk + lane * 4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                zb[slot][k] = *reinterpret_cast<const ZV*>(zr + base + k * kWave * 4);
+                if constexpr (RESID) qb[slot][k] = load_vec<false>(qr + base + k * kWave * 4, 0);
+            }
+        };
+        auto sum = [&](int slot, int r) {
+            const int c = wid + r * kFvWaves;
+            double acc = 0.0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                T z[4];
+                if constexpr (sizeof(T) == 2) {
+                    z[0] = (uint16_t)(zb[slot][k].x & 0xFFFFu);
+                    z[1] = (uint16_t)(zb[slot][k].x >> 16);
+                    z[2] = (uint16_t)(zb[slot][k].y & 0xFFFFu);
+                    z[3] = (uint16_t)(zb[slot][k].y >> 16);
+                } else {
+                    z[0] = zb[slot][k].x;
+                    z[1] = zb[slot][k].y;
+                    z[2] = zb[slot][k].z;
+                    z[3] = zb[slot][k].w;
+                }
+                float qf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (RESID) unpack(qb[slot][k], qf);
+                const int64_t i0 = (int64_t)c * kFvChunk + (k * kWave + lane) * 4;
+                double s4 = 0.0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s4 += rval(row_prob<T>(rp, sh.rr, z[e], i0 + e), qf[e], resid);
+                acc += s4;
+            }
+            publish(acc, c);
+        };
+        if (nr >= 4) {
+            ld(0, 0);
+            ld(1, 1);
+            int r0 = 0;
+            for (; r0 + 4 <= nr; r0 += 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                sum(0, r0);
+                __builtin_amdgcn_sched_barrier(0);
+                ld(0, r0 + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                sum(1, r0 + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                ld(1, r0 + 3);
+            }
+            // rounds r0, r0 + 1 are in flight; at most one remains after them
+            sum(0, r0);
+            if (r0 + 2 < nr) ld(0, r0 + 2);
+            sum(1, r0 + 1);
+            if (r0 + 2 < nr) sum(0, r0 + 2);
+        } else {
+            for (int r = 0; r < nr; ++r) {
+                ld(0, r);
+                sum(0, r);
+            }
+        }
+        cdone = nfull;
+    }
+    // the rest (a partial last chunk, or every chunk of an unaligned row)
+    for (int c = cdone + wid; c < nch; c += kFvWaves) {
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            double r[4];
+            weights((int64_t)c * kFvChunk + (k * kWave + lane) * 4, r);
+            double s4 = 0.0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s4 += r[e];
+            acc += s4;
+        }
+        publish(acc, c);
+    }
+    __syncthreads();
+    if (wid == 0) {
+        double R, base;
+        int force_last;
+        const int cstar = wave_pick(nch, [&](int i) { return sh.chunk[i]; }, R, uf, base, force_last);
+        int64_t y = -1;
+        if (cstar >= 0) {
+            const int64_t cb = (int64_t)cstar * kFvChunk;
+            double r[4][4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) weights(cb + (k * kWave + lane) * 4, r[k]);
+            int64_t mylast = -1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (r[k][e] > 0.0) mylast = cb + (k * kWave + lane) * 4 + e;
+            const int64_t lastpos = wave_allreduce(mylast, [](int64_t a, int64_t b) { return a > b ? a : b; });
+            if (!force_last) {
+                const double Tt = uf * R;
+                double run = base;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (y >= 0) continue;   // wave-uniform
+                    const double s = ((r[k][0] + r[k][1]) + r[k][2]) + r[k][3];
+                    const double incl = wave_incl_scan(s);
+                    const double excl = wave_shift_up1(incl);
+                    const uint64_t hit = __ballot(run + incl > Tt && s > 0.0);
+                    if (hit) {
+                        const int ls = __ffsll((unsigned long long)hit) - 1;
+                        int64_t cand = -1;
+                        if (lane == ls) {
+                            const int64_t i0 = cb + (k * kWave + lane) * 4;
+                            double xr = run + excl;
+                            int last_e = -1;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if (cand >= 0) continue;
+                                if (r[k][e] > 0.0) last_e = e;
+                                xr += r[k][e];
+                                if (r[k][e] > 0.0 && xr > Tt) cand = i0 + e;
+                            }
+                            if (cand < 0) cand = i0 + last_e;
+                        }
+                        y = read_lane(cand, ls);
+                    } else {
+                        run += read_lane(incl, kWave - 1);
+                    }
+                }
+            }
+            if (y < 0) y = lastpos;
+        }
+        if (lane == 0) sh.y = y;
+    }
+    __syncthreads();
+    return sh.y;
+}
+
+// NV > 0: bf16 logits whose rows are 16-byte aligned with V a multiple of 8
+// and V <= 8192 * NV take the register-resident statistics (as the softmax
+// kernel does); NV = 0: streamed statistics for every temperature row.
+template <typename T, int NV>
+__global__ __launch_bounds__(kFvBlock) void verify_fused_kernel(
+    const T* __restrict__ logits, const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
+    const float* __restrict__ top_p, const float* __restrict__ q, const int32_t* __restrict__ x,
+    const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
+    const int32_t* __restrict__ req_index, int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len) {
+    __shared__ FusedShared sh;
+    const int64_t b = req_index ? (int64_t)req_index[blockIdx.x] : (int64_t)blockIdx.x;
+    if (b < 0 || b >= B) return;   // uniform over the workgroup
+    const int N = D + 1;
+    const int tid = threadIdx.x;
+    const float Tm = temperature[b];
+    const int32_t k = top_k ? top_k[b] : 0;
+    const float tp = top_p ? top_p[b] : 1.0f;
+
+    // draft ids, q at the ids and the uniform codes, read once
+    if (tid <= D) {
+        sh.code[tid] = uniform_code(philox_word(seed[b], offset[b], (uint64_t)tid));
+        if (tid < D) {
+            const int32_t xi = x[b * D + tid];
+            sh.xs[tid] = xi;
+            const bool inr = xi >= 0 && (int64_t)xi < V;
+            sh.qx[tid] = inr ? q[(b * D + tid) * V + xi] : 0.0f;
+            T zv{};
+            if (inr) zv = logits[(b * N + tid) * V + xi];
+            uint32_t bits = 0;
+            __builtin_memcpy(&bits, &zv, sizeof(T));
+            sh.zx[tid] = bits;
+        }
+    }
+    __syncthreads();
+
+    // ---- rows 0..L: statistics, then the accept test at the draft id
+    RowProb rp{kProbOneHot, 0.0f, 0.0f, 0.0f, 0u, 0};
+    int L = D;
+    for (int j = 0; j <= D; ++j) {
+        const T* row = logits + ((int64_t)b * N + j) * V;
+        if ((double)Tm < kGreedyTemperature) {
+            __syncthreads();   // the previous row's table may still be read
+            rp.mode = kProbOneHot;
+            rp.y = row_argmax<kFvBlock, false>(row, V, sh.rr.u.sm.am);
+        } else {
+            bool done = false;
+            if constexpr (NV > 0) {
+                u32x4 w[NV];
+                RrStats st;
+                if (rr_stats<NV>(sh.rr, reinterpret_cast<const uint16_t*>(row), V, Tm, k, tp, tid, w, st)) {
+                    rp = RowProb{st.table ? kProbTable : kProbRrExp, st.m, st.scale, st.inv, st.kmin, 0};
+                    done = true;
+                }
+            }
+            if (!done) {
+                __syncthreads();
+                const StreamStats ss = streamed_stats<T>(row, V, Tm, k, tp, sh.rr.u.sm);
+                rp = RowProb{kProbStreamed, ss.m, ss.scale, ss.inv, ss.kmin, 0};
+            }
+        }
+        if (j == D) break;
+        if (tid == 0) {
+            const int32_t xj = sh.xs[j];
+            bool ok = false;
+            if (xj >= 0 && (int64_t)xj < V) {
+                T zv;
+                const uint32_t bits = sh.zx[j];
+                __builtin_memcpy(&zv, &bits, sizeof(T));
+                const float pv = row_prob<T>(rp, sh.rr, zv, xj);
+                ok = (double)((float)sh.code[j] * 0x1p-24f) * (double)sh.qx[j] < (double)pv;
+            }
+            sh.acc = ok ? 1 : 0;
+        }
+        __syncthreads();
+        if (!sh.acc) {
+            L = j;
+            break;
+        }
+    }
+
+    // ---- draw from row L's residual (or the bonus row), then from the
+    // target row, then floor(u_f * V)
+    const bool resid = L < D;
+    const T* zr = logits + ((int64_t)b * N + L) * V;
+    const float* qr = resid ? q + ((int64_t)b * D + L) * V : nullptr;
+    const double uf = (double)sh.code[D] * 0x1p-24;
+    int64_t y = resid ? fused_draw<T, true>(sh, rp, zr, qr, V, uf)
+                      : fused_draw<T, false>(sh, rp, zr, nullptr, V, uf);
+    if (y < 0 && resid) y = fused_draw<T, false>(sh, rp, zr, nullptr, V, uf);
+    if (y < 0) y = (int64_t)(((uint64_t)sh.code[D] * (uint64_t)V) >> 24);
+    if (tid < N) {
+        int32_t t;
+        if (tid < L) t = sh.xs[tid];
+        else t = (tid == L) ? (int32_t)y : -1;
+        accepted[b * N + tid] = t;
+    }
+    if (tid == 0) accept_len[b] = L;
+}
+
+int64_t verify_fused_max_vocab() { return (int64_t)kFvMaxChunks * kFvChunk; }
+
+template <typename T, int NV>
+static void launch_fv(const T* logits, const float* temperature, const int32_t* top_k, const float* top_p,
+                      const float* q, const int32_t* x, const uint64_t* seed, const uint64_t* offset, int64_t B,
+                      int D, int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted,
+                      int32_t* accept_len, hipStream_t stream) {
+    hipLaunchKernelGGL((verify_fused_kernel<T, NV>), dim3((unsigned)n_req), dim3(kFvBlock), 0, stream, logits,
+                       temperature, top_k, top_p, q, x, seed, offset, B, D, V, req_index, accepted, accept_len);
+}
+
+hipError_t launch_verify_fused(const void* logits, int dtype, const float* temperature, const int32_t* top_k,
+                               const float* top_p, const float* draft_probs, const int32_t* draft_ids,
+                               const uint64_t* seed, const uint64_t* offset, int64_t B, int D, int64_t V,
+                               const int32_t* req_index, int64_t n_req, int32_t* accepted, int32_t* accept_len,
+                               hipStream_t stream) {
+    if (V > verify_fused_max_vocab()) return hipErrorInvalidValue;
+    if (dtype == kDtypeBF16) {
+        const uint16_t* lg = static_cast<const uint16_t*>(logits);
+        const int64_t nv = (V + kRrBlock * 8 - 1) / (kRrBlock * 8);
+        // the register-resident path needs every row 16-byte aligned
+        const bool rr = (V & 7) == 0 && (uintptr_t)lg % 16 == 0 && nv <= 20;
+#define SV_FV(NVV) \
+    launch_fv<uint16_t, NVV>(lg, temperature, top_k, top_p, draft_probs, draft_ids, seed, offset, B, D, V, req_index, \
+                             n_req, accepted, accept_len, stream)
+        if (!rr) SV_FV(0);
+        else if (nv <= 1) SV_FV(1);
+        else if (nv <= 2) SV_FV(2);
+        else if (nv <= 4) SV_FV(4);
+        else if (nv <= 8) SV_FV(8);
+        else if (nv <= 12) SV_FV(12);
+        else if (nv <= 16) SV_FV(16);
+        else SV_FV(20);
+#undef SV_FV
+    } else {
+        launch_fv<float, 0>(static_cast<const float*>(logits), temperature, top_k, top_p, draft_probs, draft_ids,
+                            seed, offset, B, D, V, req_index, n_req, accepted, accept_len, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -36,4 +36,12 @@ hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temp
                                 int32_t* accepted, int32_t* accept_len, int32_t* sampled_out,
                                 hipStream_t stream);
 
+// Fused target rows + chain rejection (V <= verify_fused_max_vocab()).
+int64_t verify_fused_max_vocab();
+hipError_t launch_verify_fused(const void* logits, int dtype, const float* temperature, const int32_t* top_k,
+                               const float* top_p, const float* draft_probs, const int32_t* draft_ids,
+                               const uint64_t* seed, const uint64_t* offset, int64_t B, int D, int64_t V,
+                               const int32_t* req_index, int64_t n_req, int32_t* accepted, int32_t* accept_len,
+                               hipStream_t stream);
+
 }  // namespace sv
