@@ -13,6 +13,8 @@ Functions mirror the C entry points:
 * ``chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None)``
 * ``greedy_verify(target_logits, draft_ids, req_index=None, ...)``
 * ``gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, ...)``
+* ``verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None,
+  top_p=None, req_index=None)``: softmax_renorm followed by chain_reject in one launch
 
 ``accept_length`` is the number of accepted drafts L in [0, D]; a request
 emits L + 1 tokens.
