@@ -143,3 +143,34 @@ def test_verify_fused_config5_filtered_rows(sv):
                               c["draft_ids"], c["seed"], c["offset"], requests=sample)
     flagged = assert_match(A, Ls, ref, sample, "cfg5 fused")
     log(f"config 5 fused: mean L={Ls[filt].mean():.3f}, sampled flagged={flagged}")
+
+
+def test_verify_fused_other_row_paths(sv):
+    """bf16 rows too long for the register-resident statistics (streamed),
+    logits whose rows are not 16-byte aligned (streamed), the largest
+    vocabulary the call accepts, and 16 drafts."""
+    torch = __import__("torch")
+    for V, dt, D, shift in ((200000, "bf16", 3, 0), (32000, "bf16", 2, 1), (524288, "f32", 1, 0),
+                            (5000, "bf16", 16, 0), (9000, "f32", 16, 3)):
+        B = 3
+        N = D + 1
+        c = fuzz_case(900 + V + D, B, D, V, dt)
+        T = np.array([0.9, 1.1, 0.0], np.float32)
+        k = np.array([40, 0, 0], np.int32)
+        p = np.array([0.95, 0.85, 1.0], np.float32)
+        zt = dev_logits(c["logits"], dt)
+        if shift:
+            flat = torch.empty(zt.numel() + 8, dtype=zt.dtype, device="cuda")
+            z = flat[shift:shift + zt.numel()].view(B, N, V)
+            z.copy_(zt)
+        else:
+            z = zt
+        log(f"fused other paths: V={V} dtype={dt} D={D} shift={shift}")
+        args = (dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["seed"]), dev(c["offset"]))
+        acc, alen = sv.verify_fused(z, dev(T), *args, top_k=dev(k), top_p=dev(p))
+        A, Ls = np_i(acc), np_i(alen)
+        A2, L2 = two_call(sv, z, dev(T), dev(k), dev(p), *args, B=B, N=N, V=V)
+        assert np.array_equal(A, A2) and np.array_equal(Ls, L2), (V, dt, D, shift)
+        ref = oracle.verify_fused(c["logits"], dt, T, k, p, c["draft_probs"], c["draft_ids"], c["seed"],
+                                  c["offset"])
+        assert_match(A, Ls, ref, range(B), (V, dt, D, shift))
