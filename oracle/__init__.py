@@ -21,6 +21,7 @@ from .verify import (  # noqa: F401
     greedy_verify,
     gumbel_row,
     gumbel_sample,
+    one_hot_drafts,
     renorm_row,
     residual_draw,
     softmax_renorm,

@@ -226,8 +226,28 @@ def chain_reject_core(q: np.ndarray, x: np.ndarray, p: np.ndarray,
     return dict(tokens=tokens, L=L, near_accept=near_accept, near_cdf=near_cdf)
 
 
+def one_hot_drafts(x: np.ndarray, V: int) -> np.ndarray:
+    """Draft distributions of a target-only verify: row i is one-hot at x_i
+    (all zeros when x_i lies outside [0, V)).
+
+    tokenspeed flashinfer.py, ``verify``: without draft probabilities the
+    chain kernel is given the draft tokens alone, with acceptance thresholds
+    (``threshold_single``, ``threshold_acc``); at thresholds of one that is the
+    rejection rule with a point-mass draft, which is what this builds.
+    """
+    x = np.asarray(x)
+    q = np.zeros((x.shape[0], V))
+    for i, xi in enumerate(x):
+        if 0 <= int(xi) < V:
+            q[i, int(xi)] = 1.0
+    return q
+
+
 def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, requests=None):
     """Batch form of ``rejection_sampling_one_model``.
+
+    ``draft_probs`` None is the target-only verify: every draft distribution is
+    one-hot at its draft id (``one_hot_drafts``).
 
     Returns accepted_tokens [B, D+1] (int64, -1 padded; rows not computed are
     -2), accept_length [B] (number of accepted drafts, -2 if not computed),
@@ -244,7 +264,8 @@ def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, requests=No
     reqs = range(B) if requests is None else [int(r) for r in requests]
     for b in reqs:
         ua, uf, code = chain_uniforms(int(seed[b]), int(offset[b]), D)
-        res = chain_reject_core(draft_probs[b], draft_ids[b], target_probs[b], ua, uf, code)
+        q = one_hot_drafts(draft_ids[b], np.shape(target_probs)[-1]) if draft_probs is None else draft_probs[b]
+        res = chain_reject_core(q, draft_ids[b], target_probs[b], ua, uf, code)
         tokens[b] = res["tokens"]
         L[b] = res["L"]
         if res["near_cdf"]:

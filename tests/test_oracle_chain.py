@@ -204,3 +204,44 @@ def test_inverse_cdf_exact_boundary_convention():
     assert y == 2
     y, _ = residual_draw(np.array([0.0, 0.25, 0.0, 0.75]), np.zeros(4), e, 1)
     assert y == 1
+
+
+def test_target_only_first_token_law_is_target_row():
+    """Point-mass drafts (no draft probabilities): for a fixed draft id the
+    first emitted token follows p_0 exactly (accept x w.p. p_0(x), otherwise
+    draw from p_0 without x), and the accept rate at position 0 is p_0(x)."""
+    rng = np.random.default_rng(61)
+    V, D, trials = 6, 2, 30000
+    p = _rows(rng, V, D + 1, zero_frac=0.1)[None]
+    x = np.array([[2, 4]], np.int32)
+    first = np.zeros(V)
+    acc0 = 0
+    for t in range(trials):
+        out = chain_reject(None, x, p, np.array([t + 1], np.uint64), np.array([(7 * t) & 0xFFFF], np.uint64))
+        first[out["accepted_tokens"][0, 0]] += 1
+        acc0 += out["accept_length"][0] >= 1
+    exp = p[0, 0].astype(np.float64) * trials
+    m = exp > 5
+    chi2 = ((first[m] - exp[m]) ** 2 / exp[m]).sum()
+    assert chi2 < 25, (chi2, first, exp)
+    pa = float(p[0, 0, 2])
+    assert abs(acc0 / trials - pa) < 5 * np.sqrt(pa * (1 - pa) / trials) + 1e-3
+
+
+def test_target_only_is_the_one_hot_draft_case():
+    rng = np.random.default_rng(62)
+    B, D, V = 8, 3, 40
+    p = np.stack([_rows(rng, V, D + 1) for _ in range(B)])
+    x = rng.integers(-2, V + 2, (B, D)).astype(np.int32)
+    seed = rng.integers(1, 2 ** 40, B).astype(np.uint64)
+    off = rng.integers(0, 2 ** 20, B).astype(np.uint64)
+    a = chain_reject(None, x, p, seed, off)
+    # acceptance at position i is exactly u_i < p_i(x_i) for a valid id
+    for b in range(B):
+        ua, _, _ = chain_uniforms(int(seed[b]), int(off[b]), D)
+        L = 0
+        while L < D and 0 <= x[b, L] < V and ua[L] < p[b, L, x[b, L]]:
+            L += 1
+        assert a["accept_length"][b] == L
+        if L < D and 0 <= x[b, L] < V:
+            assert a["accepted_tokens"][b, L] != x[b, L] or p[b, L, x[b, L]] > 1.0
