@@ -101,7 +101,7 @@ int specverify_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t 
  * per-request Philox seed/offset; returns the accepted draft tokens, the
  * corrected or bonus token, then -1.
  *
- * draft_probs     [B, D, V] float   q (may be NULL when D == 0)
+ * draft_probs     [B, D, V] float   q, or NULL: target-only verify (below)
  * draft_ids       [B, D] int32      x (may be NULL when D == 0)
  * target_probs    [B, D+1, V] float p
  * seed, offset    [B] uint64        Philox key and subsequence of each request
@@ -115,6 +115,14 @@ int specverify_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t 
  * The draw is y = min{ j : sum_{v<=j} r_v > u_f * R }, R = sum r, with
  * double-precision sums in ascending index order; an empty r falls back to
  * the target row, and an all-zero target row to floor(u_f * V).
+ *
+ * Target-only verify (draft_probs NULL, D > 0): "tokenspeed
+ * sampling/backends/flashinfer.py", FlashInferSamplingBackend.verify, passes
+ * the chain kernel draft tokens without draft probabilities, with acceptance
+ * thresholds; this is the thresholds-of-one case: q_i is the point mass at
+ * x_i (the zero row for an id outside [0, V)), so x_i is accepted iff
+ * u_i < p_i(x_i), and the correction is drawn from p_i with x_i weighing
+ * max(0, p_i(x_i) - 1).
  *
  * Memory: when a request's row is split over several workgroups (small
  * batches), they hand their partial sums over through a workspace the

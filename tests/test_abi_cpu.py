@@ -56,7 +56,6 @@ def _chain(**kw):
     (dict(n=3), "n_req=3"),
     (dict(n=5, req=P), "n_req=5"),
     (dict(p=None), "target_probs"),
-    (dict(q=None), "draft_probs"),
     (dict(x=None), "draft_ids"),
     (dict(seed=None), "seed"),
     (dict(off=None), "offset"),
@@ -75,6 +74,9 @@ def test_chain_reject_zero_draft_allows_null_draft_buffers_and_empty_batch_is_no
     # n_req = 0 returns OK without touching any device
     assert _chain(B=0, n=0) == sv.OK
     assert _chain(n=0, req=P) == sv.OK
+    # draft_probs NULL with D > 0 is the target-only verify: not an argument error
+    assert _chain(q=None, p=None) == sv.INVALID_ARGUMENT
+    assert "target_probs" in sv.lib().specverify_last_error().decode()
     # D = 0: draft buffers may be NULL (the failure is then a missing target buffer)
     assert _chain(D=0, q=None, x=None, p=None) == sv.INVALID_ARGUMENT
     assert "target_probs" in sv.lib().specverify_last_error().decode()

@@ -234,6 +234,36 @@ def test_chain_reject_large_batches(sv):
     log(f"chain large batch flagged requests: {flagged}")
 
 
+def test_chain_reject_target_only(sv):
+    """Target-only verify (no draft probabilities: point-mass drafts), on the
+    split-row and one-workgroup-per-request paths, aligned and unaligned rows,
+    with invalid ids, all-zero and one-hot target rows."""
+    torch = __import__("torch")
+    flagged = 0
+    cases = [(6, 3, V, sp, 0) for V in (1, 7, 1000, 4097, 32000) for sp in (None, "invalid_ids", "onehot")]
+    cases += [(6, 4, 3001, "zeros", 0), (5, 3, 1003, None, 1), (300, 5, 20000, None, 0), (260, 2, 4096, "onehot", 0)]
+    for i, (B, D, V, sp, shift) in enumerate(cases):
+        c = fuzz_case(1100 + i, B, D, V, "f32", special=sp)
+        if sp is None and i % 2 == 0:
+            # drafts at each row's most likely token half of the time, so acceptances happen
+            c["draft_ids"] = np.where(np.random.default_rng(i).random((B, D)) < 0.5,
+                                      c["target_probs"][:, :D].argmax(-1), c["draft_ids"]).astype(np.int32)
+        log(f"chain target-only {i}: B={B} D={D} V={V} special={sp} shift={shift}")
+        p = dev(c["target_probs"])
+        if shift:
+            flat = torch.empty(p.numel() + 4, device="cuda")
+            pp = flat[shift:shift + p.numel()].view(B, D + 1, V)
+            pp.copy_(p)
+            p = pp
+        ref = oracle.chain_reject(None, c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
+        acc, acc_full = guarded_i32((B, D + 1))
+        alen, alen_full = guarded_i32((B,))
+        sv.chain_reject(None, dev(c["draft_ids"]), p, dev(c["seed"]), dev(c["offset"]), out=(acc, alen))
+        flagged += assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, V, sp, shift))
+        assert guard_intact(acc_full, B * (D + 1)) and guard_intact(alen_full, B)
+    log(f"chain target-only flagged requests: {flagged}")
+
+
 def test_chain_reject_request_subset_and_determinism(sv):
     B, D, V = 9, 4, 3001
     c = fuzz_case(91, B, D, V, "f32")

@@ -172,16 +172,21 @@ def softmax_renorm(logits, temperature, top_k=None, top_p=None, req_index=None, 
 
 
 def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None, out=None):
-    """Chain rejection sampling; returns (accepted_tokens [B, D+1] int32, accept_length [B] int32)."""
+    """Chain rejection sampling; returns (accepted_tokens [B, D+1] int32, accept_length [B] int32).
+
+    ``draft_probs`` None is the target-only verify: each draft is a point mass at its id."""
     torch = _torch()
     _need(target_probs, "target_probs", (torch.float32,), None, 3)
     dev = target_probs.device
     B, N, V = target_probs.shape
     D = N - 1
-    _need(draft_probs, "draft_probs", (torch.float32,), dev, 3)
+    if draft_probs is not None:
+        _need(draft_probs, "draft_probs", (torch.float32,), dev, 3)
+        if tuple(draft_probs.shape) != (B, D, V):
+            raise ValueError(f"draft_probs must be [{B},{D},{V}]")
     _need(draft_ids, "draft_ids", (torch.int32,), dev, 2)
-    if tuple(draft_probs.shape) != (B, D, V) or tuple(draft_ids.shape) != (B, D):
-        raise ValueError(f"draft_probs must be [{B},{D},{V}] and draft_ids [{B},{D}]")
+    if tuple(draft_ids.shape) != (B, D):
+        raise ValueError(f"draft_ids must be [{B},{D}]")
     _u64(seed, "seed", B, dev)
     _u64(offset, "offset", B, dev)
     req_index, n_req = _req(req_index, B, dev)

@@ -180,10 +180,7 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids, 
     SV_TRY(check_draft(fn, D));
     SV_TRY(check_sizes(fn, B, D + 1, V, req_index, n_req, 4));
     if (n_req == 0) return SPECVERIFY_OK;
-    if (D > 0) {
-        SV_REQUIRE(draft_probs, "draft_probs");
-        SV_REQUIRE(draft_ids, "draft_ids");
-    }
+    if (D > 0) SV_REQUIRE(draft_ids, "draft_ids");   // draft_probs NULL: point-mass drafts
     SV_REQUIRE(target_probs, "target_probs");
     SV_REQUIRE(seed, "seed");
     SV_REQUIRE(offset, "offset");

@@ -22,6 +22,9 @@
 //    reproducible run to run.
 // 4. Degenerate rows (residual mass not positive) fall back to a draw from the
 //    target row by the same workgroup, then to floor(u_f * V).
+// Without draft distributions (target-only verify) each draft is a point mass
+// at its id: the probe takes q(x) = 1 and the residual pass streams p_L alone,
+// the rejected id weighing max(0, p - 1).
 #include "sv_draw.hpp"
 #include "sv_launch.hpp"
 
@@ -49,6 +52,7 @@ struct ChainShared {
     double chunk[kFallbackChunks];
     uint32_t code;
     int L;
+    int32_t xL;   // point-mass drafts: the rejected id (-1 if none or out of range)
     int last;
     int64_t y;
 };
@@ -98,7 +102,7 @@ __device__ __forceinline__ void load_run(const float* row, int64_t base, int64_t
 template <int NSUB>
 __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int64_t V, bool aligned,
                                int64_t base, double run, double T, bool force_last, int64_t& lastpos,
-                               double& total) {
+                               double& total, int64_t xo = -1) {
     const int lane = threadIdx.x & (kWave - 1);
     float pf[NSUB][4], qf[NSUB][4];
     load_run<NSUB, false>(pr, base, V, aligned, pf);
@@ -110,12 +114,17 @@ __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int
 #pragma unroll
             for (int e = 0; e < 4; ++e) qf[k][e] = 0.0f;
     }
+    // entry weight; with point-mass drafts the rejected id xo weighs max(0, p - 1)
+    auto rv = [&](int k, int e) {
+        const double r = rval(pf[k][e], qf[k][e], resid);
+        return base + (k * kWave + lane) * 4 + e == xo ? fmax(0.0, (double)pf[k][e] - 1.0) : r;
+    };
     int64_t mylast = -1;
 #pragma unroll
     for (int k = 0; k < NSUB; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (rval(pf[k][e], qf[k][e], resid) > 0.0) mylast = base + (k * kWave + lane) * 4 + e;
+            if (rv(k, e) > 0.0) mylast = base + (k * kWave + lane) * 4 + e;
     lastpos = wave_allreduce(mylast, [](int64_t a, int64_t b) { return a > b ? a : b; });
     total = 0.0;
     if (force_last) return -1;
@@ -123,7 +132,7 @@ __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int
     for (int k = 0; k < NSUB; ++k) {
         double r[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = rval(pf[k][e], qf[k][e], resid);
+        for (int e = 0; e < 4; ++e) r[e] = rv(k, e);
         const double s = ((r[0] + r[1]) + r[2]) + r[3];
         const double incl = wave_incl_scan(s);
         const double excl = wave_shift_up1(incl);
@@ -228,9 +237,9 @@ __device__ __forceinline__ double read_partial(double* src) {
 // flight (consume a slot, refill it); the remaining rounds use buffer loads
 // with the row as the range, so chunks past the end read as zeros.  Returns,
 // on lane r, the sum of round r's chunk of this wave.
-template <bool RESID, int DEPTH>
+template <bool RESID, int DEPTH, bool ONEHOT = false>
 __device__ __forceinline__ double stream_chunks_fast(const float* pr, const float* qr, int64_t V, int64_t chunk0,
-                                                     int R) {
+                                                     int R, int64_t xo = -1) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     constexpr bool kNT = SV_CHAIN_NT != 0;
     const int64_t lane_off = (int64_t)wid * kChunk + lane * 4;   // floats
@@ -253,9 +262,19 @@ __device__ __forceinline__ double stream_chunks_fast(const float* pr, const floa
             float pf[4], qf[4] = {0.f, 0.f, 0.f, 0.f};
             unpack(p4[k], pf);
             if constexpr (RESID) unpack(q4[k], qf);
+            double rr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[e] = rval(pf[e], qf[e], RESID);
+            if constexpr (ONEHOT) {
+                // point-mass draft at xo: that entry weighs max(0, p - 1)
+                const int64_t d = xo - ((chunk0 + (int64_t)r * kChainWaves) * kChunk + lane_off + k * kWave * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (d == e) rr[e] = fmax(0.0, (double)pf[e] - 1.0);
+            }
             double s4 = 0.0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s4 += rval(pf[e], qf[e], RESID);
+            for (int e = 0; e < 4; ++e) s4 += rr[e];
             acc += s4;
         }
         acc = wave_allreduce(acc, OpSumD{});
@@ -304,8 +323,11 @@ __device__ __forceinline__ double stream_chunks_fast(const float* pr, const floa
     return mine;
 }
 
-// kDraft: D > 0 (the probe loads draft ids and probabilities).
-template <bool kDraft>
+// Draft mode: kNoDraft (D = 0), kDraftProbs (draft distributions given) or
+// kPointDraft (no draft distributions: each draft is a point mass at its id,
+// so q(x) = 1 and the residual is p with the rejected id weighing max(0, p - 1)).
+constexpr int kNoDraft = 0, kDraftProbs = 1, kPointDraft = 2;
+template <int kMode>
 __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const float* __restrict__ q, const int32_t* __restrict__ x, const float* __restrict__ p,
     const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
@@ -330,7 +352,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     if (tid <= D) {
         uint32_t w;
         bool ok = false;
-        if constexpr (kDraft) {
+        if constexpr (kMode != kNoDraft) {
             // lanes 0 and 1 (both active: D >= 1) fetch seed and offset with
             // the id loads; lane D repeats lane D-1's loads (in bounds), so no
             // lane branches and the Philox rounds overlap the draft-probability
@@ -341,10 +363,18 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
             const bool inr = tid < D && xi >= 0 && (int64_t)xi < V;
             const int64_t xc = inr ? (int64_t)xi : 0;
             const float a = p[(b * N + ic) * V + xc];
-            const float cq = q[(b * D + ic) * V + xc];
+            const float cq = kMode == kDraftProbs ? q[(b * D + ic) * V + xc] : 1.0f;
             __builtin_amdgcn_sched_barrier(0);
             w = philox_word(read_lane(so, 0), read_lane(so, 1), (uint64_t)tid);
             ok = inr && (double)uniform_of(w) * (double)cq < (double)a;
+            if constexpr (kMode == kPointDraft) {
+                // the rejected id, read from its lane (lanes 0..D are all active here)
+                const int32_t xsel = inr ? xi : -1;
+                const uint64_t rj = __ballot(tid < D && !ok);
+                const int Lr = rj ? __ffsll((unsigned long long)rj) - 1 : D;
+                const int32_t xr = Lr < D ? read_lane(xsel, Lr) : -1;
+                if (tid == 0) sh.xL = xr;
+            }
         } else {
             w = philox_word(seed[b], offset[b], (uint64_t)tid);
         }
@@ -354,7 +384,11 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     }
     __syncthreads();
     const int L = sh.L;
-    const bool resid = L < D;
+    // a residual row with draft probabilities streams q_L; with point-mass
+    // drafts it streams p_L alone, the rejected id xo weighing max(0, p - 1)
+    const bool resid = kMode == kDraftProbs && L < D;
+    const bool point = kMode == kPointDraft && L < D;
+    const int64_t xo = point ? (int64_t)sh.xL : -1;
     const float* pr = p + (b * N + L) * V;
     const float* qr = resid ? q + (b * D + L) * V : nullptr;
     const bool aligned = ((uintptr_t)pr % 16 == 0) && (!resid || (uintptr_t)qr % 16 == 0);
@@ -367,6 +401,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     double mine = 0.0;
     if (aligned && (V & 3) == 0 && V < ((int64_t)1 << 29)) {
         if (resid) mine = stream_chunks_fast<true, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
+        else if (point) mine = stream_chunks_fast<false, SV_CHAIN_DEPTH, true>(pr, qr, V, chunk0, R, xo);
         else mine = stream_chunks_fast<false, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
     } else {
         float pa[4][4], qa[4][4], pb[4][4], qb[4][4];
@@ -385,7 +420,11 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
                 for (int k = 0; k < 4; ++k) {
                     double s4 = 0.0;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) s4 += rval(pf[k][e], resid ? qf[k][e] : 0.0f, resid);
+                    for (int e = 0; e < 4; ++e) {
+                        double r = rval(pf[k][e], resid ? qf[k][e] : 0.0f, resid);
+                        if (ch * kChunk + (k * kWave + lane) * 4 + e == xo) r = fmax(0.0, (double)pf[k][e] - 1.0);
+                        s4 += r;
+                    }
                     acc += s4;
                 }
             }
@@ -452,14 +491,14 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
             int64_t lastpos;
             double tot;
             y = wave_search<4>(pr, qr, resid, V, aligned, (int64_t)cstar * kChunk, base, uf * R_tot,
-                               force_last != 0, lastpos, tot);
+                               force_last != 0, lastpos, tot, xo);
             if (y < 0) y = lastpos;
         }
         if (lane == 0) sh.y = y;
     }
     __syncthreads();
     int64_t y = sh.y;
-    if (y < 0 && resid) y = draw_row_single(pr, V, uf, sh);
+    if (y < 0 && (resid || point)) y = draw_row_single(pr, V, uf, sh);
     if (y < 0) y = (int64_t)(((uint64_t)sh.code * (uint64_t)V) >> 24);
     if (tid < N) {
         int32_t t;
@@ -500,7 +539,8 @@ hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_id
     const int64_t per_xcd = (total + 7) / 8;
     const int64_t grid = per_xcd * 8;
     if (grid > 2147483647LL) return hipErrorInvalidValue;
-    auto* kernel = D > 0 ? chain_reject_kernel<true> : chain_reject_kernel<false>;
+    auto* kernel = D == 0 ? chain_reject_kernel<kNoDraft>
+                          : (draft_probs ? chain_reject_kernel<kDraftProbs> : chain_reject_kernel<kPointDraft>);
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kChainBlock), 0, stream, draft_probs, draft_ids,
                        target_probs, seed, offset, B, D, V, req_index, n_req, C, R, per_xcd, accepted, accept_len,
                        partial, counter);
