@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large_vocab_chain_reject",
-                    choices=["large_vocab_chain_reject", "topk_topp_chain", "greedy", "mixed", "mixed_fused"])
+                    choices=["large_vocab_chain_reject", "large_vocab_target_only", "topk_topp_chain", "greedy",
+                             "mixed", "mixed_fused"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -172,6 +173,50 @@ class ChainWorkload:
         while True:
             off = self.reps[passes % self.R]["off_host"]
             oracle.chain_reject(h["draft_probs"], h["draft_ids"], h["target_probs"], h["seed"], off)
+            rows += self.rows
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
+                          f"{el:.1f}s single-threaded numpy"}
+
+
+class TargetOnlyWorkload(ChainWorkload):
+    """The large-vocab chain inputs verified without draft probabilities (point-mass drafts)."""
+    name = "large_vocab_target_only"
+    counters = "chain_reject_target_only_counters.txt"
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        self.sv.chain_reject(None, r["x"], r["p"], r["seed"], r["off"], out=(self.acc, self.alen))
+
+    def algorithmic_bytes(self):
+        """Per request: one target line per probed position, one target row (p_L or the bonus row p_D)."""
+        per = []
+        self.L = []
+        for i in range(self.R):
+            self.step(i)
+            L = self.alen.cpu().numpy().astype(np.int64)
+            self.L.append(L)
+            D, V = self.D, self.V
+            probes = PROBE_GRANULE * np.minimum(L + 1, D)
+            per.append(int(4 * V * self.B + probes.sum() + self.B * (8 * D + 24)))
+        return float(np.mean(per))
+
+    def config(self):
+        c = super().config()
+        c["input"] = "float32 target probabilities, draft ids only (no draft probabilities)"
+        return c
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, passes = 0, time.perf_counter(), 0
+        while True:
+            off = self.reps[passes % self.R]["off_host"]
+            oracle.chain_reject(None, h["draft_ids"], h["target_probs"], h["seed"], off)
             rows += self.rows
             passes += 1
             el = time.perf_counter() - t0
@@ -476,7 +521,7 @@ class MixedFusedWorkload(MixedWorkload):
         return self.bytes_by_call["verify_fused"]
 
 
-WORKLOADS = {c.name: c for c in (ChainWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
+WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
                                  MixedFusedWorkload)}
 
 
