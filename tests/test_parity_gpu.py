@@ -196,10 +196,12 @@ def test_chain_reject_large_batches(sv):
     """Batches of long rows, with rows split over several workgroups (partial
     sums published, last workgroup locates) and with one workgroup per
     request: a ragged last chunk, up to 1024 requests, all-bonus and
-    all-residual batches, degenerate rows, and a request subset with skipped
-    and repeated indices."""
+    all-residual batches, degenerate rows, a row of 293 chunks, and a
+    request subset with skipped and repeated indices."""
     cases = ((64, 5, 65536, None), (300, 3, 16424, None), (1024, 3, 4096, None), (130, 4, 32768, "zeros"),
-             (110, 2, 40000, "equal"), (140, 2, 30000, "disjoint"), (70, 7, 60000, None), (160, 0, 65536, None))
+             (110, 2, 40000, "equal"), (140, 2, 30000, "disjoint"), (70, 7, 60000, None), (160, 0, 65536, None),
+             # one workgroup per request: no drafts, all accepted, a row of 293 chunks
+             (300, 0, 8192, None), (270, 2, 8000, "equal"), (256, 1, 300000, None))
     flagged = 0
     for B, D, V, special in cases:
         c = fuzz_case(900 + B + V, B, D, V, "f32", special=special)
