@@ -16,12 +16,14 @@ from .verify import (  # noqa: F401
     RNG_SLOT_SPAN,
     chain_reject,
     chain_reject_core,
+    chain_reject_ragged,
     chain_uniforms,
     decode_logits,
     greedy_verify,
     gumbel_row,
     gumbel_sample,
     one_hot_drafts,
+    ragged_pad,
     renorm_row,
     residual_draw,
     softmax_renorm,

@@ -275,6 +275,89 @@ def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, requests=No
     return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
 
 
+# --------------------------------------------------------------------------- ragged chain rejection
+def ragged_pad(draft_probs, draft_ids, target_packed, qo_indptr, D: int):
+    """The padded rectangle a ragged verify batch is scattered into.
+
+    TensorRT-LLM interface.py, the ragged branch of the one-model sampler
+    (``scatter_ragged_to_padded`` then ``fill_padded_rows_onehot``, for target
+    and draft rows alike): request r owns packed target rows
+    [qo_indptr[r], qo_indptr[r+1]), verify_lens[r] = their count.  Target rows
+    at positions >= verify_lens[r] and draft rows at positions >=
+    verify_lens[r] - 1 are one-hot at token 0, and missing draft ids are 0:
+    at the request's own last position acceptance emits token 0 with
+    probability p(0) and a rejection samples p with token 0 removed, which
+    together sample p.
+
+    ``draft_probs`` None is the target-only verify (point masses at the draft
+    ids).  Returns (q [B, D, V], x [B, D], p [B, D+1, V], lens [B]); a request
+    whose length is outside [1, D+1] or whose rows fall outside the packed
+    array gets length -1 (and is not verified).
+    """
+    target_packed = np.asarray(target_packed)
+    T, V = target_packed.shape
+    ind = np.asarray(qo_indptr, dtype=np.int64)
+    B = ind.shape[0] - 1
+    p = np.zeros((B, D + 1, V))
+    q = np.zeros((B, D, V))
+    x = np.zeros((B, D), dtype=np.int64)
+    lens = np.full(B, -1, dtype=np.int64)
+    for b in range(B):
+        base, n = int(ind[b]), int(ind[b + 1] - ind[b])
+        if not (1 <= n <= D + 1 and 0 <= base and base + n <= T):
+            continue
+        lens[b] = n
+        d = n - 1
+        p[b, :n] = target_packed[base:base + n]
+        p[b, n:, 0] = 1.0
+        x[b, :d] = np.asarray(draft_ids)[b, :d]
+        if draft_probs is None:
+            q[b, :d] = one_hot_drafts(x[b, :d], V)
+        else:
+            q[b, :d] = np.asarray(draft_probs)[b, :d]
+        q[b, d:, 0] = 1.0
+    return q, x, p, lens
+
+
+def chain_reject_ragged(draft_probs, draft_ids, target_packed, qo_indptr, seed, offset, requests=None):
+    """Ragged (per-request verify length) chain rejection.
+
+    TensorRT-LLM interface.py, ragged branch of the one-model sampler: the
+    packed rows are padded as ``ragged_pad`` states, the chain verify runs on
+    the padded rectangle, and the emitted count is clamped to verify_lens
+    ("accepting past it commits tokens the target never scored").  Returned
+    accept_length is the number of accepted draft tokens after the clamp
+    (emitted - 1); tokens after the emitted ones are -1.  Requests with an
+    invalid length get accept_length -1 and all tokens -1.
+
+    Same return dict as ``chain_reject``.
+    """
+    B, D = np.asarray(draft_ids).shape
+    q, x, p, lens = ragged_pad(draft_probs, draft_ids, target_packed, qo_indptr, D)
+    tokens = np.full((B, D + 1), -2, dtype=np.int64)
+    L = np.full(B, -2, dtype=np.int64)
+    flag_pos = np.full(B, D + 1, dtype=np.int64)
+    near_accept = np.full(B, -1, dtype=np.int64)
+    reqs = range(B) if requests is None else [int(r) for r in requests]
+    for b in reqs:
+        if lens[b] < 0:
+            tokens[b] = -1
+            L[b] = -1
+            continue
+        ua, uf, code = chain_uniforms(int(seed[b]), int(offset[b]), D)
+        res = chain_reject_core(q[b], x[b], p[b], ua, uf, code)
+        emitted = min(res["L"] + 1, int(lens[b]))
+        t = res["tokens"].copy()
+        t[emitted:] = -1
+        tokens[b] = t
+        L[b] = emitted - 1
+        if res["near_cdf"] and res["L"] < emitted:
+            flag_pos[b] = res["L"]
+        if res["near_accept"] is not None and res["near_accept"] < emitted:
+            near_accept[b] = res["near_accept"]
+    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
+
+
 # --------------------------------------------------------------------------- fused target rows + chain rejection
 def verify_fused(logits, dtype, temperature, top_k, top_p, draft_probs, draft_ids, seed, offset, requests=None):
     """Target rows from logits, then chain rejection, as one call.
