@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large_vocab_chain_reject",
-                    choices=["large_vocab_chain_reject", "large_vocab_target_only", "topk_topp_chain", "greedy",
+                    choices=["large_vocab_chain_reject", "large_vocab_target_only", "large_vocab_ragged", "topk_topp_chain",
+                             "greedy",
                              "mixed", "mixed_fused"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
@@ -217,6 +218,86 @@ class TargetOnlyWorkload(ChainWorkload):
         while True:
             off = self.reps[passes % self.R]["off_host"]
             oracle.chain_reject(None, h["draft_ids"], h["target_probs"], h["seed"], off)
+            rows += self.rows
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
+                          f"{el:.1f}s single-threaded numpy"}
+
+
+class RaggedWorkload:
+    """The large-vocab chain inputs with per-request verify lengths len_b ~ U{1..6} over packed target rows."""
+    name = "large_vocab_ragged"
+    kernel = "chain_reject_kernel"
+    sources = ("chain_reject.hip", "sv_draw.hpp", "sv_common.hpp")
+    counters = "chain_reject_ragged_counters.txt"
+    dtype = "f32"
+
+    def __init__(self, dev, replicas):
+        from workloads import make_ragged_config
+        t0 = time.time()
+        self.host = make_ragged_config()
+        log(f"generated inputs in {time.time() - t0:.1f}s")
+        h = self.host
+        self.B, self.D, self.V = h["B"], h["D"], h["V"]
+        self.R = replicas or 4
+        self.reps = []
+        for r in range(self.R):
+            off = np.full(self.B, 4096 * r, np.uint64)
+            self.reps.append(dict(q=_t(h["draft_probs"], dev), x=_t(h["draft_ids"], dev),
+                                  p=_t(h["target_rows"], dev), ind=_t(h["qo_indptr"], dev), seed=_t(h["seed"], dev),
+                                  off=_t(off, dev), off_host=off))
+        import token_sampling_temp_amd as sv
+        self.sv = sv
+        import torch
+        self.acc = torch.empty((self.B, self.D + 1), dtype=torch.int32, device=dev)
+        self.alen = torch.empty((self.B,), dtype=torch.int32, device=dev)
+        self.rows = int(h["verify_lens"].sum())
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        self.sv.chain_reject_ragged(r["q"], r["x"], r["p"], r["ind"], r["seed"], r["off"], out=(self.acc, self.alen))
+
+    def algorithmic_bytes(self):
+        """Per request: one target and one draft line per probed position, then the row pass its outcome
+        needs: p_L and q_L after a rejection before its last position d, p_d after a rejection at d (or the
+        bonus when d = D), nothing when token 0 was accepted at d."""
+        per = []
+        self.L = []
+        d = self.host["verify_lens"] - 1
+        for i in range(self.R):
+            self.step(i)
+            L = self.alen.cpu().numpy().astype(np.int64)
+            tok = self.acc.cpu().numpy()
+            self.L.append(L)
+            D, V = self.D, self.V
+            at_d = tok[np.arange(self.B), np.minimum(L, D)]
+            rows = np.where(L < d, 8 * V, np.where((d < D) & (at_d == 0), 0, 4 * V))
+            probes = 2 * PROBE_GRANULE * np.minimum(L + 1, D)
+            per.append(int(rows.sum() + probes.sum() + self.B * (8 * D + 32)))
+        return float(np.mean(per))
+
+    def extra(self):
+        L = np.concatenate(self.L)
+        return {"mean_accept_length": round(float(L.mean()), 4),
+                "mean_verify_length": round(float(self.host["verify_lens"].mean()), 4)}
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "draft_tokens": self.D, "vocab": self.V,
+                "verified_rows": self.rows, "input": "float32 packed target rows, per-request verify lengths "
+                "U{1..6}, float32 draft probabilities", "replicas": self.R}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, passes = 0, time.perf_counter(), 0
+        while True:
+            off = self.reps[passes % self.R]["off_host"]
+            oracle.chain_reject_ragged(h["draft_probs"], h["draft_ids"], h["target_rows"], h["qo_indptr"], h["seed"],
+                                       off)
             rows += self.rows
             passes += 1
             el = time.perf_counter() - t0
@@ -521,7 +602,7 @@ class MixedFusedWorkload(MixedWorkload):
         return self.bytes_by_call["verify_fused"]
 
 
-WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
+WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
                                  MixedFusedWorkload)}
 
 

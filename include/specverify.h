@@ -142,6 +142,42 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids,
                             int32_t* accept_length, void* stream);
 
 /*
+ * Ragged chain rejection: each request verifies its own number of positions.
+ *
+ * Passage: "TensorRT-LLM _torch/speculative/interface.py", SpecMetadata
+ * (verify_lens, qo_indptr: request r owns packed rows [qo_indptr[r],
+ * qo_indptr[r+1])) and the ragged branch of the one-model sampler: target rows
+ * are scattered to the padded [B, D+1, V] layout, padding rows of target and
+ * draft are one-hot at token 0 (missing draft ids are 0), the chain verify
+ * runs on the rectangle, and the emitted count is clamped to verify_lens.
+ *
+ * draft_probs     [B, D, V] float32 or NULL (point-mass drafts, as in
+ *                 specverify_chain_reject); rows at positions >= len_b - 1 are
+ *                 not read
+ * draft_ids       [B, D] int32; entries at positions >= len_b - 1 are not read
+ * target_probs    [n_rows, V] float32, packed rows
+ * qo_indptr       [B+1] int32, request b's rows are [qo_indptr[b], qo_indptr[b+1]),
+ *                 len_b = their count, 1 <= len_b <= D+1
+ * seed, offset, B, D, V, req_index, n_req, stream: as in specverify_chain_reject
+ * accepted_tokens [B, D+1] int32    output: x_0..x_{L-1}, y, then -1
+ * accept_length   [B] int32         output: L in [0, len_b - 1]
+ *
+ * With d = len_b - 1, positions i < d verify as in specverify_chain_reject.
+ * Position d drafts token 0 as a point mass: if u_d < p_d(0) the request
+ * emits x_0..x_{d-1}, 0 (L = d); if it rejects there, y is drawn from p_d with
+ * token 0 removed.  Together these sample p_d (the page's argument for its
+ * padding).  When len_b = D+1 the request is verified exactly as by
+ * specverify_chain_reject.  A request whose length is outside [1, D+1] or
+ * whose rows fall outside [0, n_rows) gets accept_length -1 and all tokens
+ * -1; nothing of it is read.  Memory: the workspace of specverify_chain_reject.
+ */
+int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* draft_ids,
+                                   const float* target_probs, const int32_t* qo_indptr, int64_t n_rows,
+                                   const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D,
+                                   int64_t V, const int32_t* req_index, int64_t n_req,
+                                   int32_t* accepted_tokens, int32_t* accept_length, void* stream);
+
+/*
  * Greedy chain verify.
  *
  * Passage: "tokenspeed sampling/backends/flashinfer.py",

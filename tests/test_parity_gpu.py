@@ -266,6 +266,75 @@ def test_chain_reject_target_only(sv):
     log(f"chain target-only flagged requests: {flagged}")
 
 
+def _ragged_pack(c, lens):
+    """Packed target rows and qo_indptr from a dense fuzz case and per-request lengths."""
+    p = c["target_probs"]
+    rows = np.concatenate([p[b, :n] for b, n in enumerate(lens)], axis=0)
+    ind = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return np.ascontiguousarray(rows), ind
+
+
+def test_chain_reject_ragged(sv):
+    """Per-request verify lengths over packed target rows, with and without
+    draft probabilities, on split rows and one workgroup per request, aligned
+    and unaligned V, degenerate rows, all lengths 1, invalid lengths, and a
+    request subset."""
+    torch = __import__("torch")
+    flagged = 0
+    cases = [(6, 3, 1000, None), (5, 4, 32000, None), (6, 2, 4097, "zeros"), (7, 5, 3001, "disjoint"),
+             (300, 5, 20000, None), (260, 3, 5003, None), (258, 4, 8192, "onehot"), (256, 2, 4096, "len1")]
+    for i, (B, D, V, sp) in enumerate(cases):
+        c = fuzz_case(1300 + i, B, D, V, "f32", special=None if sp == "len1" else sp)
+        rng = np.random.default_rng(1300 + i)
+        lens = np.ones(B, np.int64) if sp == "len1" else rng.integers(1, D + 2, B)
+        if sp is None and i % 2 == 0:
+            # drafts at each row's most likely token half of the time, so long acceptances happen
+            c["draft_ids"] = np.where(rng.random((B, D)) < 0.5, c["target_probs"][:, :D].argmax(-1),
+                                      c["draft_ids"]).astype(np.int32)
+        rows, ind = _ragged_pack(c, lens)
+        if i == 1:
+            ind[2] = ind[1]                    # request 1: length 0 (request 2 then reads past its rows)
+        for q in (c["draft_probs"], None):
+            log(f"chain ragged {i}: B={B} D={D} V={V} special={sp} draft_probs={q is not None}")
+            ref = oracle.chain_reject_ragged(q, c["draft_ids"], rows, ind, c["seed"], c["offset"])
+            acc, acc_full = guarded_i32((B, D + 1))
+            alen, alen_full = guarded_i32((B,))
+            sv.chain_reject_ragged(None if q is None else dev(q), dev(c["draft_ids"]), dev(rows), dev(ind),
+                                   dev(c["seed"]), dev(c["offset"]), out=(acc, alen))
+            flagged += assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, V, sp, q is not None))
+            assert guard_intact(acc_full, B * (D + 1)) and guard_intact(alen_full, B)
+    # request subset on the one-workgroup path: other rows untouched
+    B, D, V = 300, 4, 12288
+    c = fuzz_case(1399, B, D, V, "f32")
+    lens = np.random.default_rng(9).integers(1, D + 2, B)
+    rows, ind = _ragged_pack(c, lens)
+    reqs = np.random.default_rng(8).permutation(B)[:270].astype(np.int32)
+    log(f"chain ragged subset: B={B} D={D} V={V} n_req={len(reqs)}")
+    ref = oracle.chain_reject_ragged(c["draft_probs"], c["draft_ids"], rows, ind, c["seed"], c["offset"])
+    acc = torch.full((B, D + 1), SENTINEL, dtype=torch.int32, device="cuda")
+    alen = torch.full((B,), SENTINEL, dtype=torch.int32, device="cuda")
+    sv.chain_reject_ragged(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(rows), dev(ind), dev(c["seed"]),
+                           dev(c["offset"]), req_index=dev(reqs), out=(acc, alen))
+    flagged += assert_chain_match(np_i(acc), np_i(alen), ref, sorted(set(reqs.tolist())), "ragged subset")
+    rest = np.setdiff1d(np.arange(B), reqs)
+    assert np.all(np_i(acc)[rest] == SENTINEL) and np.all(np_i(alen)[rest] == SENTINEL)
+    log(f"chain ragged flagged requests: {flagged}")
+
+
+def test_chain_reject_ragged_large_vocab_full(sv):
+    """The large-vocab workload with per-request verify lengths drawn from {1..D+1}."""
+    from workloads import make_ragged_config
+    c = make_ragged_config()
+    B, D, V = c["B"], c["D"], c["V"]
+    log(f"chain ragged large vocab: B={B} D={D} V={V} rows={c['target_rows'].shape[0]}")
+    ref = oracle.chain_reject_ragged(c["draft_probs"], c["draft_ids"], c["target_rows"], c["qo_indptr"], c["seed"],
+                                     c["offset"])
+    acc, alen = sv.chain_reject_ragged(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_rows"]),
+                                       dev(c["qo_indptr"]), dev(c["seed"]), dev(c["offset"]))
+    flagged = assert_chain_match(np_i(acc), np_i(alen), ref, range(B), "ragged large vocab")
+    log(f"ragged large vocab: mean accept length {np_i(alen).mean():.3f}, flagged {flagged}")
+
+
 def test_chain_reject_request_subset_and_determinism(sv):
     B, D, V = 9, 4, 3001
     c = fuzz_case(91, B, D, V, "f32")

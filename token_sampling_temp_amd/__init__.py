@@ -11,6 +11,8 @@ Functions mirror the C entry points:
 
 * ``softmax_renorm(logits, temperature, top_k=None, top_p=None, req_index=None)``
 * ``chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None)``
+* ``chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None)``:
+  per-request verify lengths over packed target rows
 * ``greedy_verify(target_logits, draft_ids, req_index=None, ...)``
 * ``gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, ...)``
 * ``verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None,
@@ -35,6 +37,7 @@ RNG_SLOT_SPAN = 32
 SYMBOLS = (
     "specverify_softmax_renorm",
     "specverify_chain_reject",
+    "specverify_chain_reject_ragged",
     "specverify_greedy_verify",
     "specverify_gumbel_sample",
     "specverify_verify_fused",
@@ -67,10 +70,12 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     L.specverify_softmax_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp, vp]
     L.specverify_chain_reject.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.specverify_chain_reject_ragged.argtypes = [vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
     L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
-    for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_greedy_verify",
+    for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_chain_reject_ragged",
+                 "specverify_greedy_verify",
                  "specverify_gumbel_sample", "specverify_verify_fused"):
         getattr(L, name).restype = ctypes.c_int
     L.specverify_status_string.argtypes = [ctypes.c_int]
@@ -236,6 +241,38 @@ def verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offse
         _ptr(draft_probs), _ptr(draft_ids), _ptr(seed), _ptr(offset), B, D, V, _ptr(req_index), n_req, _ptr(acc),
         _ptr(alen), _stream_ptr(dev))
     _check("specverify_verify_fused", st)
+    return acc, alen
+
+
+def chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None, out=None):
+    """Ragged chain rejection over packed target rows [n_rows, V]; request b owns rows
+    [qo_indptr[b], qo_indptr[b+1]).  Returns (accepted_tokens [B, D+1] int32,
+    accept_length [B] int32); ``draft_probs`` None means point-mass drafts."""
+    torch = _torch()
+    _need(target_probs, "target_probs", (torch.float32,), None, 2)
+    dev = target_probs.device
+    n_rows, V = target_probs.shape
+    _need(draft_ids, "draft_ids", (torch.int32,), dev, 2)
+    B, D = draft_ids.shape
+    if draft_probs is not None:
+        _need(draft_probs, "draft_probs", (torch.float32,), dev, 3)
+        if tuple(draft_probs.shape) != (B, D, V):
+            raise ValueError(f"draft_probs must be [{B},{D},{V}]")
+    _need(qo_indptr, "qo_indptr", (torch.int32,), dev, 1)
+    if qo_indptr.shape[0] != B + 1:
+        raise ValueError(f"qo_indptr must have shape [{B + 1}]")
+    _u64(seed, "seed", B, dev)
+    _u64(offset, "offset", B, dev)
+    req_index, n_req = _req(req_index, B, dev)
+    if out is None:
+        acc = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        acc, alen = out
+    st = lib().specverify_chain_reject_ragged(
+        _ptr(draft_probs), _ptr(draft_ids), _ptr(target_probs), _ptr(qo_indptr), n_rows, _ptr(seed), _ptr(offset),
+        B, D, V, _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
+    _check("specverify_chain_reject_ragged", st)
     return acc, alen
 
 

@@ -190,9 +190,38 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids, 
     uint32_t* counter = nullptr;
     double* partial = nullptr;
     SV_TRY(chain_workspace(fn, static_cast<hipStream_t>(stream), n_req, V, &counter, &partial));
-    return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, seed, offset, B, (int)D, V,
-                                                req_index, n_req, accepted_tokens, accept_length, counter, partial,
-                                                static_cast<hipStream_t>(stream)));
+    return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, nullptr, 0, seed, offset, B,
+                                                (int)D, V, req_index, n_req, accepted_tokens, accept_length,
+                                                counter, partial, static_cast<hipStream_t>(stream)));
+}
+
+int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
+                                   const int32_t* qo_indptr, int64_t n_rows, const uint64_t* seed,
+                                   const uint64_t* offset, int64_t B, int64_t D, int64_t V,
+                                   const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
+                                   int32_t* accept_length, void* stream) {
+    const char* fn = "specverify_chain_reject_ragged";
+    SV_TRY(check_draft(fn, D));
+    SV_TRY(check_sizes(fn, B, D + 1, V, req_index, n_req, 4));
+    if (n_rows < 0 || n_rows > 2147483647LL)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: n_rows=%lld must be in [0, 2^31)", fn, (long long)n_rows);
+    if ((long double)n_rows * (long double)V * 4.0L > 4.0e18L)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: tensor size overflows", fn);
+    if (n_req == 0) return SPECVERIFY_OK;
+    if (D > 0) SV_REQUIRE(draft_ids, "draft_ids");   // draft_probs NULL: point-mass drafts
+    SV_REQUIRE(target_probs, "target_probs");
+    SV_REQUIRE(qo_indptr, "qo_indptr");
+    SV_REQUIRE(seed, "seed");
+    SV_REQUIRE(offset, "offset");
+    SV_REQUIRE(accepted_tokens, "accepted_tokens");
+    SV_REQUIRE(accept_length, "accept_length");
+    SV_TRY(check_device());
+    uint32_t* counter = nullptr;
+    double* partial = nullptr;
+    SV_TRY(chain_workspace(fn, static_cast<hipStream_t>(stream), n_req, V, &counter, &partial));
+    return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, qo_indptr, n_rows, seed,
+                                                offset, B, (int)D, V, req_index, n_req, accepted_tokens,
+                                                accept_length, counter, partial, static_cast<hipStream_t>(stream)));
 }
 
 int specverify_greedy_verify(const void* target_logits, int dtype, const int32_t* draft_ids, int64_t B,

@@ -331,9 +331,9 @@ template <int kMode>
 __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const float* __restrict__ q, const int32_t* __restrict__ x, const float* __restrict__ p,
     const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
-    const int32_t* __restrict__ req_index, int64_t n_req, int C, int R, int64_t per_xcd,
-    int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len, double* __restrict__ partial,
-    uint32_t* __restrict__ counter) {
+    const int32_t* __restrict__ qo_indptr, int64_t n_rows, const int32_t* __restrict__ req_index, int64_t n_req,
+    int C, int R, int64_t per_xcd, int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len,
+    double* __restrict__ partial, uint32_t* __restrict__ counter) {
     __shared__ ChainShared sh;
     // XCD-aware mapping: workgroups are dispatched round-robin over the 8 XCDs,
     // so consecutive virtual ids (one request's segments) share an XCD's L2.
@@ -345,6 +345,27 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     if (b < 0 || b >= B) return;   // every workgroup of this slot leaves: its counter is untouched
     const int N = D + 1;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+
+    // Target rows of request b start at row `base`; it verifies d <= D drafts.
+    // Ragged batches (qo_indptr given) pack each request's d + 1 rows; the
+    // positions past d are one-hot at token 0 for target and draft alike and
+    // so are never read: position d drafts token 0 as a point mass, every
+    // later position accepts, and the emitted count is clamped to d + 1.
+    int64_t base = b * N;
+    int d = D;
+    if (qo_indptr) {
+        const int64_t lo = qo_indptr[b], n = (int64_t)qo_indptr[b + 1] - lo;
+        if (!(n >= 1 && n <= N && lo >= 0 && lo + n <= n_rows)) {
+            // invalid length or rows outside the packed array: marked, nothing read
+            if (c == 0) {
+                if (tid < N) accepted[b * N + tid] = -1;
+                if (tid == 0) accept_len[b] = -1;
+            }
+            return;
+        }
+        base = lo;
+        d = (int)(n - 1);
+    }
 
     // ---- 1. probe (wave 0): lane i < D tests position i, lane D draws u_f.
     // The loads at the draft ids are issued before the Philox rounds, so the
@@ -359,14 +380,15 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
             // round trip
             const uint64_t so = ((tid & 1) ? offset : seed)[b];
             const int ic = tid < D ? tid : D - 1;
-            const int32_t xi = x[b * D + ic];
+            // positions from d on draft token 0 as a point mass; only row d is read
+            const int32_t xi = ic < d ? x[b * D + ic] : 0;
             const bool inr = tid < D && xi >= 0 && (int64_t)xi < V;
             const int64_t xc = inr ? (int64_t)xi : 0;
-            const float a = p[(b * N + ic) * V + xc];
-            const float cq = kMode == kDraftProbs ? q[(b * D + ic) * V + xc] : 1.0f;
+            const float a = p[(base + (ic < d ? ic : d)) * V + xc];
+            const float cq = (kMode == kDraftProbs && ic < d) ? q[(b * D + ic) * V + xc] : 1.0f;
             __builtin_amdgcn_sched_barrier(0);
             w = philox_word(read_lane(so, 0), read_lane(so, 1), (uint64_t)tid);
-            ok = inr && (double)uniform_of(w) * (double)cq < (double)a;
+            ok = (inr && (double)uniform_of(w) * (double)cq < (double)a) || (tid > d && tid < D);
             if constexpr (kMode == kPointDraft) {
                 // the rejected id, read from its lane (lanes 0..D are all active here)
                 const int32_t xsel = inr ? xi : -1;
@@ -384,12 +406,22 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     }
     __syncthreads();
     const int L = sh.L;
+    if (L > d) {
+        // a ragged request accepted token 0 at its own last position: its
+        // emitted tokens are the d drafts and 0, with no row to stream
+        if (c == 0) {
+            if (tid < N) accepted[b * N + tid] = tid < d ? x[b * D + tid] : (tid == d ? 0 : -1);
+            if (tid == 0) accept_len[b] = d;
+        }
+        return;
+    }
     // a residual row with draft probabilities streams q_L; with point-mass
-    // drafts it streams p_L alone, the rejected id xo weighing max(0, p - 1)
-    const bool resid = kMode == kDraftProbs && L < D;
-    const bool point = kMode == kPointDraft && L < D;
-    const int64_t xo = point ? (int64_t)sh.xL : -1;
-    const float* pr = p + (b * N + L) * V;
+    // drafts (and at a ragged request's own last position, token 0) it streams
+    // p_L alone, the rejected id xo weighing max(0, p - 1)
+    const bool resid = kMode == kDraftProbs && L < d;
+    const bool point = (kMode == kPointDraft && L < d) || (L == d && d < D);
+    const int64_t xo = point ? (L < d ? (int64_t)sh.xL : 0) : -1;
+    const float* pr = p + (base + L) * V;
     const float* qr = resid ? q + (b * D + L) * V : nullptr;
     const bool aligned = ((uintptr_t)pr % 16 == 0) && (!resid || (uintptr_t)qr % 16 == 0);
     const int64_t nchunks = (V + kChunk - 1) / kChunk;
@@ -530,9 +562,10 @@ static void chain_split(int64_t n_req, int64_t V, int& C, int& R) {
 }
 
 hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
-                               const uint64_t* seed, const uint64_t* offset, int64_t B, int D, int64_t V,
-                               const int32_t* req_index, int64_t n_req, int32_t* accepted, int32_t* accept_len,
-                               uint32_t* counter, double* partial, hipStream_t stream) {
+                               const int32_t* qo_indptr, int64_t n_rows, const uint64_t* seed,
+                               const uint64_t* offset, int64_t B, int D, int64_t V, const int32_t* req_index,
+                               int64_t n_req, int32_t* accepted, int32_t* accept_len, uint32_t* counter,
+                               double* partial, hipStream_t stream) {
     int C, R;
     chain_split(n_req, V, C, R);
     const int64_t total = n_req * C;
@@ -542,8 +575,8 @@ hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_id
     auto* kernel = D == 0 ? chain_reject_kernel<kNoDraft>
                           : (draft_probs ? chain_reject_kernel<kDraftProbs> : chain_reject_kernel<kPointDraft>);
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kChainBlock), 0, stream, draft_probs, draft_ids,
-                       target_probs, seed, offset, B, D, V, req_index, n_req, C, R, per_xcd, accepted, accept_len,
-                       partial, counter);
+                       target_probs, seed, offset, B, D, V, qo_indptr, n_rows, req_index, n_req, C, R, per_xcd,
+                       accepted, accept_len, partial, counter);
     return hipGetLastError();
 }
 

@@ -20,10 +20,13 @@ hipError_t launch_greedy_verify(const void* logits, int dtype, const int32_t* dr
 // between calls (the kernel resets them) and n_req * chain_partials_per_request(V)
 // doubles of partial sums.
 int64_t chain_partials_per_request(int64_t V);
+// qo_indptr NULL: dense target rows [B, D+1, V]; else packed rows [n_rows, V],
+// request b owning rows [qo_indptr[b], qo_indptr[b+1]).
 hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
-                               const uint64_t* seed, const uint64_t* offset, int64_t B, int D, int64_t V,
-                               const int32_t* req_index, int64_t n_req, int32_t* accepted, int32_t* accept_len,
-                               uint32_t* counter, double* partial, hipStream_t stream);
+                               const int32_t* qo_indptr, int64_t n_rows, const uint64_t* seed,
+                               const uint64_t* offset, int64_t B, int D, int64_t V, const int32_t* req_index,
+                               int64_t n_req, int32_t* accepted, int32_t* accept_len, uint32_t* counter,
+                               double* partial, hipStream_t stream);
 
 hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t npos, int64_t V,
                                  const float* temperature, const int32_t* top_k, const float* top_p,

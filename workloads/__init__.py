@@ -16,5 +16,6 @@ from .synth import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_config,
+    make_ragged_config,
     fuzz_case,
 )

@@ -251,6 +251,21 @@ def make_config(cfg: int, replica: int = 0, **kw) -> dict:
     return out
 
 
+def make_ragged_config(replica: int = 0) -> dict:
+    """The large-vocab inputs with per-request verify lengths: request b
+    verifies len_b ~ U{1..D+1} positions (data RNG, independent of the rest),
+    and its first len_b target rows are packed in request order
+    (``target_rows`` [sum len, V], ``qo_indptr`` [B+1])."""
+    out = make_config(3, replica)
+    B, D = out["B"], out["D"]
+    lens = data_rng(30, replica).integers(1, D + 2, B)
+    out["verify_lens"] = lens
+    out["qo_indptr"] = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    out["target_rows"] = np.ascontiguousarray(
+        np.concatenate([out["target_probs"][b, :n] for b, n in enumerate(lens)], axis=0))
+    return out
+
+
 def fuzz_case(seed: int, B: int, D: int, V: int, dtype: str = "f32", sigma: float = 2.0,
               draft_noise: float = 0.5, special: str | None = None) -> dict:
     """A small random case for parity fuzzing.
