@@ -53,8 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large_vocab_chain_reject",
-                    choices=["large_vocab_chain_reject", "large_vocab_target_only", "large_vocab_ragged", "topk_topp_chain",
-                             "greedy",
+                    choices=["large_vocab_chain_reject", "large_vocab_target_only", "large_vocab_ragged", "d2t_expand",
+                             "topk_topp_chain", "greedy",
                              "mixed", "mixed_fused"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
@@ -306,6 +306,62 @@ class RaggedWorkload:
         return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
                 "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
                           f"{el:.1f}s single-threaded numpy"}
+
+
+class DraftVocabWorkload:
+    """Draft distributions over a 32000-entry draft vocabulary placed into the 128256-entry target
+    vocabulary (ascending d2t table), 256 requests x 5 drafts."""
+    name = "d2t_expand"
+    kernel = "d2t_expand_kernel"
+    sources = ("d2t_expand.hip", "sv_common.hpp")
+    counters = "d2t_expand_counters.txt"
+    dtype = "f32"
+
+    def __init__(self, dev, replicas):
+        from workloads import make_d2t
+        self.B, self.D, self.Vd, self.V = 256, 5, 32000, 128256
+        rows = self.B * self.D
+        rng = np.random.default_rng(7)
+        q = rng.random((rows, self.Vd), dtype=np.float32)
+        self.d2t_host = make_d2t(0, self.Vd, self.V)
+        self.q_host = q
+        self.R = replicas or 4
+        import torch
+        self.reps = [dict(q=_t(q, dev), out=torch.empty((rows, self.V), dtype=torch.float32, device=dev))
+                     for _ in range(self.R)]
+        import token_sampling_temp_amd as sv
+        self.sv = sv
+        self.t2d = sv.d2t_inverse(_t(self.d2t_host, dev), self.Vd, self.V)   # once per table
+        self.rows = rows
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        self.sv.d2t_expand(r["q"], self.t2d, out=r["out"])
+
+    def algorithmic_bytes(self):
+        """Per row: the target row written (4 V) and the draft row read (4 Vd); the inverse table
+        (4 V) once."""
+        return float(self.rows * (4 * self.V + 4 * self.Vd) + 4 * self.V)
+
+    def extra(self):
+        return {}
+
+    def config(self):
+        return {"workload": self.name, "rows": self.rows, "draft_vocab": self.Vd, "vocab": self.V,
+                "input": "float32 draft probabilities, inverse table of an ascending d2t table", "replicas": self.R}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        rows, t0, passes = 0, time.perf_counter(), 0
+        while True:
+            oracle.d2t_expand(self.q_host, self.d2t_host, self.V)
+            rows += self.rows
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{passes} full expansions of {self.rows} rows, {el:.1f}s single-threaded numpy"}
 
 
 class GreedyWorkload:
@@ -602,7 +658,8 @@ class MixedFusedWorkload(MixedWorkload):
         return self.bytes_by_call["verify_fused"]
 
 
-WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
+WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, DraftVocabWorkload,
+                                 GreedyWorkload, TopkToppWorkload, MixedWorkload,
                                  MixedFusedWorkload)}
 
 

@@ -178,6 +178,37 @@ int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* draf
                                    int32_t* accepted_tokens, int32_t* accept_length, void* stream);
 
 /*
+ * Draft -> target vocabulary placement of draft distributions.
+ *
+ * Passage: "TensorRT-LLM _torch/speculative/interface.py", one-model sampler
+ * (draft vocabulary smaller than the target's): target_indices =
+ * (source_indices + d2t) % vocab_size, computed once and kept in the
+ * speculative metadata, and the draft probabilities are scattered into a
+ * zero-filled full_draft_probs; without a d2t table they fill the first Vd
+ * entries.  The result is the draft_probs argument of specverify_chain_reject
+ * / specverify_chain_reject_ragged (draft ids are target-vocabulary ids).
+ *
+ * specverify_d2t_inverse builds, once per table, the inverse map
+ *   d2t  [Vd] int64 offsets or NULL (then Vd <= V); draft entry s belongs to
+ *        target entry (s + d2t[s]) mod V, a floor modulus (negative offsets wrap)
+ *   t2d  [V] int32 output: the draft entry of each target entry, -1 for none
+ * The mapping must send distinct draft entries to distinct target entries,
+ * as the page's scatter assumes; otherwise which entry a shared target keeps
+ * is unspecified.
+ *
+ * specverify_d2t_expand places the rows (a gather: every output row is
+ * written once, in order)
+ *   draft_probs      [rows, Vd] float32 (rows = B * D)
+ *   t2d              [V] int32 from specverify_d2t_inverse
+ *   full_draft_probs [rows, V] float32 output: entry t = draft_probs[t2d[t]],
+ *                    0 where t2d[t] is outside [0, Vd)
+ * Neither call uses a workspace.
+ */
+int specverify_d2t_inverse(const int64_t* d2t, int64_t Vd, int64_t V, int32_t* t2d, void* stream);
+int specverify_d2t_expand(const float* draft_probs, const int32_t* t2d, int64_t rows, int64_t Vd, int64_t V,
+                          float* full_draft_probs, void* stream);
+
+/*
  * Greedy chain verify.
  *
  * Passage: "tokenspeed sampling/backends/flashinfer.py",

@@ -18,6 +18,7 @@ from .verify import (  # noqa: F401
     chain_reject_core,
     chain_reject_ragged,
     chain_uniforms,
+    d2t_expand,
     decode_logits,
     greedy_verify,
     gumbel_row,

@@ -275,6 +275,28 @@ def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, requests=No
     return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
 
 
+# --------------------------------------------------------------------------- draft -> target vocabulary
+def d2t_expand(draft_probs, d2t, V: int) -> np.ndarray:
+    """Draft distributions over a reduced draft vocabulary, placed in the target vocabulary.
+
+    TensorRT-LLM interface.py, one-model sampler: draft entry s goes to
+    target index (s + d2t[s]) mod V of a zero-filled row
+    (``target_indices = (source_indices + d2t) % vocab_size``); without a
+    d2t table the draft vocabulary is the first Vd target entries.  The
+    mapping is assumed one-to-one, as the page's scatter does.
+    draft_probs [..., Vd] -> [..., V] (same dtype).
+    """
+    draft_probs = np.asarray(draft_probs)
+    Vd = draft_probs.shape[-1]
+    out = np.zeros(draft_probs.shape[:-1] + (V,), dtype=draft_probs.dtype)
+    if d2t is None:
+        out[..., :Vd] = draft_probs
+    else:
+        target = (np.arange(Vd, dtype=np.int64) + np.asarray(d2t, dtype=np.int64)) % V   # floor mod, as torch's %
+        out[..., target] = draft_probs
+    return out
+
+
 # --------------------------------------------------------------------------- ragged chain rejection
 def ragged_pad(draft_probs, draft_ids, target_packed, qo_indptr, D: int):
     """The padded rectangle a ragged verify batch is scattered into.

@@ -19,7 +19,7 @@ P = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(specverify_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(specverify_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -132,6 +132,26 @@ def test_chain_reject_ragged_invalid_arguments():
     assert L.specverify_chain_reject_ragged(P, P, None, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
     assert L.specverify_chain_reject_ragged(None, None, None, None, 0, None, None, 4, 3, 10, P, 0, None, None,
                                             None) == 0
+
+
+def test_d2t_invalid_arguments():
+    L = sv.lib()
+    # inverse: (d2t, Vd, V, t2d, stream)
+    assert L.specverify_d2t_inverse(None, 12, 10, P, None) == 1
+    assert "Vd=12" in L.specverify_last_error().decode()
+    assert L.specverify_d2t_inverse(P, 0, 10, P, None) == 1
+    assert L.specverify_d2t_inverse(P, 8, 0, P, None) == 1
+    assert L.specverify_d2t_inverse(P, 8, 10, None, None) == 1
+    assert "t2d" in L.specverify_last_error().decode()
+    # expand: (draft_probs, t2d, rows, Vd, V, out, stream)
+    assert L.specverify_d2t_expand(P, P, -1, 8, 10, P, None) == 1
+    assert L.specverify_d2t_expand(P, P, 4, 0, 10, P, None) == 1
+    assert L.specverify_d2t_expand(None, P, 4, 8, 10, P, None) == 1
+    assert "draft_probs" in L.specverify_last_error().decode()
+    assert L.specverify_d2t_expand(P, None, 4, 8, 10, P, None) == 1
+    assert "t2d" in L.specverify_last_error().decode()
+    assert L.specverify_d2t_expand(P, P, 4, 8, 10, None, None) == 1
+    assert L.specverify_d2t_expand(None, None, 0, 8, 10, None, None) == 0
 
 
 def test_binding_rejects_cpu_tensors():

@@ -106,3 +106,27 @@ def test_clamp_padding_and_invalid_lengths():
     out = chain_reject_ragged(q, x, rows, bad, seed, off)
     for b in (0, 2, B - 1):
         assert out["accept_length"][b] == -1 and np.all(out["accepted_tokens"][b] == -1)
+
+
+def test_d2t_expand_placement_and_mass():
+    """Draft -> target placement: with a zero table and equal vocabularies it
+    is the identity; otherwise every draft entry lands at (s + d2t[s]) mod V
+    (negative offsets wrap as a floor modulus), every other target entry is
+    zero, and each row keeps its mass."""
+    from oracle import d2t_expand
+    rng = np.random.default_rng(73)
+    q = _rows(rng, 8, 6)
+    assert np.array_equal(d2t_expand(q, np.zeros(8, np.int64), 8), q)
+    assert np.array_equal(d2t_expand(q, None, 8), q)
+    # a hand-worked table: V = 11, draft ids 0..7 at targets 3, 4, 10, 0, 1, 5, 6, 9
+    d2t = np.array([3, 3, 8, -3, -3, 0, 0, 2], np.int64)
+    want = [3, 4, 10, 0, 1, 5, 6, 9]
+    out = d2t_expand(q, d2t, 11)
+    for s_, t in enumerate(want):
+        assert np.array_equal(out[:, t], q[:, s_])
+    others = np.setdiff1d(np.arange(11), want)
+    assert np.all(out[:, others] == 0)
+    assert np.allclose(out.astype(np.float64).sum(-1), q.astype(np.float64).sum(-1), rtol=0, atol=1e-12)
+    # without a table the draft vocabulary is the first Vd target entries
+    out = d2t_expand(q, None, 11)
+    assert np.array_equal(out[:, :8], q) and np.all(out[:, 8:] == 0)

@@ -335,6 +335,62 @@ def test_chain_reject_ragged_large_vocab_full(sv):
     log(f"ragged large vocab: mean accept length {np_i(alen).mean():.3f}, flagged {flagged}")
 
 
+def test_d2t_expand(sv):
+    """Draft -> target placement, bit-exact, through the inverse table:
+    ascending and shuffled tables, negative offsets, no table, odd and
+    unaligned row lengths."""
+    torch = __import__("torch")
+    from workloads import make_d2t
+    rng = np.random.default_rng(1401)
+    for i, (rows, Vd, V, kind) in enumerate([(7, 100, 1000, "sorted"), (5, 999, 1003, "shuffled"),
+                                             (3, 1000, 1000, "shuffled"), (6, 37, 4097, None),
+                                             (1280, 3200, 12826, "sorted"), (4, 32000, 128256, "sorted")]):
+        q = rng.random((rows, Vd)).astype(np.float32)
+        d2t = None if kind is None else make_d2t(i, Vd, V, shuffled=kind == "shuffled")
+        log(f"d2t expand {i}: rows={rows} Vd={Vd} V={V} table={kind}")
+        ref = oracle.d2t_expand(q, d2t, V)
+        t2d = sv.d2t_inverse(None if d2t is None else dev(d2t), Vd, V, device="cuda")
+        want = np.full(V, -1, np.int64)
+        want[np.arange(Vd) if d2t is None else (np.arange(Vd) + d2t) % V] = np.arange(Vd)
+        assert np.array_equal(np_i(t2d).astype(np.int64), want), i
+        out = sv.d2t_expand(dev(q), t2d)
+        assert np.array_equal(out.cpu().numpy(), ref), i
+    # an output row view that is not 16-byte aligned, guard bands intact
+    rows, Vd, V = 4, 300, 1001
+    q = rng.random((rows, Vd)).astype(np.float32)
+    d2t = make_d2t(9, Vd, V)
+    flat = torch.full((rows * V + 6,), 7.0, device="cuda")
+    out = flat[3:3 + rows * V].view(rows, V)
+    log(f"d2t expand unaligned output: rows={rows} Vd={Vd} V={V}")
+    sv.d2t_expand(dev(q), sv.d2t_inverse(dev(d2t), Vd, V), out=out)
+    assert np.array_equal(out.cpu().numpy(), oracle.d2t_expand(q, d2t, V))
+    f = flat.cpu().numpy()
+    assert np.all(f[:3] == 7.0) and np.all(f[3 + rows * V:] == 7.0)
+
+
+def test_ragged_verify_with_reduced_draft_vocab(sv):
+    """The reduced-vocabulary drafter end to end: d2t placement, then the
+    ragged chain verify, against the oracle's placement and ragged verify."""
+    from workloads import make_d2t
+    for B, D, Vd, V in ((6, 3, 300, 1000), (260, 4, 3200, 12288)):
+        rng = np.random.default_rng(B + V)
+        c = fuzz_case(1500 + B, B, D, V, "f32")
+        d2t = make_d2t(B, Vd, V)
+        tgt = (np.arange(Vd) + d2t) % V
+        # draft distributions over the draft vocabulary: the fuzz draft rows restricted to the mapped ids
+        qd = c["draft_probs"][:, :, tgt].astype(np.float64)
+        qd = (qd / qd.sum(-1, keepdims=True)).astype(np.float32)
+        x = tgt[rng.integers(0, Vd, (B, D))].astype(np.int32)          # draft ids are target ids
+        lens = rng.integers(1, D + 2, B)
+        rows, ind = _ragged_pack(c, lens)
+        log(f"ragged verify with a reduced draft vocabulary: B={B} D={D} Vd={Vd} V={V}")
+        q_full = oracle.d2t_expand(qd, d2t, V)
+        ref = oracle.chain_reject_ragged(q_full, x, rows, ind, c["seed"], c["offset"])
+        qg = sv.d2t_expand(dev(qd), sv.d2t_inverse(dev(d2t), Vd, V))
+        acc, alen = sv.chain_reject_ragged(qg, dev(x), dev(rows), dev(ind), dev(c["seed"]), dev(c["offset"]))
+        assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, Vd, V))
+
+
 def test_chain_reject_request_subset_and_determinism(sv):
     B, D, V = 9, 4, 3001
     c = fuzz_case(91, B, D, V, "f32")

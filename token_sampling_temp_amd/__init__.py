@@ -13,6 +13,8 @@ Functions mirror the C entry points:
 * ``chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None)``
 * ``chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None)``:
   per-request verify lengths over packed target rows
+* ``d2t_inverse(d2t, Vd, V)`` and ``d2t_expand(draft_probs, t2d)``: draft distributions over a
+  reduced draft vocabulary placed in the target vocabulary
 * ``greedy_verify(target_logits, draft_ids, req_index=None, ...)``
 * ``gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, ...)``
 * ``verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None,
@@ -38,6 +40,8 @@ SYMBOLS = (
     "specverify_softmax_renorm",
     "specverify_chain_reject",
     "specverify_chain_reject_ragged",
+    "specverify_d2t_inverse",
+    "specverify_d2t_expand",
     "specverify_greedy_verify",
     "specverify_gumbel_sample",
     "specverify_verify_fused",
@@ -71,11 +75,13 @@ def lib() -> ctypes.CDLL:
     L.specverify_softmax_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp, vp]
     L.specverify_chain_reject.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
     L.specverify_chain_reject_ragged.argtypes = [vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.specverify_d2t_inverse.argtypes = [vp, i64, i64, vp, vp]
+    L.specverify_d2t_expand.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
     for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_chain_reject_ragged",
-                 "specverify_greedy_verify",
+                 "specverify_d2t_inverse", "specverify_d2t_expand", "specverify_greedy_verify",
                  "specverify_gumbel_sample", "specverify_verify_fused"):
         getattr(L, name).restype = ctypes.c_int
     L.specverify_status_string.argtypes = [ctypes.c_int]
@@ -274,6 +280,47 @@ def chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, o
         B, D, V, _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
     _check("specverify_chain_reject_ragged", st)
     return acc, alen
+
+
+def d2t_inverse(d2t, Vd, V, device=None, out=None):
+    """Inverse map t2d [V] int32 (draft entry of each target entry, -1 for none) of the offset
+    table d2t [Vd] int64 (None: the first Vd target entries); built once per table."""
+    torch = _torch()
+    if d2t is not None:
+        _need(d2t, "d2t", (torch.int64,), None, 1)
+        if d2t.shape[0] != Vd:
+            raise ValueError(f"d2t must have shape [{Vd}]")
+        device = d2t.device
+    if device is None:
+        raise ValueError("device is required when d2t is None")
+    if out is None:
+        out = torch.empty((int(V),), dtype=torch.int32, device=device)
+    else:
+        _need(out, "out", (torch.int32,), torch.device(device), 1)
+    st = lib().specverify_d2t_inverse(_ptr(d2t), int(Vd), int(V), _ptr(out), _stream_ptr(torch.device(device)))
+    _check("specverify_d2t_inverse", st)
+    return out
+
+
+def d2t_expand(draft_probs, t2d, out=None):
+    """Place draft_probs [..., Vd] into the target vocabulary with the inverse map t2d [V]:
+    [..., V], entry t = draft_probs[..., t2d[t]] (0 where t2d[t] < 0)."""
+    torch = _torch()
+    _need(draft_probs, "draft_probs", (torch.float32,), None)
+    dev = draft_probs.device
+    _need(t2d, "t2d", (torch.int32,), dev, 1)
+    Vd, V = int(draft_probs.shape[-1]), int(t2d.shape[0])
+    rows = draft_probs.numel() // Vd if Vd else 0
+    shape = tuple(draft_probs.shape[:-1]) + (V,)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must be {shape}")
+    st = lib().specverify_d2t_expand(_ptr(draft_probs), _ptr(t2d), rows, Vd, V, _ptr(out), _stream_ptr(dev))
+    _check("specverify_d2t_expand", st)
+    return out
 
 
 def greedy_verify(target_logits, draft_ids, req_index=None, predict=True, accept_index=True,

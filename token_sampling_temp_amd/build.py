@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "chain_reject.hip", "greedy_verify.hip", "softmax_renorm.hip", "gumbel_sample.hip",
-           "fused_verify.hip"]
+           "fused_verify.hip", "d2t_expand.hip"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

@@ -224,6 +224,39 @@ int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* draf
                                                 accept_length, counter, partial, static_cast<hipStream_t>(stream)));
 }
 
+int specverify_d2t_inverse(const int64_t* d2t, int64_t Vd, int64_t V, int32_t* t2d, void* stream) {
+    const char* fn = "specverify_d2t_inverse";
+    if (V < 1 || V > kMaxV)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: V=%lld must be in [1, 2^31)", fn, (long long)V);
+    if (Vd < 1 || Vd > kMaxV)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: Vd=%lld must be in [1, 2^31)", fn, (long long)Vd);
+    if (!d2t && Vd > V)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: without a d2t table Vd=%lld must not exceed V=%lld", fn,
+                    (long long)Vd, (long long)V);
+    SV_REQUIRE(t2d, "t2d");
+    SV_TRY(check_device());
+    return launched(fn, sv::launch_d2t_inverse(d2t, Vd, V, t2d, static_cast<hipStream_t>(stream)));
+}
+
+int specverify_d2t_expand(const float* draft_probs, const int32_t* t2d, int64_t rows, int64_t Vd, int64_t V,
+                          float* full_draft_probs, void* stream) {
+    const char* fn = "specverify_d2t_expand";
+    if (rows < 0) return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: rows=%lld must be >= 0", fn, (long long)rows);
+    if (V < 1 || V > kMaxV)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: V=%lld must be in [1, 2^31)", fn, (long long)V);
+    if (Vd < 1 || Vd > kMaxV)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: Vd=%lld must be in [1, 2^31)", fn, (long long)Vd);
+    if ((long double)rows * (long double)(V > Vd ? V : Vd) * 4.0L > 4.0e18L)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: tensor size overflows", fn);
+    if (rows == 0) return SPECVERIFY_OK;
+    SV_REQUIRE(draft_probs, "draft_probs");
+    SV_REQUIRE(t2d, "t2d");
+    SV_REQUIRE(full_draft_probs, "full_draft_probs");
+    SV_TRY(check_device());
+    return launched(fn, sv::launch_d2t_expand(draft_probs, t2d, rows, Vd, V, full_draft_probs,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int specverify_greedy_verify(const void* target_logits, int dtype, const int32_t* draft_ids, int64_t B,
                              int64_t D, int64_t V, const int32_t* req_index, int64_t n_req,
                              int32_t* accepted_tokens, int32_t* accept_length, int32_t* predict,

@@ -28,6 +28,14 @@ hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_id
                                int64_t n_req, int32_t* accepted, int32_t* accept_len, uint32_t* counter,
                                double* partial, hipStream_t stream);
 
+// Draft -> target vocabulary placement.  launch_d2t_inverse builds t2d [V]
+// (draft entry of each target entry, -1 for none) from the offset table
+// d2t [Vd] (NULL: the first Vd target entries); launch_d2t_expand writes
+// out [rows, V] with out[t] = draft_probs[t2d[t]] (0 where t2d[t] < 0).
+hipError_t launch_d2t_inverse(const int64_t* d2t, int64_t Vd, int64_t V, int32_t* t2d, hipStream_t stream);
+hipError_t launch_d2t_expand(const float* draft_probs, const int32_t* t2d, int64_t rows, int64_t Vd, int64_t V,
+                             float* out, hipStream_t stream);
+
 hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t npos, int64_t V,
                                  const float* temperature, const int32_t* top_k, const float* top_p,
                                  const int32_t* req_index, int64_t n_req, float* probs_out,

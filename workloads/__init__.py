@@ -16,6 +16,7 @@ from .synth import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_config,
+    make_d2t,
     make_ragged_config,
     fuzz_case,
 )

@@ -266,6 +266,18 @@ def make_ragged_config(replica: int = 0) -> dict:
     return out
 
 
+def make_d2t(seed: int, Vd: int, V: int, shuffled: bool = False) -> np.ndarray:
+    """A one-to-one draft -> target offset table: draft id s maps to target id
+    t_s = s + d2t[s] (mod V), the t_s a seeded sample of Vd distinct target
+    ids, ascending (a reduced-vocabulary drafter keeps the target's order) or
+    shuffled."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2000, seed, Vd, V])))
+    t = rng.choice(V, size=Vd, replace=False)
+    if not shuffled:
+        t = np.sort(t)
+    return (t.astype(np.int64) - np.arange(Vd, dtype=np.int64))
+
+
 def fuzz_case(seed: int, B: int, D: int, V: int, dtype: str = "f32", sigma: float = 2.0,
               draft_noise: float = 0.5, special: str | None = None) -> dict:
     """A small random case for parity fuzzing.
