@@ -23,10 +23,12 @@ from .verify import (  # noqa: F401
     greedy_verify,
     gumbel_row,
     gumbel_sample,
+    joint_filter_row,
     one_hot_drafts,
     ragged_pad,
     renorm_row,
     residual_draw,
+    sample,
     softmax_renorm,
     temperature_softmax,
     verify_fused,

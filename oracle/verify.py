@@ -150,6 +150,95 @@ def softmax_renorm(logits, dtype, temperature, top_k=None, top_p=None, requests=
     return out, flags
 
 
+# --------------------------------------------------------------------------- single-step sampling
+MINP_BAND = 1e-9
+
+
+def joint_filter_row(z: np.ndarray, temperature: float, top_k: int, top_p: float, min_p: float):
+    """Weights of one row after the joint top-k / top-p / min-p filter.
+
+    tokenspeed flashinfer.py, ``sample``: ``softmax(logits, temperature)``
+    then ``top_k_top_p_sampling_from_probs(..., filter_apply_order="joint")``:
+    both filters judge the unfiltered distribution and a token is kept when
+    it passes both -- top-k keeps every value >= the k-th largest (ties kept,
+    off when k <= 0 or k >= V), top-p keeps the smallest set of largest values
+    whose mass reaches top_p of the row's whole mass (ties at the threshold
+    kept, active iff top_p < 1).  TensorRT-LLM interface.py passes per-request
+    ``min_ps`` to its fused sampler; read plainly, min-p keeps p_v >= min_p *
+    p_max, i.e. (z_v - max z) >= T ln(min_p), compared on logits in float64
+    (off when min_p <= 0).
+    Returns (unnormalised kept weights exp((z - max) / T) float64 [V], flagged):
+    ``flagged`` marks a row with a top-p threshold within TOPP_BAND of a mass
+    boundary or a logit within MINP_BAND of the min-p threshold.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    V = z.shape[0]
+    m = z.max()
+    T = float(temperature)
+    w = np.exp((z - m) / T)
+    kept = np.ones(V, dtype=bool)
+    k = int(top_k)
+    if 0 < k < V:
+        kth = np.partition(z, V - k)[V - k]
+        kept &= z >= kth
+    flagged = False
+    tp = float(top_p)
+    if tp < 1.0:
+        total = math.fsum(w)
+        vals, inv = np.unique(z, return_inverse=True)
+        mass = np.bincount(inv.reshape(-1), weights=w)
+        cum = np.cumsum(mass[::-1])
+        hit = np.nonzero(cum >= tp * total)[0]
+        i = int(hit[0]) if hit.size else cum.shape[0] - 1
+        kept &= z >= vals[::-1][i]
+        near = abs(cum[i] / total - tp) < TOPP_BAND
+        if i > 0:
+            near = near or abs(cum[i - 1] / total - tp) < TOPP_BAND
+        flagged = bool(near)
+    mp = float(min_p)
+    if mp > 0.0:
+        thr = T * math.log(mp)
+        d = z - m
+        kept &= d >= thr
+        flagged = flagged or bool(np.any(np.abs(d - thr) < MINP_BAND * max(1.0, abs(thr))))
+    return np.where(kept, w, 0.0), flagged
+
+
+def sample(logits, dtype, temperature, top_k, top_p, min_p, seed, offset, requests=None):
+    """Single-step sampling of one token per request from logits [B, V].
+
+    tokenspeed flashinfer.py, ``sample``: all-greedy batches take the row
+    argmax; otherwise the joint-filtered, renormalised temperature softmax is
+    sampled with the request's Philox (seed, offset).  Here a row below the
+    greedy temperature takes its argmax; every other row draws by inverse CDF
+    over ascending vocabulary index with the uniform of word 0 of its stream
+    (the bonus draw of a verify without drafts).  Per-request arrays may be
+    None (top_k off, top_p 1, min_p 0).
+    Returns dict(tokens [B] int64 (-2 where not computed), flagged [B] bool).
+    """
+    B, V = np.shape(logits)
+    tokens = np.full(B, -2, dtype=np.int64)
+    flagged = np.zeros(B, dtype=bool)
+    reqs = range(B) if requests is None else [int(r) for r in requests]
+    for b in reqs:
+        z = decode_logits(logits[b], dtype)
+        T = float(temperature[b])
+        if is_greedy(T):
+            tokens[b] = int(np.argmax(z))
+            continue
+        k = 0 if top_k is None else int(top_k[b])
+        tp = 1.0 if top_p is None else float(top_p[b])
+        mp = 0.0 if min_p is None else float(min_p[b])
+        r, fl = joint_filter_row(z, T, k, tp, mp)
+        wd = philox.words(int(seed[b]), int(offset[b]), 1)
+        u = float(philox.uniform(wd)[0])
+        code = int(philox.uniform_code(wd)[0])
+        y, near = residual_draw(r, r, u, code)
+        tokens[b] = y
+        flagged[b] = fl or near
+    return dict(tokens=tokens, flagged=flagged)
+
+
 # --------------------------------------------------------------------------- chain rejection
 def chain_uniforms(seed: int, offset: int, D: int):
     """Accept uniforms u_0..u_{D-1} and the final uniform (with its odd code) of one request."""
