@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large_vocab_chain_reject",
                     choices=["large_vocab_chain_reject", "large_vocab_target_only", "large_vocab_ragged", "d2t_expand",
-                             "topk_topp_chain", "greedy",
+                             "sample", "topk_topp_chain", "greedy",
                              "mixed", "mixed_fused"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
@@ -364,6 +364,67 @@ class DraftVocabWorkload:
                 "sample": f"{passes} full expansions of {self.rows} rows, {el:.1f}s single-threaded numpy"}
 
 
+class SampleWorkload:
+    """Single-step sampling of 1024 bf16 rows of V=129280: a quarter greedy, the rest T ~ U[0.5, 1.2]
+    with top-k in {0, 20, 100}, top-p 1 or U[0.8, 0.95] and min-p in {0, 0.05} (joint filter)."""
+    name = "sample"
+    kernel = "sample_kernel"
+    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_common.hpp")
+    counters = "sample_counters.txt"
+    dtype = "bf16"
+
+    def __init__(self, dev, replicas):
+        from workloads import make_sample_config
+        t0 = time.time()
+        self.host = make_sample_config()
+        log(f"generated inputs in {time.time() - t0:.1f}s")
+        h = self.host
+        self.B, self.V = h["logits"].shape
+        self.R = replicas or 2
+        self.reps = []
+        for r in range(self.R):
+            off = np.full(self.B, 4096 * r, np.uint64)
+            self.reps.append(dict(z=_bf16(h["logits"], dev), T=_t(h["temperature"], dev), k=_t(h["top_k"], dev),
+                                  p=_t(h["top_p"], dev), mp=_t(h["min_p"], dev), seed=_t(h["seed"], dev),
+                                  off=_t(off, dev), off_host=off))
+        import token_sampling_temp_amd as sv
+        import torch
+        self.sv = sv
+        self.out = torch.empty((self.B,), dtype=torch.int32, device=dev)
+        self.rows = self.B
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        self.sv.sample(r["z"], r["T"], r["seed"], r["off"], top_k=r["k"], top_p=r["p"], min_p=r["mp"], out=self.out)
+
+    def algorithmic_bytes(self):
+        """One read of every logit row (2 V bytes) and the token written."""
+        return float(self.B * (2 * self.V + 4) + self.B * 32)
+
+    def extra(self):
+        return {}
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "vocab": self.V, "input": "bf16 logits, per-row "
+                "temperature, top-k, top-p, min-p (joint filter)", "replicas": self.R}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, n = 0, time.perf_counter(), 0
+        while True:
+            reqs = [(n * 16 + j) % self.B for j in range(16)]
+            oracle.sample(h["logits"], "bf16", h["temperature"], h["top_k"], h["top_p"], h["min_p"], h["seed"],
+                          h["offset"], requests=reqs)
+            rows += len(reqs)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{rows} rows in groups of 16, {el:.1f}s single-threaded numpy"}
+
+
 class GreedyWorkload:
     name = "greedy"
     kernel = "greedy_verify_kernel"
@@ -659,7 +720,7 @@ class MixedFusedWorkload(MixedWorkload):
 
 
 WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, DraftVocabWorkload,
-                                 GreedyWorkload, TopkToppWorkload, MixedWorkload,
+                                 SampleWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
                                  MixedFusedWorkload)}
 
 

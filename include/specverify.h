@@ -209,6 +209,38 @@ int specverify_d2t_expand(const float* draft_probs, const int32_t* t2d, int64_t 
                           float* full_draft_probs, void* stream);
 
 /*
+ * Single-step sampling: one token per request from its logits row.
+ *
+ * Passage: "tokenspeed sampling/backends/flashinfer.py", sample -- all-greedy
+ * batches take the row argmax; otherwise softmax(logits, temperature) and
+ * top_k_top_p_sampling_from_probs(probs, top_k, top_p, filter_apply_order=
+ * "joint", seed, offset, deterministic=True).  Min-p: "TensorRT-LLM
+ * _torch/speculative/interface.py" passes per-request min_ps to its fused
+ * sampler.
+ *
+ * logits      [B, V] float32 or bf16 (dtype), V <= 524288
+ * temperature [B] float32; below 1e-5 the row takes its lowest-index argmax
+ * top_k       [B] int32 or NULL (off); top_p [B] float32 or NULL (1, off);
+ * min_p       [B] float32 or NULL (0, off)
+ * seed, offset [B] uint64: the request's Philox stream; the draw uses word 0
+ * tokens      [B] int32 output
+ *
+ * Joint filter: top-k keeps every value >= the k-th largest (ties kept; off
+ * for k <= 0 or k >= V); top-p keeps the smallest set of largest values whose
+ * mass reaches top_p of the WHOLE row's mass (ties kept; active iff
+ * top_p < 1); both judge the unfiltered row, and a token is kept when it
+ * passes both.  Min-p keeps (z - max z) >= T ln(min(min_p, 1)), compared on
+ * logits in double precision (active iff min_p > 0), i.e. p >= min_p * p_max.
+ * The token is y = min{ j : sum_{v<=j} p'_v > u * R } over the kept,
+ * renormalised probabilities p' (double sums in ascending index order), u
+ * the uniform of word 0.  No workspace.
+ */
+int specverify_sample(const void* logits, int dtype, const float* temperature, const int32_t* top_k,
+                      const float* top_p, const float* min_p, const uint64_t* seed, const uint64_t* offset,
+                      int64_t B, int64_t V, const int32_t* req_index, int64_t n_req, int32_t* tokens,
+                      void* stream);
+
+/*
  * Greedy chain verify.
  *
  * Passage: "tokenspeed sampling/backends/flashinfer.py",

@@ -197,7 +197,7 @@ def joint_filter_row(z: np.ndarray, temperature: float, top_k: int, top_p: float
         flagged = bool(near)
     mp = float(min_p)
     if mp > 0.0:
-        thr = T * math.log(mp)
+        thr = T * math.log(min(mp, 1.0))      # min_p >= 1 keeps the maximal value(s)
         d = z - m
         kept &= d >= thr
         flagged = flagged or bool(np.any(np.abs(d - thr) < MINP_BAND * max(1.0, abs(thr))))

@@ -154,6 +154,21 @@ def test_d2t_invalid_arguments():
     assert L.specverify_d2t_expand(None, None, 0, 8, 10, None, None) == 0
 
 
+def test_sample_invalid_arguments():
+    L = sv.lib()
+    # (logits, dtype, T, top_k, top_p, min_p, seed, offset, B, V, req_index, n_req, tokens, stream)
+    assert L.specverify_sample(P, 2, P, None, None, None, P, P, 4, 10, None, 4, P, None) == 1
+    assert "dtype=2" in L.specverify_last_error().decode()
+    assert L.specverify_sample(P, 1, None, None, None, None, P, P, 4, 10, None, 4, P, None) == 1
+    assert "temperature" in L.specverify_last_error().decode()
+    assert L.specverify_sample(P, 1, P, None, None, None, P, P, 4, 600000, None, 4, P, None) == 1
+    assert "exceeds" in L.specverify_last_error().decode()
+    assert L.specverify_sample(P, 1, P, None, None, None, P, P, 4, 10, None, 4, None, None) == 1
+    assert "tokens" in L.specverify_last_error().decode()
+    assert L.specverify_sample(P, 1, P, None, None, None, None, P, 4, 10, None, 4, P, None) == 1
+    assert L.specverify_sample(None, 0, None, None, None, None, None, None, 4, 10, P, 0, None, None) == 0
+
+
 def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     z = torch.zeros(2, 3, 8)

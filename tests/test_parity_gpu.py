@@ -391,6 +391,62 @@ def test_ragged_verify_with_reduced_draft_vocab(sv):
         assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, Vd, V))
 
 
+def _sample_params(rng, B, V):
+    T = rng.uniform(0.4, 1.3, B).astype(np.float32)
+    T[rng.random(B) < 0.15] = 0.0                                            # greedy rows
+    k = np.where(rng.random(B) < 0.5, rng.choice([1, 2, 5, 20, 100, V, V + 3], B), 0).astype(np.int32)
+    tp = np.where(rng.random(B) < 0.6, rng.uniform(0.0, 1.0, B), 1.0).astype(np.float32)
+    mp = np.where(rng.random(B) < 0.4, rng.choice([0.001, 0.02, 0.1, 0.5, 1.0, 1.5], B), 0.0).astype(np.float32)
+    return T, k, tp, mp
+
+
+def test_sample_fuzz(sv):
+    """Single-step sampling against the oracle: f32 and bf16 rows, greedy
+    rows, every filter alone and together (k = 1, k >= V, top_p 0, min_p >= 1),
+    ties, all-zero rows, odd V, optional parameter arrays absent."""
+    flagged = 0
+    for i, (B, V, dt, sp) in enumerate([(40, 1000, "f32", None), (40, 1000, "bf16", None), (33, 4097, "bf16", "ties"),
+                                        (20, 32000, "bf16", None), (17, 3001, "f32", "zeros"), (9, 7, "f32", None),
+                                        (12, 129280, "bf16", None), (8, 1, "bf16", None)]):
+        c = fuzz_case(1600 + i, B, 0, V, dt, special=sp)
+        z = c["logits"][:, 0]
+        rng = np.random.default_rng(1600 + i)
+        T, k, tp, mp = _sample_params(rng, B, V)
+        for opt in ((k, tp, mp), (None, None, None), (k, None, mp)):
+            log(f"sample fuzz {i}: B={B} V={V} dtype={dt} special={sp} filters={[o is not None for o in opt]}")
+            ref = oracle.sample(z, dt, T, opt[0], opt[1], opt[2], c["seed"], c["offset"])
+            tok = sv.sample(dev_logits(np.ascontiguousarray(z), dt), dev(T), dev(c["seed"]), dev(c["offset"]),
+                            top_k=None if opt[0] is None else dev(opt[0]),
+                            top_p=None if opt[1] is None else dev(opt[1]),
+                            min_p=None if opt[2] is None else dev(opt[2]))
+            got = np_i(tok)
+            ok = (got == ref["tokens"]) | ref["flagged"]
+            assert np.all(ok), (i, np.nonzero(~ok)[0], got[~ok], ref["tokens"][~ok])
+            flagged += int(ref["flagged"].sum())
+    log(f"sample flagged rows: {flagged}")
+
+
+def test_sample_mixed_batch_and_subset(sv):
+    """The mixed workload's rows (B=1024, V=129280 bf16), sampled through a
+    request subset; rows outside it are untouched."""
+    torch = __import__("torch")
+    from workloads import make_sample_config
+    c = make_sample_config()
+    B, V = c["logits"].shape
+    reqs = np.random.default_rng(3).permutation(B)[:200].astype(np.int32)
+    log(f"sample mixed batch: B={B} V={V} n_req={len(reqs)}")
+    ref = oracle.sample(c["logits"], "bf16", c["temperature"], c["top_k"], c["top_p"], c["min_p"], c["seed"],
+                        c["offset"], requests=reqs)
+    out = torch.full((B,), SENTINEL, dtype=torch.int32, device="cuda")
+    sv.sample(dev_logits(c["logits"], "bf16"), dev(c["temperature"]), dev(c["seed"]), dev(c["offset"]),
+              top_k=dev(c["top_k"]), top_p=dev(c["top_p"]), min_p=dev(c["min_p"]), req_index=dev(reqs), out=out)
+    got = np_i(out)
+    ok = (got[reqs] == ref["tokens"][reqs]) | ref["flagged"][reqs]
+    assert np.all(ok), np.nonzero(~ok)
+    rest = np.setdiff1d(np.arange(B), reqs)
+    assert np.all(got[rest] == SENTINEL)
+
+
 def test_chain_reject_request_subset_and_determinism(sv):
     B, D, V = 9, 4, 3001
     c = fuzz_case(91, B, D, V, "f32")

@@ -13,6 +13,8 @@ Functions mirror the C entry points:
 * ``chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None)``
 * ``chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None)``:
   per-request verify lengths over packed target rows
+* ``sample(logits, temperature, seed, offset, top_k=None, top_p=None, min_p=None, req_index=None)``:
+  single-step sampling with the joint top-k/top-p filter and min-p
 * ``d2t_inverse(d2t, Vd, V)`` and ``d2t_expand(draft_probs, t2d)``: draft distributions over a
   reduced draft vocabulary placed in the target vocabulary
 * ``greedy_verify(target_logits, draft_ids, req_index=None, ...)``
@@ -45,6 +47,7 @@ SYMBOLS = (
     "specverify_greedy_verify",
     "specverify_gumbel_sample",
     "specverify_verify_fused",
+    "specverify_sample",
     "specverify_status_string",
     "specverify_last_error",
     "specverify_version",
@@ -80,9 +83,10 @@ def lib() -> ctypes.CDLL:
     L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.specverify_sample.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, i64, vp, vp]
     for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_chain_reject_ragged",
                  "specverify_d2t_inverse", "specverify_d2t_expand", "specverify_greedy_verify",
-                 "specverify_gumbel_sample", "specverify_verify_fused"):
+                 "specverify_gumbel_sample", "specverify_verify_fused", "specverify_sample"):
         getattr(L, name).restype = ctypes.c_int
     L.specverify_status_string.argtypes = [ctypes.c_int]
     L.specverify_status_string.restype = ctypes.c_char_p
@@ -320,6 +324,31 @@ def d2t_expand(draft_probs, t2d, out=None):
             raise ValueError(f"out must be {shape}")
     st = lib().specverify_d2t_expand(_ptr(draft_probs), _ptr(t2d), rows, Vd, V, _ptr(out), _stream_ptr(dev))
     _check("specverify_d2t_expand", st)
+    return out
+
+
+def sample(logits, temperature, seed, offset, top_k=None, top_p=None, min_p=None, req_index=None, out=None):
+    """Single-step sampling: one token per row of logits [B, V] (float32 or bfloat16); returns tokens [B] int32."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32, torch.bfloat16), None, 2)
+    dev = logits.device
+    B, V = logits.shape
+    _need(temperature, "temperature", (torch.float32,), dev, 1)
+    if top_k is not None:
+        _need(top_k, "top_k", (torch.int32,), dev, 1)
+    if top_p is not None:
+        _need(top_p, "top_p", (torch.float32,), dev, 1)
+    if min_p is not None:
+        _need(min_p, "min_p", (torch.float32,), dev, 1)
+    _u64(seed, "seed", B, dev)
+    _u64(offset, "offset", B, dev)
+    req_index, n_req = _req(req_index, B, dev)
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = lib().specverify_sample(_ptr(logits), _logit_dtype(logits), _ptr(temperature), _ptr(top_k), _ptr(top_p),
+                                 _ptr(min_p), _ptr(seed), _ptr(offset), B, V, _ptr(req_index), n_req, _ptr(out),
+                                 _stream_ptr(dev))
+    _check("specverify_sample", st)
     return out
 
 

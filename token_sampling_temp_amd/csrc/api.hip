@@ -299,6 +299,26 @@ int specverify_gumbel_sample(const void* target_logits, int dtype, const float* 
                                                  sampled_out, static_cast<hipStream_t>(stream)));
 }
 
+int specverify_sample(const void* logits, int dtype, const float* temperature, const int32_t* top_k,
+                      const float* top_p, const float* min_p, const uint64_t* seed, const uint64_t* offset, int64_t B,
+                      int64_t V, const int32_t* req_index, int64_t n_req, int32_t* tokens, void* stream) {
+    const char* fn = "specverify_sample";
+    SV_TRY(check_dtype(fn, dtype));
+    SV_TRY(check_sizes(fn, B, 1, V, req_index, n_req, 4));
+    if (V > sv::verify_fused_max_vocab())
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: V=%lld exceeds %lld", fn, (long long)V,
+                    (long long)sv::verify_fused_max_vocab());
+    if (n_req == 0) return SPECVERIFY_OK;
+    SV_REQUIRE(logits, "logits");
+    SV_REQUIRE(temperature, "temperature");
+    SV_REQUIRE(seed, "seed");
+    SV_REQUIRE(offset, "offset");
+    SV_REQUIRE(tokens, "tokens");
+    SV_TRY(check_device());
+    return launched(fn, sv::launch_sample(logits, dtype, temperature, top_k, top_p, min_p, seed, offset, B, V,
+                                          req_index, n_req, tokens, static_cast<hipStream_t>(stream)));
+}
+
 int specverify_verify_fused(const void* target_logits, int dtype, const float* temperature, const int32_t* top_k,
                             const float* top_p, const float* draft_probs, const int32_t* draft_ids,
                             const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D, int64_t V,

@@ -45,7 +45,8 @@ struct RowProb {
     int mode;
     float m, scale, inv;
     uint32_t kmin;
-    int64_t y;   // one-hot index
+    int64_t y;                  // one-hot index
+    double thr = -INFINITY;     // streamed rows: min-p threshold on v - m (single-step sampling)
 };
 
 __device__ __forceinline__ float raw_value(uint16_t h) { return bf16_to_float(h); }
@@ -64,7 +65,8 @@ __device__ __forceinline__ float row_prob(const RowProb rp, const RrShared& sh, 
         }
     }
     const float v = raw_value(raw);
-    return logit_key<T>(v) >= rp.kmin ? exp2f((v - rp.m) * rp.scale) * rp.inv : 0.0f;
+    return (logit_key<T>(v) >= rp.kmin && (double)v - (double)rp.m >= rp.thr) ? exp2f((v - rp.m) * rp.scale) * rp.inv
+                                                                               : 0.0f;
 }
 
 // Four consecutive logits starting at idx (a multiple of 4); entries past V
@@ -370,6 +372,88 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_kernel(
         accepted[b * N + tid] = t;
     }
     if (tid == 0) accept_len[b] = L;
+}
+
+// Single-step sampling ("tokenspeed sampling/backends/flashinfer.py",
+// sample: softmax(logits, T), then top_k_top_p_sampling_from_probs with the
+// joint filter order, per-request seed and offset; min-p as TensorRT-LLM's
+// fused sampler takes it).  One 1024-thread workgroup per request: a row
+// below the greedy temperature takes its argmax; otherwise the joint
+// statistics (register-resident for bf16 rows that fit, streamed otherwise)
+// and the verify's draw on row 0 with the uniform of word 0 of the request's
+// stream (the bonus draw of a verify without drafts).
+template <typename T, int NV>
+__global__ __launch_bounds__(kFvBlock) void sample_kernel(
+    const T* __restrict__ logits, const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
+    const float* __restrict__ top_p, const float* __restrict__ min_p, const uint64_t* __restrict__ seed,
+    const uint64_t* __restrict__ offset, int64_t B, int64_t V, const int32_t* __restrict__ req_index,
+    int32_t* __restrict__ tokens) {
+    __shared__ FusedShared sh;
+    const int64_t b = req_index ? (int64_t)req_index[blockIdx.x] : (int64_t)blockIdx.x;
+    if (b < 0 || b >= B) return;   // uniform over the workgroup
+    const int tid = threadIdx.x;
+    const T* row = logits + b * V;
+    const float Tm = temperature[b];
+    if ((double)Tm < kGreedyTemperature) {
+        const int64_t y = row_argmax<kFvBlock, false>(row, V, sh.rr.u.sm.am);
+        if (tid == 0) tokens[b] = (int32_t)y;
+        return;
+    }
+    if (tid == 0) sh.code[0] = uniform_code(philox_word(seed[b], offset[b], 0));
+    const int32_t k = top_k ? top_k[b] : 0;
+    const float tp = top_p ? top_p[b] : 1.0f;
+    const float mp = min_p ? min_p[b] : 0.0f;
+    RowProb rp{kProbStreamed, 0.0f, 0.0f, 0.0f, 0u, 0};
+    bool done = false;
+    if constexpr (NV > 0) {
+        u32x4 w[NV];
+        RrStats st;
+        if (rr_stats<NV, true>(sh.rr, reinterpret_cast<const uint16_t*>(row), V, Tm, k, tp, tid, w, st, mp)) {
+            rp = RowProb{st.table ? kProbTable : kProbRrExp, st.m, st.scale, st.inv, st.kmin, 0};
+            done = true;
+        }
+    }
+    if (!done) {
+        __syncthreads();
+        const JointStats js = streamed_stats_joint<T>(row, V, Tm, k, tp, mp, sh.rr.u.sm);
+        rp = RowProb{kProbStreamed, js.m, js.scale, js.inv, js.kmin, 0};
+        rp.thr = js.thr;
+    }
+    __syncthreads();
+    const double uf = (double)sh.code[0] * 0x1p-24;
+    int64_t y = fused_draw<T, false>(sh, rp, row, nullptr, V, uf);
+    if (y < 0) y = (int64_t)(((uint64_t)sh.code[0] * (uint64_t)V) >> 24);
+    if (tid == 0) tokens[b] = (int32_t)y;
+}
+
+hipError_t launch_sample(const void* logits, int dtype, const float* temperature, const int32_t* top_k,
+                         const float* top_p, const float* min_p, const uint64_t* seed, const uint64_t* offset,
+                         int64_t B, int64_t V, const int32_t* req_index, int64_t n_req, int32_t* tokens,
+                         hipStream_t stream) {
+    if (V > (int64_t)kFvMaxChunks * kFvChunk) return hipErrorInvalidValue;
+    if (dtype == kDtypeBF16) {
+        const uint16_t* lg = static_cast<const uint16_t*>(logits);
+        const int64_t nv = (V + kRrBlock * 8 - 1) / (kRrBlock * 8);
+        // the register-resident path needs every row 16-byte aligned
+        const bool rr = (V & 7) == 0 && (uintptr_t)lg % 16 == 0 && nv <= 20;
+#define SV_SK(NVV)                                                                                                   \
+    hipLaunchKernelGGL((sample_kernel<uint16_t, NVV>), dim3((unsigned)n_req), dim3(kFvBlock), 0, stream, lg,         \
+                       temperature, top_k, top_p, min_p, seed, offset, B, V, req_index, tokens)
+        if (!rr) SV_SK(0);
+        else if (nv <= 1) SV_SK(1);
+        else if (nv <= 2) SV_SK(2);
+        else if (nv <= 4) SV_SK(4);
+        else if (nv <= 8) SV_SK(8);
+        else if (nv <= 12) SV_SK(12);
+        else if (nv <= 16) SV_SK(16);
+        else SV_SK(20);
+#undef SV_SK
+    } else {
+        hipLaunchKernelGGL((sample_kernel<float, 0>), dim3((unsigned)n_req), dim3(kFvBlock), 0, stream,
+                           static_cast<const float*>(logits), temperature, top_k, top_p, min_p, seed, offset, B, V,
+                           req_index, tokens);
+    }
+    return hipGetLastError();
 }
 
 int64_t verify_fused_max_vocab() { return (int64_t)kFvMaxChunks * kFvChunk; }

@@ -36,6 +36,13 @@ hipError_t launch_d2t_inverse(const int64_t* d2t, int64_t Vd, int64_t V, int32_t
 hipError_t launch_d2t_expand(const float* draft_probs, const int32_t* t2d, int64_t rows, int64_t Vd, int64_t V,
                              float* out, hipStream_t stream);
 
+// Single-step sampling of one token per request from logits [B, V]
+// (V <= verify_fused_max_vocab()).
+hipError_t launch_sample(const void* logits, int dtype, const float* temperature, const int32_t* top_k,
+                         const float* top_p, const float* min_p, const uint64_t* seed, const uint64_t* offset,
+                         int64_t B, int64_t V, const int32_t* req_index, int64_t n_req, int32_t* tokens,
+                         hipStream_t stream);
+
 hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t npos, int64_t V,
                                  const float* temperature, const int32_t* top_k, const float* top_p,
                                  const int32_t* req_index, int64_t n_req, float* probs_out,

@@ -231,6 +231,51 @@ __device__ __forceinline__ StreamStats streamed_stats(const T* __restrict__ row,
     return StreamStats{m, scale, (float)(1.0 / S), kmin};
 }
 
+// Statistics of one row for single-step sampling's joint filter: top-k and
+// the top-p nucleus both judge the unfiltered row (the nucleus from the mass
+// of every key, so radix_mass_key runs over all keys), and min-p keeps
+// (v - m) >= thr = T ln(min(min_p, 1)) compared in double (thr = -inf when
+// min_p is not positive).  An element v then has probability
+// exp2f((v - m) * scale) * inv if its key is >= kmin and it passes min-p.
+struct JointStats {
+    float m, scale, inv;
+    uint32_t kmin;
+    double thr;
+};
+
+template <typename T>
+__device__ __forceinline__ JointStats streamed_stats_joint(const T* __restrict__ row, int64_t V, float Tm, int32_t k,
+                                                           float tp, float mp, SmShared& sh) {
+    float lm = -INFINITY;
+    row_foreach<kSmBlock, false>(row, V, [&](float v, int64_t) { lm = fmaxf(lm, v); });
+    const float m = block_reduce<kSmBlock>(lm, OpMaxF{}, -INFINITY, sh.red_f);
+    const float scale = kLog2e / Tm;
+
+    uint32_t kmin = 0;
+    if (k > 0 && (int64_t)k < V) kmin = radix_kth_key<T>(row, V, (uint32_t)k, sh);
+
+    if (tp < 1.0f) {
+        const int lg = V > 1 ? 64 - __clzll((unsigned long long)(V - 1)) : 0;
+        const int qshift = 62 - lg;
+        const double qscale = ldexp(1.0, qshift);
+        uint64_t part = 0;
+        row_foreach<kSmBlock, false>(row, V, [&](float v, int64_t) {
+            part += (uint64_t)__double2ull_rn((double)exp2f((v - m) * scale) * qscale);
+        });
+        const uint64_t s_fx = block_reduce<kSmBlock>(part, OpSumU64{}, (uint64_t)0, sh.red_u);
+        const uint32_t kp = radix_mass_key<T>(row, V, 0u, m, scale, qshift, (double)tp * (double)s_fx, sh);
+        kmin = kmin > kp ? kmin : kp;
+    }
+    const double thr = mp > 0.0f ? (double)Tm * log(mp < 1.0f ? (double)mp : 1.0) : -INFINITY;
+
+    double ps = 0.0;
+    row_foreach<kSmBlock, false>(row, V, [&](float v, int64_t) {
+        if (logit_key<T>(v) >= kmin && (double)v - (double)m >= thr) ps += (double)exp2f((v - m) * scale);
+    });
+    const double S = block_reduce<kSmBlock>(ps, OpSumD{}, 0.0, sh.red_d);
+    return JointStats{m, scale, (float)(1.0 / S), kmin, thr};
+}
+
 // One row streamed from global memory (every pass re-reads it).
 template <typename T>
 __device__ __forceinline__ void softmax_row_streamed(const T* __restrict__ row, float* __restrict__ orow, int64_t V,
@@ -654,9 +699,16 @@ struct RrStats {
 // 16-byte vector lies wholly inside or wholly past the end of the row; buffer
 // loads return zeros past the end) into w as keys, then selects and builds
 // the table.  Returns false if a histogram counter overflowed.
-template <int NV>
+//
+// JOINT (single-step sampling): top-k and the top-p nucleus both judge the
+// unfiltered row (the nucleus walk runs over every key), and min-p (mp > 0)
+// keeps the keys whose value v satisfies (v - m) >= T ln(min(mp, 1)) in
+// double, the smallest such key found by binary search (keys order like their
+// values); the kept key is the largest of the three thresholds.
+template <int NV, bool JOINT = false>
 __device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restrict__ row, int64_t V, float Tm,
-                                         int32_t k, float tp, int tid, u32x4 (&w)[NV], RrStats& st) {
+                                         int32_t k, float tp, int tid, u32x4 (&w)[NV], RrStats& st,
+                                         float mp = 0.0f) {
     const __amdgpu_buffer_rsrc_t rin = make_rsrc(row, (uint32_t)(V * 2));
     const int vfull = (int)(V / (kRrBlock * 8));   // vectors in range for every thread
     auto ebase = [&](int v) { return (v * kRrBlock + tid) * 8; };
@@ -730,7 +782,34 @@ __device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restric
     const int qs = 62 - lg;
     const bool direct = mkey - kmin < (uint32_t)kDirectSpan;
     double S;
-    if (tp < 1.0f && direct) {
+    if constexpr (JOINT) {
+        if (tp < 1.0f) {
+            const uint64_t total = rr_block_reduce(sh, tid, rr_total_mass(sh, tid, 0u, m, scale, qs), OpSumU64{});
+            if (tid < kWave) rr_topp_topdown(sh, tid, 0u, mkey, m, scale, qs, tp, total);
+            lds_barrier();
+            kmin = max(kmin, sh.sel_digit);
+        }
+        if (mp > 0.0f) {
+            const double thr = (double)Tm * log(mp < 1.0f ? (double)mp : 1.0);
+            uint32_t lo = 0, hi = mkey;   // the maximum's key always passes (thr <= 0)
+            while (lo < hi) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if ((double)key_to_float(mid) - (double)m >= thr) hi = mid;
+                else lo = mid + 1;
+            }
+            kmin = max(kmin, lo);
+        }
+        if (mkey - kmin < (uint32_t)kDirectSpan) {
+            if (tid < kWave) {
+                const double ws = rr_span_weight(sh, tid, kmin, mkey, m, scale);
+                if (tid == 0) sh.sel_above = __builtin_bit_cast(uint64_t, ws);
+            }
+            lds_barrier();
+            S = __builtin_bit_cast(double, sh.sel_above);
+        } else {
+            S = rr_block_reduce(sh, tid, rr_kept_weight(sh, tid, kmin, m, scale), OpSumD{});
+        }
+    } else if (tp < 1.0f && direct) {
         if (tid < kWave) rr_topp_direct(sh, tid, kmin, mkey, m, scale, qs, tp);
         lds_barrier();
         kmin = sh.sel_digit;

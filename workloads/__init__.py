@@ -18,5 +18,6 @@ from .synth import (  # noqa: F401
     make_config,
     make_d2t,
     make_ragged_config,
+    make_sample_config,
     fuzz_case,
 )

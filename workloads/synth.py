@@ -266,6 +266,26 @@ def make_ragged_config(replica: int = 0) -> dict:
     return out
 
 
+def make_sample_config(replica: int = 0, B: int = 1024, V: int = 129280) -> dict:
+    """Single-step sampling rows at the mixed workload's shape: bf16 logits
+    ~ N(0, 2.5) [B, V]; per row (data RNG) a quarter greedy (T = 0), the rest
+    T ~ U[0.5, 1.2] with top_k in {0, 20, 100}, top_p 1 or U[0.8, 0.95] and
+    min_p in {0, 0.05}; Philox seed_b = 6 * 2^32 + b."""
+    rng = data_rng(6, replica)
+    z = np.empty((B, V), np.uint16)
+    for b0 in range(0, B, 128):
+        blk = rng.standard_normal((min(128, B - b0), V), dtype=np.float32)
+        blk *= np.float32(2.5)
+        z[b0:b0 + blk.shape[0]] = f32_to_bf16_bits(blk)
+    T = rng.uniform(0.5, 1.2, B).astype(np.float32)
+    T[rng.random(B) < 0.25] = 0.0
+    top_k = rng.choice([0, 20, 100], B).astype(np.int32)
+    top_p = np.where(rng.random(B) < 0.5, rng.uniform(0.8, 0.95, B), 1.0).astype(np.float32)
+    min_p = np.where(rng.random(B) < 0.5, 0.05, 0.0).astype(np.float32)
+    return dict(dtype="bf16", logits=z, temperature=T, top_k=top_k, top_p=top_p, min_p=min_p,
+                seed=_seeds(6, B), offset=np.full(B, 4096 * replica, np.uint64))
+
+
 def make_d2t(seed: int, Vd: int, V: int, shuffled: bool = False) -> np.ndarray:
     """A one-to-one draft -> target offset table: draft id s maps to target id
     t_s = s + d2t[s] (mod V), the t_s a seeded sample of Vd distinct target
