@@ -165,8 +165,8 @@ def joint_filter_row(z: np.ndarray, temperature: float, top_k: int, top_p: float
     whose mass reaches top_p of the row's whole mass (ties at the threshold
     kept, active iff top_p < 1).  TensorRT-LLM interface.py passes per-request
     ``min_ps`` to its fused sampler; read plainly, min-p keeps p_v >= min_p *
-    p_max, i.e. (z_v - max z) >= T ln(min_p), compared on logits in float64
-    (off when min_p <= 0).
+    p_max, i.e. (z_v - max z) >= T ln(min(min_p, 1)), compared on logits in
+    float64 (off when min_p <= 0; min_p >= 1 keeps the maximal values).
     Returns (unnormalised kept weights exp((z - max) / T) float64 [V], flagged):
     ``flagged`` marks a row with a top-p threshold within TOPP_BAND of a mass
     boundary or a logit within MINP_BAND of the min-p threshold.
