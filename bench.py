@@ -15,9 +15,15 @@ call's rows.  Timing uses HIP events on the stream the kernels run on.
 
 Other workloads (``--workload``) exist for profiling: ``topk_topp_chain``
 (softmax_renorm -> chain_reject, B=64 D=3 V=32000 bf16), ``greedy`` (greedy
-verify, B=512 N=4 V=151936 bf16) and ``mixed`` (B=1024 D=7 V=129280 bf16: 256
+verify, B=512 N=4 V=151936 bf16), ``mixed`` (B=1024 D=7 V=129280 bf16: 256
 requests each greedy, temperature-only (Gumbel), top-k and top-p, every mode
-dispatched through req_index; per-call times are reported).
+dispatched through req_index; per-call times are reported), ``mixed_fused``
+(the same with the fused verify for the top-k/top-p requests),
+``large_vocab_target_only`` (the default inputs without draft
+probabilities), ``large_vocab_ragged`` (per-request verify lengths U{1..6}
+over packed rows; rows/s counts the verified rows), ``d2t_expand`` (1280
+draft rows of a 32000-entry draft vocabulary placed in V=128256) and
+``sample`` (single-step sampling of 1024 bf16 rows of V=129280).
 
 The CPU baseline is the numpy oracle timed on this host on the same inputs
 (whole batches repeated for --cpu-seconds), single threaded.
