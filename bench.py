@@ -21,7 +21,9 @@ dispatched through req_index; per-call times are reported), ``mixed_fused``
 (the same with the fused verify for the top-k/top-p requests),
 ``large_vocab_target_only`` (the default inputs without draft
 probabilities), ``large_vocab_ragged`` (per-request verify lengths U{1..6}
-over packed rows; rows/s counts the verified rows), ``d2t_expand`` (1280
+over packed rows; rows/s counts the verified rows), ``large_vocab_ragged_d2t``
+(the same with draft rows over a 32000-entry draft vocabulary read through
+the inverse d2t table), ``d2t_expand`` (1280
 draft rows of a 32000-entry draft vocabulary placed in V=128256) and
 ``sample`` (single-step sampling of 1024 bf16 rows of V=129280).
 
@@ -59,7 +61,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large_vocab_chain_reject",
-                    choices=["large_vocab_chain_reject", "large_vocab_target_only", "large_vocab_ragged", "d2t_expand",
+                    choices=["large_vocab_chain_reject", "large_vocab_target_only", "large_vocab_ragged",
+                             "large_vocab_ragged_d2t", "d2t_expand",
                              "sample", "topk_topp_chain", "greedy",
                              "mixed", "mixed_fused"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
@@ -311,6 +314,82 @@ class RaggedWorkload:
                 break
         return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
                 "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
+                          f"{el:.1f}s single-threaded numpy"}
+
+
+class RaggedD2tWorkload(RaggedWorkload):
+    """The ragged large-vocab inputs with a draft model over a 32000-entry draft vocabulary: the verify reads
+    the draft rows [256, 5, 32000] through the inverse d2t table, with no expanded rows."""
+    name = "large_vocab_ragged_d2t"
+    counters = "chain_reject_ragged_d2t_counters.txt"
+
+    def __init__(self, dev, replicas):
+        from workloads import make_ragged_d2t_config
+        t0 = time.time()
+        self.host = make_ragged_d2t_config()
+        log(f"generated inputs in {time.time() - t0:.1f}s")
+        h = self.host
+        self.B, self.D, self.V = h["B"], h["D"], h["V"]
+        self.Vd = h["draft_probs_d"].shape[-1]
+        self.R = replicas or 4
+        import token_sampling_temp_amd as sv
+        import torch
+        self.sv = sv
+        self.t2d = sv.d2t_inverse(_t(h["d2t"], dev), self.Vd, self.V)   # once per table
+        self.reps = []
+        for r in range(self.R):
+            off = np.full(self.B, 4096 * r, np.uint64)
+            self.reps.append(dict(q=_t(h["draft_probs_d"], dev), x=_t(h["draft_ids"], dev),
+                                  p=_t(h["target_rows"], dev), ind=_t(h["qo_indptr"], dev), seed=_t(h["seed"], dev),
+                                  off=_t(off, dev), off_host=off))
+        self.acc = torch.empty((self.B, self.D + 1), dtype=torch.int32, device=dev)
+        self.alen = torch.empty((self.B,), dtype=torch.int32, device=dev)
+        self.rows = int(h["verify_lens"].sum())
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        self.sv.chain_reject_ragged(r["q"], r["x"], r["p"], r["ind"], r["seed"], r["off"], out=(self.acc, self.alen),
+                                    t2d=self.t2d)
+
+    def algorithmic_bytes(self):
+        """As the ragged workload, with a draft row costing 4 Vd (read through the table) and the table
+        (4 V) read once per launch."""
+        per = []
+        self.L = []
+        d = self.host["verify_lens"] - 1
+        for i in range(self.R):
+            self.step(i)
+            L = self.alen.cpu().numpy().astype(np.int64)
+            tok = self.acc.cpu().numpy()
+            self.L.append(L)
+            D, V, Vd = self.D, self.V, self.Vd
+            at_d = tok[np.arange(self.B), np.minimum(L, D)]
+            rows = np.where(L < d, 4 * V + 4 * Vd, np.where((d < D) & (at_d == 0), 0, 4 * V))
+            probes = 3 * PROBE_GRANULE * np.minimum(L + 1, D)
+            per.append(int(rows.sum() + probes.sum() + self.B * (8 * D + 32) + 4 * V))
+        return float(np.mean(per))
+
+    def config(self):
+        c = super().config()
+        c["input"] = ("float32 packed target rows, per-request verify lengths U{1..6}, float32 draft rows over a "
+                      "32000-entry draft vocabulary read through the inverse d2t table")
+        return c
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, passes = 0, time.perf_counter(), 0
+        while True:
+            off = self.reps[passes % self.R]["off_host"]
+            q_full = oracle.d2t_expand(h["draft_probs_d"], h["d2t"], self.V)
+            oracle.chain_reject_ragged(q_full, h["draft_ids"], h["target_rows"], h["qo_indptr"], h["seed"], off)
+            rows += self.rows
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{passes} full batches of {self.B} requests (placement + ragged verify), "
                           f"{el:.1f}s single-threaded numpy"}
 
 
@@ -725,7 +804,8 @@ class MixedFusedWorkload(MixedWorkload):
         return self.bytes_by_call["verify_fused"]
 
 
-WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, DraftVocabWorkload,
+WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, RaggedD2tWorkload,
+                                 DraftVocabWorkload,
                                  SampleWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
                                  MixedFusedWorkload)}
 

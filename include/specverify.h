@@ -153,7 +153,13 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids,
  *
  * draft_probs     [B, D, V] float32 or NULL (point-mass drafts, as in
  *                 specverify_chain_reject); rows at positions >= len_b - 1 are
- *                 not read
+ *                 not read.  With t2d: [B, D, Vd], rows over a smaller draft
+ *                 vocabulary
+ * t2d, Vd         NULL, or the inverse table of specverify_d2t_inverse [V]
+ *                 int32 and the draft vocabulary size: target entry v of a
+ *                 draft row is draft_probs[..., t2d[v]] (0 where t2d[v] is
+ *                 outside [0, Vd)), exactly the row specverify_d2t_expand
+ *                 would write, without writing it; needs draft_probs
  * draft_ids       [B, D] int32; entries at positions >= len_b - 1 are not read
  * target_probs    [n_rows, V] float32, packed rows
  * qo_indptr       [B+1] int32, request b's rows are [qo_indptr[b], qo_indptr[b+1]),
@@ -171,11 +177,12 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids,
  * whose rows fall outside [0, n_rows) gets accept_length -1 and all tokens
  * -1; nothing of it is read.  Memory: the workspace of specverify_chain_reject.
  */
-int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* draft_ids,
-                                   const float* target_probs, const int32_t* qo_indptr, int64_t n_rows,
-                                   const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D,
-                                   int64_t V, const int32_t* req_index, int64_t n_req,
-                                   int32_t* accepted_tokens, int32_t* accept_length, void* stream);
+int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* t2d, int64_t Vd,
+                                   const int32_t* draft_ids, const float* target_probs,
+                                   const int32_t* qo_indptr, int64_t n_rows, const uint64_t* seed,
+                                   const uint64_t* offset, int64_t B, int64_t D, int64_t V,
+                                   const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
+                                   int32_t* accept_length, void* stream);
 
 /*
  * Draft -> target vocabulary placement of draft distributions.

@@ -121,17 +121,21 @@ def test_verify_fused_invalid_arguments():
 
 def test_chain_reject_ragged_invalid_arguments():
     L = sv.lib()
-    # (q, x, p, qo_indptr, n_rows, seed, offset, B, D, V, req_index, n_req, acc, alen, stream)
-    assert L.specverify_chain_reject_ragged(P, P, P, None, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    # (q, t2d, Vd, x, p, qo_indptr, n_rows, seed, offset, B, D, V, req_index, n_req, acc, alen, stream)
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, None, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
     assert "qo_indptr" in L.specverify_last_error().decode()
-    assert L.specverify_chain_reject_ragged(P, P, P, P, -1, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, P, -1, P, P, 4, 3, 10, None, 4, P, P, None) == 1
     assert "n_rows" in L.specverify_last_error().decode()
-    assert L.specverify_chain_reject_ragged(P, P, P, P, 8, P, P, 4, 17, 10, None, 4, P, P, None) == 1
-    assert L.specverify_chain_reject_ragged(P, None, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, P, 8, P, P, 4, 17, 10, None, 4, P, P, None) == 1
+    assert L.specverify_chain_reject_ragged(P, None, 0, None, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
     assert "draft_ids" in L.specverify_last_error().decode()
-    assert L.specverify_chain_reject_ragged(P, P, None, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
-    assert L.specverify_chain_reject_ragged(None, None, None, None, 0, None, None, 4, 3, 10, P, 0, None, None,
-                                            None) == 0
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, None, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_chain_reject_ragged(None, P, 5, P, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert "t2d needs draft_probs" in L.specverify_last_error().decode()
+    assert L.specverify_chain_reject_ragged(P, P, 0, P, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert "Vd=0" in L.specverify_last_error().decode()
+    assert L.specverify_chain_reject_ragged(None, None, 0, None, None, None, 0, None, None, 4, 3, 10, P, 0, None,
+                                            None, None) == 0
 
 
 def test_d2t_invalid_arguments():

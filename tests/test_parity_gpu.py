@@ -369,10 +369,12 @@ def test_d2t_expand(sv):
 
 
 def test_ragged_verify_with_reduced_draft_vocab(sv):
-    """The reduced-vocabulary drafter end to end: d2t placement, then the
-    ragged chain verify, against the oracle's placement and ragged verify."""
+    """The reduced-vocabulary drafter end to end: d2t placement then the
+    ragged chain verify, and the verify reading the draft rows through the
+    inverse table, against the oracle's placement and ragged verify; split
+    and one-workgroup rows, aligned and odd V."""
     from workloads import make_d2t
-    for B, D, Vd, V in ((6, 3, 300, 1000), (260, 4, 3200, 12288)):
+    for B, D, Vd, V in ((6, 3, 300, 1000), (260, 4, 3200, 12288), (5, 2, 333, 1001), (257, 3, 5000, 20001)):
         rng = np.random.default_rng(B + V)
         c = fuzz_case(1500 + B, B, D, V, "f32")
         d2t = make_d2t(B, Vd, V)
@@ -386,9 +388,14 @@ def test_ragged_verify_with_reduced_draft_vocab(sv):
         log(f"ragged verify with a reduced draft vocabulary: B={B} D={D} Vd={Vd} V={V}")
         q_full = oracle.d2t_expand(qd, d2t, V)
         ref = oracle.chain_reject_ragged(q_full, x, rows, ind, c["seed"], c["offset"])
-        qg = sv.d2t_expand(dev(qd), sv.d2t_inverse(dev(d2t), Vd, V))
+        t2d = sv.d2t_inverse(dev(d2t), Vd, V)
+        qg = sv.d2t_expand(dev(qd), t2d)
         acc, alen = sv.chain_reject_ragged(qg, dev(x), dev(rows), dev(ind), dev(c["seed"]), dev(c["offset"]))
-        assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, Vd, V))
+        assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, Vd, V, "expanded"))
+        # the same verify reading the draft rows through t2d, with nothing expanded
+        acc, alen = sv.chain_reject_ragged(dev(qd), dev(x), dev(rows), dev(ind), dev(c["seed"]), dev(c["offset"]),
+                                           t2d=t2d)
+        assert_chain_match(np_i(acc), np_i(alen), ref, range(B), (B, D, Vd, V, "through t2d"))
 
 
 def _sample_params(rng, B, V):
@@ -445,6 +452,24 @@ def test_sample_mixed_batch_and_subset(sv):
     assert np.all(ok), np.nonzero(~ok)
     rest = np.setdiff1d(np.arange(B), reqs)
     assert np.all(got[rest] == SENTINEL)
+
+
+def test_ragged_verify_reduced_vocab_large(sv):
+    """The large-vocab ragged workload with a 32000-entry draft vocabulary,
+    the draft rows read through the inverse table."""
+    from workloads import make_ragged_d2t_config
+    c = make_ragged_d2t_config()
+    B, D, V = c["B"], c["D"], c["V"]
+    Vd = c["draft_probs_d"].shape[-1]
+    log(f"ragged verify through t2d, large vocab: B={B} D={D} Vd={Vd} V={V}")
+    q_full = oracle.d2t_expand(c["draft_probs_d"], c["d2t"], V)
+    ref = oracle.chain_reject_ragged(q_full, c["draft_ids"], c["target_rows"], c["qo_indptr"], c["seed"],
+                                     c["offset"])
+    t2d = sv.d2t_inverse(dev(c["d2t"]), Vd, V)
+    acc, alen = sv.chain_reject_ragged(dev(c["draft_probs_d"]), dev(c["draft_ids"]), dev(c["target_rows"]),
+                                       dev(c["qo_indptr"]), dev(c["seed"]), dev(c["offset"]), t2d=t2d)
+    flagged = assert_chain_match(np_i(acc), np_i(alen), ref, range(B), "ragged through t2d")
+    log(f"mean accept length {np_i(alen).mean():.3f}, flagged {flagged}")
 
 
 def test_chain_reject_request_subset_and_determinism(sv):

@@ -77,7 +77,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     L.specverify_softmax_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp, vp]
     L.specverify_chain_reject.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
-    L.specverify_chain_reject_ragged.argtypes = [vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.specverify_chain_reject_ragged.argtypes = [vp, vp, i64, vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, i64, vp,
+                                                 vp, vp]
     L.specverify_d2t_inverse.argtypes = [vp, i64, i64, vp, vp]
     L.specverify_d2t_expand.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
@@ -254,20 +255,30 @@ def verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offse
     return acc, alen
 
 
-def chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None, out=None):
+def chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None, out=None,
+                        t2d=None):
     """Ragged chain rejection over packed target rows [n_rows, V]; request b owns rows
     [qo_indptr[b], qo_indptr[b+1]).  Returns (accepted_tokens [B, D+1] int32,
-    accept_length [B] int32); ``draft_probs`` None means point-mass drafts."""
+    accept_length [B] int32); ``draft_probs`` None means point-mass drafts.  With ``t2d``
+    (from ``d2t_inverse``) the draft rows are [B, D, Vd] over a smaller draft vocabulary."""
     torch = _torch()
     _need(target_probs, "target_probs", (torch.float32,), None, 2)
     dev = target_probs.device
     n_rows, V = target_probs.shape
     _need(draft_ids, "draft_ids", (torch.int32,), dev, 2)
     B, D = draft_ids.shape
+    Vd = V
+    if t2d is not None:
+        if draft_probs is None:
+            raise ValueError("t2d needs draft_probs")
+        _need(t2d, "t2d", (torch.int32,), dev, 1)
+        if t2d.shape[0] != V:
+            raise ValueError(f"t2d must have shape [{V}]")
+        Vd = int(draft_probs.shape[-1])
     if draft_probs is not None:
         _need(draft_probs, "draft_probs", (torch.float32,), dev, 3)
-        if tuple(draft_probs.shape) != (B, D, V):
-            raise ValueError(f"draft_probs must be [{B},{D},{V}]")
+        if tuple(draft_probs.shape) != (B, D, Vd):
+            raise ValueError(f"draft_probs must be [{B},{D},{Vd}]")
     _need(qo_indptr, "qo_indptr", (torch.int32,), dev, 1)
     if qo_indptr.shape[0] != B + 1:
         raise ValueError(f"qo_indptr must have shape [{B + 1}]")
@@ -280,8 +291,8 @@ def chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, o
     else:
         acc, alen = out
     st = lib().specverify_chain_reject_ragged(
-        _ptr(draft_probs), _ptr(draft_ids), _ptr(target_probs), _ptr(qo_indptr), n_rows, _ptr(seed), _ptr(offset),
-        B, D, V, _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
+        _ptr(draft_probs), _ptr(t2d), Vd, _ptr(draft_ids), _ptr(target_probs), _ptr(qo_indptr), n_rows, _ptr(seed),
+        _ptr(offset), B, D, V, _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
     _check("specverify_chain_reject_ragged", st)
     return acc, alen
 

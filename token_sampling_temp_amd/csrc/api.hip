@@ -190,18 +190,24 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids, 
     uint32_t* counter = nullptr;
     double* partial = nullptr;
     SV_TRY(chain_workspace(fn, static_cast<hipStream_t>(stream), n_req, V, &counter, &partial));
-    return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, nullptr, 0, seed, offset, B,
-                                                (int)D, V, req_index, n_req, accepted_tokens, accept_length,
-                                                counter, partial, static_cast<hipStream_t>(stream)));
+    return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, nullptr, 0, nullptr, V, seed,
+                                                offset, B, (int)D, V, req_index, n_req, accepted_tokens,
+                                                accept_length, counter, partial, static_cast<hipStream_t>(stream)));
 }
 
-int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
-                                   const int32_t* qo_indptr, int64_t n_rows, const uint64_t* seed,
-                                   const uint64_t* offset, int64_t B, int64_t D, int64_t V,
-                                   const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
+int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* t2d, int64_t Vd,
+                                   const int32_t* draft_ids, const float* target_probs, const int32_t* qo_indptr,
+                                   int64_t n_rows, const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D,
+                                   int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
                                    int32_t* accept_length, void* stream) {
     const char* fn = "specverify_chain_reject_ragged";
     SV_TRY(check_draft(fn, D));
+    if (t2d && !draft_probs)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: t2d needs draft_probs (a draft vocabulary of Vd entries)", fn);
+    if (t2d && (Vd < 1 || Vd > kMaxV))
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: Vd=%lld must be in [1, 2^31)", fn, (long long)Vd);
+    if (t2d && (long double)B * (long double)D * (long double)Vd * 4.0L > 4.0e18L)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: tensor size overflows", fn);
     SV_TRY(check_sizes(fn, B, D + 1, V, req_index, n_req, 4));
     if (n_rows < 0 || n_rows > 2147483647LL)
         return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: n_rows=%lld must be in [0, 2^31)", fn, (long long)n_rows);
@@ -219,9 +225,10 @@ int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* draf
     uint32_t* counter = nullptr;
     double* partial = nullptr;
     SV_TRY(chain_workspace(fn, static_cast<hipStream_t>(stream), n_req, V, &counter, &partial));
-    return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, qo_indptr, n_rows, seed,
-                                                offset, B, (int)D, V, req_index, n_req, accepted_tokens,
-                                                accept_length, counter, partial, static_cast<hipStream_t>(stream)));
+    return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, qo_indptr, n_rows, t2d,
+                                                t2d ? Vd : V, seed, offset, B, (int)D, V, req_index, n_req,
+                                                accepted_tokens, accept_length, counter, partial,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int specverify_d2t_inverse(const int64_t* d2t, int64_t Vd, int64_t V, int32_t* t2d, void* stream) {

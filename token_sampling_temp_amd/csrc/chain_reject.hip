@@ -94,6 +94,31 @@ __device__ __forceinline__ void load_run(const float* row, int64_t base, int64_t
     }
 }
 
+// The draft row's entries of a run, laid out as load_run's.  Without t2d
+// the row is indexed by target entry; with t2d (a draft row over a smaller
+// draft vocabulary of Vd entries) target entry v holds qr[t2d[v]], 0 where
+// t2d[v] is outside [0, Vd) or v >= V.  t2d is read with load_run's pattern
+// (16-byte loads when aligned), then the draft entries are gathered.
+template <int NSUB, bool NT>
+__device__ __forceinline__ void load_q_run(const float* qr, const int32_t* t2d, int64_t Vd, int64_t base, int64_t V,
+                                           bool aligned, float (&f)[NSUB][4]) {
+    if (!t2d) {
+        load_run<NSUB, NT>(qr, base, V, aligned, f);
+        return;
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    float tb[NSUB][4];
+    load_run<NSUB, false>(reinterpret_cast<const float*>(t2d), base, V, aligned, tb);
+#pragma unroll
+    for (int k = 0; k < NSUB; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t idx = base + (k * kWave + lane) * 4 + e;
+            const int32_t sidx = __float_as_int(tb[k][e]);
+            f[k][e] = (idx < V && sidx >= 0 && (int64_t)sidx < Vd) ? qr[sidx] : 0.0f;
+        }
+}
+
 // Search NSUB sub-tiles (64 lanes x 4 entries each; index order sub-tile,
 // lane, entry) starting at `base` for min{ j : run + sum_{<=j} r > T } over
 // positive entries.  Wave-uniform result; -1 if not found.  `lastpos`
@@ -102,12 +127,12 @@ __device__ __forceinline__ void load_run(const float* row, int64_t base, int64_t
 template <int NSUB>
 __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int64_t V, bool aligned,
                                int64_t base, double run, double T, bool force_last, int64_t& lastpos,
-                               double& total, int64_t xo = -1) {
+                               double& total, int64_t xo = -1, const int32_t* t2d = nullptr, int64_t Vd = 0) {
     const int lane = threadIdx.x & (kWave - 1);
     float pf[NSUB][4], qf[NSUB][4];
     load_run<NSUB, false>(pr, base, V, aligned, pf);
     if (resid) {
-        load_run<NSUB, false>(qr, base, V, aligned, qf);
+        load_q_run<NSUB, false>(qr, t2d, Vd, base, V, aligned, qf);
     } else {
 #pragma unroll
         for (int k = 0; k < NSUB; ++k)
@@ -331,9 +356,10 @@ template <int kMode>
 __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const float* __restrict__ q, const int32_t* __restrict__ x, const float* __restrict__ p,
     const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
-    const int32_t* __restrict__ qo_indptr, int64_t n_rows, const int32_t* __restrict__ req_index, int64_t n_req,
-    int C, int R, int64_t per_xcd, int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len,
-    double* __restrict__ partial, uint32_t* __restrict__ counter) {
+    const int32_t* __restrict__ qo_indptr, int64_t n_rows, const int32_t* __restrict__ t2d, int64_t Vd,
+    const int32_t* __restrict__ req_index, int64_t n_req, int C, int R, int64_t per_xcd,
+    int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len, double* __restrict__ partial,
+    uint32_t* __restrict__ counter) {
     __shared__ ChainShared sh;
     // XCD-aware mapping: workgroups are dispatched round-robin over the 8 XCDs,
     // so consecutive virtual ids (one request's segments) share an XCD's L2.
@@ -385,7 +411,16 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
             const bool inr = tid < D && xi >= 0 && (int64_t)xi < V;
             const int64_t xc = inr ? (int64_t)xi : 0;
             const float a = p[(base + (ic < d ? ic : d)) * V + xc];
-            const float cq = (kMode == kDraftProbs && ic < d) ? q[(b * D + ic) * V + xc] : 1.0f;
+            float cq = 1.0f;
+            if (kMode == kDraftProbs && ic < d) {
+                if (t2d) {
+                    // draft row over the draft vocabulary: the id's entry through t2d
+                    const int32_t sx = inr ? t2d[xc] : -1;
+                    cq = (sx >= 0 && (int64_t)sx < Vd) ? q[(b * D + ic) * Vd + sx] : 0.0f;
+                } else {
+                    cq = q[(b * D + ic) * V + xc];
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
             w = philox_word(read_lane(so, 0), read_lane(so, 1), (uint64_t)tid);
             ok = (inr && (double)uniform_of(w) * (double)cq < (double)a) || (tid > d && tid < D);
@@ -422,8 +457,10 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const bool point = (kMode == kPointDraft && L < d) || (L == d && d < D);
     const int64_t xo = point ? (L < d ? (int64_t)sh.xL : 0) : -1;
     const float* pr = p + (base + L) * V;
-    const float* qr = resid ? q + (b * D + L) * V : nullptr;
-    const bool aligned = ((uintptr_t)pr % 16 == 0) && (!resid || (uintptr_t)qr % 16 == 0);
+    // draft rows hold V entries, or Vd (read through t2d) for a smaller draft vocabulary
+    const float* qr = resid ? q + (b * D + L) * (t2d ? Vd : V) : nullptr;
+    const bool aligned = ((uintptr_t)pr % 16 == 0) &&
+                         (!resid || (t2d ? (uintptr_t)t2d % 16 == 0 : (uintptr_t)qr % 16 == 0));
     const int64_t nchunks = (V + kChunk - 1) / kChunk;
 
     // ---- 2. segment pass.  Wave w owns chunks chunk0 + 4r + w, r < R (1024
@@ -431,7 +468,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     // keeps round r's chunk sum.
     const int64_t chunk0 = (int64_t)c * R * kChainWaves;
     double mine = 0.0;
-    if (aligned && (V & 3) == 0 && V < ((int64_t)1 << 29)) {
+    if (aligned && (V & 3) == 0 && V < ((int64_t)1 << 29) && !(resid && t2d)) {
         if (resid) mine = stream_chunks_fast<true, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
         else if (point) mine = stream_chunks_fast<false, SV_CHAIN_DEPTH, true>(pr, qr, V, chunk0, R, xo);
         else mine = stream_chunks_fast<false, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
@@ -441,7 +478,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
             const int64_t ch = chunk0 + (int64_t)r * kChainWaves + wid;
             if (ch < nchunks) {
                 load_run<4, SV_CHAIN_NT != 0>(pr, ch * kChunk, V, aligned, pf);
-                if (resid) load_run<4, SV_CHAIN_NT != 0>(qr, ch * kChunk, V, aligned, qf);
+                if (resid) load_q_run<4, SV_CHAIN_NT != 0>(qr, t2d, Vd, ch * kChunk, V, aligned, qf);
             }
         };
         auto sum_chunk = [&](int r, const float (&pf)[4][4], const float (&qf)[4][4]) {
@@ -523,7 +560,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
             int64_t lastpos;
             double tot;
             y = wave_search<4>(pr, qr, resid, V, aligned, (int64_t)cstar * kChunk, base, uf * R_tot,
-                               force_last != 0, lastpos, tot, xo);
+                               force_last != 0, lastpos, tot, xo, t2d, Vd);
             if (y < 0) y = lastpos;
         }
         if (lane == 0) sh.y = y;
@@ -562,7 +599,8 @@ static void chain_split(int64_t n_req, int64_t V, int& C, int& R) {
 }
 
 hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
-                               const int32_t* qo_indptr, int64_t n_rows, const uint64_t* seed,
+                               const int32_t* qo_indptr, int64_t n_rows, const int32_t* t2d, int64_t Vd,
+                               const uint64_t* seed,
                                const uint64_t* offset, int64_t B, int D, int64_t V, const int32_t* req_index,
                                int64_t n_req, int32_t* accepted, int32_t* accept_len, uint32_t* counter,
                                double* partial, hipStream_t stream) {
@@ -575,8 +613,8 @@ hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_id
     auto* kernel = D == 0 ? chain_reject_kernel<kNoDraft>
                           : (draft_probs ? chain_reject_kernel<kDraftProbs> : chain_reject_kernel<kPointDraft>);
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kChainBlock), 0, stream, draft_probs, draft_ids,
-                       target_probs, seed, offset, B, D, V, qo_indptr, n_rows, req_index, n_req, C, R, per_xcd,
-                       accepted, accept_len, partial, counter);
+                       target_probs, seed, offset, B, D, V, qo_indptr, n_rows, t2d, Vd, req_index, n_req, C, R,
+                       per_xcd, accepted, accept_len, partial, counter);
     return hipGetLastError();
 }
 

@@ -21,9 +21,12 @@ hipError_t launch_greedy_verify(const void* logits, int dtype, const int32_t* dr
 // doubles of partial sums.
 int64_t chain_partials_per_request(int64_t V);
 // qo_indptr NULL: dense target rows [B, D+1, V]; else packed rows [n_rows, V],
-// request b owning rows [qo_indptr[b], qo_indptr[b+1]).
+// request b owning rows [qo_indptr[b], qo_indptr[b+1]).  t2d NULL: draft rows
+// [B, D, V]; else [B, D, Vd] over a smaller draft vocabulary, target entry v
+// reading draft entry t2d[v].
 hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
-                               const int32_t* qo_indptr, int64_t n_rows, const uint64_t* seed,
+                               const int32_t* qo_indptr, int64_t n_rows, const int32_t* t2d, int64_t Vd,
+                               const uint64_t* seed,
                                const uint64_t* offset, int64_t B, int D, int64_t V, const int32_t* req_index,
                                int64_t n_req, int32_t* accepted, int32_t* accept_len, uint32_t* counter,
                                double* partial, hipStream_t stream);

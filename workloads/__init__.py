@@ -18,6 +18,7 @@ from .synth import (  # noqa: F401
     make_config,
     make_d2t,
     make_ragged_config,
+    make_ragged_d2t_config,
     make_sample_config,
     fuzz_case,
 )

@@ -266,6 +266,25 @@ def make_ragged_config(replica: int = 0) -> dict:
     return out
 
 
+def make_ragged_d2t_config(replica: int = 0, Vd: int = 32000) -> dict:
+    """The ragged large-vocab inputs with a draft model over a Vd-entry draft
+    vocabulary: an ascending d2t table (``make_d2t``), draft rows = the
+    config's draft rows at the mapped target ids, renormalised
+    (``draft_probs_d`` [B, D, Vd]), and draft ids drawn from those rows (data
+    RNG) and given as target ids."""
+    out = make_ragged_config(replica)
+    V = out["V"]
+    d2t = make_d2t(0, Vd, V)
+    tgt = (np.arange(Vd, dtype=np.int64) + d2t) % V
+    qd = out["draft_probs"][:, :, tgt].astype(np.float64)
+    qd /= qd.sum(axis=-1, keepdims=True)
+    rng = data_rng(31, replica)
+    out["d2t"] = d2t
+    out["draft_probs_d"] = qd.astype(np.float32)
+    out["draft_ids"] = tgt[_draw_from_rows(rng, qd)].astype(np.int32)
+    return out
+
+
 def make_sample_config(replica: int = 0, B: int = 1024, V: int = 129280) -> dict:
     """Single-step sampling rows at the mixed workload's shape: bf16 logits
     ~ N(0, 2.5) [B, V]; per row (data RNG) a quarter greedy (T = 0), the rest
