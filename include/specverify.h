@@ -32,9 +32,10 @@
  * - stream is a hipStream_t passed as void*; NULL is the default stream.
  *   Calls are asynchronous; nothing is read back to the host.  The library
  *   never synchronises.  specverify_softmax_renorm, specverify_greedy_verify,
- *   specverify_gumbel_sample and specverify_verify_fused use no device memory
- *   besides their arguments; specverify_chain_reject keeps a library-owned
- *   workspace (see there).
+ *   specverify_gumbel_sample, specverify_verify_fused, specverify_sample,
+ *   specverify_d2t_inverse and specverify_d2t_expand use no device memory
+ *   besides their arguments; specverify_chain_reject and
+ *   specverify_chain_reject_ragged keep a library-owned workspace (see there).
  * - Host-side validation runs before any HIP call.  Return codes:
  *   SPECVERIFY_OK, SPECVERIFY_INVALID_ARGUMENT (nothing launched),
  *   SPECVERIFY_UNSUPPORTED (current device is not gfx950),
