@@ -169,8 +169,10 @@ class ChainWorkload:
 
     def extra(self):
         L = np.concatenate(self.L)
+        # realised acceptance rate at position i: requests accepting i, among those that reached i
+        alpha = [round(float(np.mean(L[L >= i] > i)), 4) for i in range(self.D) if np.any(L >= i)]
         return {"mean_accept_length": round(float(L.mean()), 4),
-                "frac_all_accepted": round(float(np.mean(L == self.D)), 4)}
+                "frac_all_accepted": round(float(np.mean(L == self.D)), 4), "alpha_per_position": alpha}
 
     def config(self):
         return {"workload": self.name, "batch": self.B, "draft_tokens": self.D, "vocab": self.V,
@@ -810,6 +812,27 @@ WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorklo
                                  MixedFusedWorkload)}
 
 
+def stock_reduction_read(dev):
+    """Read bandwidth of a stock framework reduction on this GPU (torch's sum over 1 GiB of float32, four
+    buffers rotating): a reference point beside the roofline, not a peak and not a library kernel."""
+    import torch
+    bufs = [torch.ones(1 << 28, dtype=torch.float32, device=dev) for _ in range(4)]
+    for b in bufs:
+        b.sum()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    s.record()
+    for i in range(n):
+        bufs[i % 4].sum()
+    e.record()
+    torch.cuda.synchronize()
+    gbs = (4 << 28) * n / (s.elapsed_time(e) * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def per_call_times(wl, steps):
     """Average time of each call type of a multi-call step (each timed alone)."""
     import torch
@@ -899,6 +922,9 @@ def main():
             us = dom["us"]
             out["roofline"]["achieved"] = alg_bytes / (us * 1e-6) / 1e9
             out["roofline"]["frac"] = out["roofline"]["achieved"] / PEAK_HBM_GBS
+    sread = stock_reduction_read(dev)
+    out["roofline"]["torch_sum_read_GBps"] = sread
+    out["roofline"]["achieved_vs_torch_sum_read"] = out["roofline"]["achieved"] / sread
     out.update(wl.extra())
     print(json.dumps(out), flush=True)
 
