@@ -37,9 +37,9 @@ __global__ __launch_bounds__(kD2tBlock) void d2t_scatter_kernel(const int64_t* _
 }
 
 // One workgroup per row (grid-stride over rows): out[t] = q[t2d[t]], 0 where
-// t2d[t] is outside [0, Vd).  Rows whose output and the table are 16-byte aligned (V a
-// multiple of 4) take 4 entries at a time with 16-byte loads of the table
-// and 16-byte stores; others go entry by entry.
+// t2d[t] is outside [0, Vd).  Rows whose output and the table are 16-byte
+// aligned (V a multiple of 4) take 4 entries at a time with 16-byte loads of
+// the table and 16-byte stores; others go entry by entry.
 __global__ __launch_bounds__(kD2tBlock) void d2t_expand_kernel(const float* __restrict__ q,
                                                                const int32_t* __restrict__ t2d, int64_t rows,
                                                                int64_t Vd, int64_t V, float* __restrict__ out) {
