@@ -257,26 +257,35 @@ __device__ __forceinline__ double read_partial(double* src) {
 }
 
 // Segment pass for rows that are 16-byte aligned with V a multiple of 4 (and
-// V < 2^29, so every offset fits 32 bits).  Rounds whose four chunks lie
-// wholly inside the row stream with plain 16-byte loads and DEPTH rounds in
-// flight (consume a slot, refill it); the remaining rounds use buffer loads
-// with the row as the range, so chunks past the end read as zeros.  Returns,
-// on lane r, the sum of round r's chunk of this wave.
+// V < 2^29, so every offset fits 32 bits).  Every round is a buffer load with
+// the workgroup's segment of the row as the range, so chunks past the end of
+// the segment (the row's ragged last chunk, rounds that pad R to a multiple
+// of DEPTH) read as zeros without a separate tail loop; DEPTH rounds are in
+// flight from the first round to the last (consume a slot, refill it).
+// Returns, on lane r, the sum of round r's chunk of this wave.
 template <bool RESID, int DEPTH, bool ONEHOT = false>
 __device__ __forceinline__ double stream_chunks_fast(const float* pr, const float* qr, int64_t V, int64_t chunk0,
                                                      int R, int64_t xo = -1) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    constexpr bool kNT = SV_CHAIN_NT != 0;
+    constexpr int kAux = SV_CHAIN_NT ? 2 : 0;   // non-temporal
+    const int64_t s0 = chunk0 * kChunk;
+    int64_t s1 = (chunk0 + (int64_t)R * kChainWaves) * kChunk;
+    s1 = s1 < V ? s1 : V;
+    const uint32_t nbytes = (uint32_t)((s1 - s0) * 4);
+    const __amdgpu_buffer_rsrc_t rsp = make_rsrc(pr + s0, nbytes);
+    const __amdgpu_buffer_rsrc_t rsq = make_rsrc((RESID ? qr : pr) + s0, nbytes);
     const int64_t lane_off = (int64_t)wid * kChunk + lane * 4;   // floats
+    const uint32_t vo = (uint32_t)(lane_off * 4);
     u32x4 pv[DEPTH][4], qv[DEPTH][4];
     auto ld = [&](int slot, int r) {
-        const float* pp = pr + (chunk0 + (int64_t)r * kChainWaves) * kChunk + lane_off;
+        const uint32_t so = (uint32_t)r * (uint32_t)(kChainWaves * kChunk * 4);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pv[slot][k] = load_vec<kNT>(pp + k * kWave * 4, 0);
-        if constexpr (RESID) {
-            const float* qq = qr + (chunk0 + (int64_t)r * kChainWaves) * kChunk + lane_off;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) qv[slot][k] = load_vec<kNT>(qq + k * kWave * 4, 0);
+        for (int k = 0; k < 4; ++k) {
+            pv[slot][k] =
+                __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsp, vo + k * kWave * 16, so, kAux));
+            if constexpr (RESID)
+                qv[slot][k] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsq, vo + k * kWave * 16, so, kAux));
         }
     };
     double mine = 0.0;
@@ -305,46 +314,23 @@ __device__ __forceinline__ double stream_chunks_fast(const float* pr, const floa
         acc = wave_allreduce(acc, OpSumD{});
         if (lane == r) mine = acc;
     };
-    // rounds [0, rp) are wholly in range and a multiple of DEPTH
-    const int64_t nfull = V / kChunk;
-    int64_t rf = (nfull - chunk0) / kChainWaves;
-    rf = rf < 0 ? 0 : (rf > R ? R : rf);
-    const int rp = (int)(rf - rf % DEPTH);
-    if (rp > 0) {
+    // rounds [R, Rp) are past the segment and read zeros; their sums land on
+    // lanes that are never published (R <= 64)
+    const int Rp = (R + DEPTH - 1) / DEPTH * DEPTH;
 #pragma unroll
-        for (int j = 0; j < DEPTH; ++j) ld(j, j);
-        int r0 = 0;
-        for (; r0 + DEPTH < rp; r0 += DEPTH) {
+    for (int j = 0; j < DEPTH; ++j) ld(j, j);
+    int r0 = 0;
+    for (; r0 + DEPTH < Rp; r0 += DEPTH) {
 #pragma unroll
-            for (int j = 0; j < DEPTH; ++j) {
-                __builtin_amdgcn_sched_barrier(0);
-                sum(pv[j], qv[j], r0 + j);
-                __builtin_amdgcn_sched_barrier(0);
-                ld(j, r0 + j + DEPTH);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < DEPTH; ++j) sum(pv[j], qv[j], r0 + j);
-    }
-    // remaining rounds: range-checked buffer loads
-    if (rp < R) {
-        constexpr int kAux = SV_CHAIN_NT ? 2 : 0;   // non-temporal
-        const __amdgpu_buffer_rsrc_t rsp = make_rsrc(pr, (uint32_t)(V * 4));
-        const __amdgpu_buffer_rsrc_t rsq = make_rsrc(RESID ? qr : pr, (uint32_t)(V * 4));
-        const uint32_t vo = (uint32_t)(lane_off * 4);
-        for (int r = rp; r < R; ++r) {
-            const uint32_t so = (uint32_t)((chunk0 + (int64_t)r * kChainWaves) * kChunk * 4);
-            u32x4 p4[4], q4[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                p4[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsp, vo + k * kWave * 16, so, kAux));
-                q4[k] = RESID ? __builtin_bit_cast(
-                                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsq, vo + k * kWave * 16, so, kAux))
-                              : u32x4{0u, 0u, 0u, 0u};
-            }
-            sum(p4, q4, r);
+        for (int j = 0; j < DEPTH; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            sum(pv[j], qv[j], r0 + j);
+            __builtin_amdgcn_sched_barrier(0);
+            ld(j, r0 + j + DEPTH);
         }
     }
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) sum(pv[j], qv[j], r0 + j);
     return mine;
 }
 
@@ -396,6 +382,8 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     // ---- 1. probe (wave 0): lane i < D tests position i, lane D draws u_f.
     // The loads at the draft ids are issued before the Philox rounds, so the
     // rounds overlap their round trip; the first reject comes from a ballot.
+    // Lane i keeps draft id i for the output (written by the same lanes).
+    int32_t xkeep = 0;
     if (tid <= D) {
         uint32_t w;
         bool ok = false;
@@ -408,6 +396,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
             const int ic = tid < D ? tid : D - 1;
             // positions from d on draft token 0 as a point mass; only row d is read
             const int32_t xi = ic < d ? x[b * D + ic] : 0;
+            xkeep = xi;
             const bool inr = tid < D && xi >= 0 && (int64_t)xi < V;
             const int64_t xc = inr ? (int64_t)xi : 0;
             const float a = p[(base + (ic < d ? ic : d)) * V + xc];
@@ -445,7 +434,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
         // a ragged request accepted token 0 at its own last position: its
         // emitted tokens are the d drafts and 0, with no row to stream
         if (c == 0) {
-            if (tid < N) accepted[b * N + tid] = tid < d ? x[b * D + tid] : (tid == d ? 0 : -1);
+            if (tid < N) accepted[b * N + tid] = tid < d ? xkeep : (tid == d ? 0 : -1);
             if (tid == 0) accept_len[b] = d;
         }
         return;
@@ -571,7 +560,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     if (y < 0) y = (int64_t)(((uint64_t)sh.code * (uint64_t)V) >> 24);
     if (tid < N) {
         int32_t t;
-        if (tid < L) t = x[b * D + tid];
+        if (tid < L) t = xkeep;
         else t = (tid == L) ? (int32_t)y : -1;
         accepted[b * N + tid] = t;
     }
