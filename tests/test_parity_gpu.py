@@ -197,9 +197,14 @@ def test_chain_reject_large_batches(sv):
     sums published, last workgroup locates) and with one workgroup per
     request: a ragged last chunk, up to 1024 requests, all-bonus and
     all-residual batches, degenerate rows, a row of 293 chunks, and a
-    request subset with skipped and repeated indices."""
+    request subset with skipped and repeated indices.  (64, 3, 49148) and
+    (40, 5, 60000) split rows into segments of three 4096-entry rounds: the
+    load pipeline pads a segment to an even number of rounds, and the padding
+    round lies in the next segment, so it must read zeros, not that
+    segment's entries."""
     cases = ((64, 5, 65536, None), (300, 3, 16424, None), (1024, 3, 4096, None), (130, 4, 32768, "zeros"),
              (110, 2, 40000, "equal"), (140, 2, 30000, "disjoint"), (70, 7, 60000, None), (160, 0, 65536, None),
+             (64, 3, 49148, None), (40, 5, 60000, None),
              # one workgroup per request: no drafts, all accepted, a row of 293 chunks
              (300, 0, 8192, None), (270, 2, 8000, "equal"), (256, 1, 300000, None))
     flagged = 0
@@ -243,7 +248,8 @@ def test_chain_reject_target_only(sv):
     torch = __import__("torch")
     flagged = 0
     cases = [(6, 3, V, sp, 0) for V in (1, 7, 1000, 4097, 32000) for sp in (None, "invalid_ids", "onehot")]
-    cases += [(6, 4, 3001, "zeros", 0), (5, 3, 1003, None, 1), (300, 5, 20000, None, 0), (260, 2, 4096, "onehot", 0)]
+    cases += [(6, 4, 3001, "zeros", 0), (5, 3, 1003, None, 1), (300, 5, 20000, None, 0), (260, 2, 4096, "onehot", 0),
+              (40, 5, 60000, None, 0), (64, 3, 49148, "invalid_ids", 0)]
     for i, (B, D, V, sp, shift) in enumerate(cases):
         c = fuzz_case(1100 + i, B, D, V, "f32", special=sp)
         if sp is None and i % 2 == 0:
