@@ -25,6 +25,10 @@
 // Without draft distributions (target-only verify) each draft is a point mass
 // at its id: the probe takes q(x) = 1 and the residual pass streams p_L alone,
 // the rejected id weighing max(0, p - 1).
+// Draft rows over a smaller draft vocabulary (read through the inverse table
+// t2d) are copied whole into LDS when they fit (a separate instantiation with
+// dynamic LDS); the residual pass then streams p_L and t2d and looks the draft
+// entries up in LDS instead of gathering them from global memory.
 #include "sv_draw.hpp"
 #include "sv_launch.hpp"
 
@@ -47,6 +51,9 @@ constexpr int kChainBlock = SV_CHAIN_BLOCK;
 constexpr int kChainWaves = kChainBlock / kWave;
 constexpr int64_t kChunk = 1024;   // entries per wave-round; one partial sum each
 constexpr int kFallbackChunks = 512;
+// dynamic LDS for a staged draft row: the 160 KB of a gfx950 CU less the
+// static ChainShared and a margin
+constexpr int64_t kMaxStagedBytes = 150 * 1024;
 
 struct ChainShared {
     double chunk[kFallbackChunks];
@@ -263,17 +270,25 @@ __device__ __forceinline__ double read_partial(double* src) {
 // of DEPTH) read as zeros without a separate tail loop; DEPTH rounds are in
 // flight from the first round to the last (consume a slot, refill it).
 // Returns, on lane r, the sum of round r's chunk of this wave.
-template <bool RESID, int DEPTH, bool ONEHOT = false>
+//
+// T2D: the draft row lies in LDS (qlds, Vd entries) and the second stream is
+// the inverse table t2d (same offsets as the target row; read with temporal
+// loads, since every request reads the same table): target entry v weighs
+// max(0, p[v] - qlds[t2d[v]]), with q = 0 where t2d[v] is outside [0, Vd).
+template <bool RESID, int DEPTH, bool ONEHOT = false, bool T2D = false>
 __device__ __forceinline__ double stream_chunks_fast(const float* pr, const float* qr, int64_t V, int64_t chunk0,
-                                                     int R, int64_t xo = -1) {
+                                                     int R, int64_t xo = -1, const int32_t* t2d = nullptr,
+                                                     uint32_t Vd = 0, const float* qlds = nullptr) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     constexpr int kAux = SV_CHAIN_NT ? 2 : 0;   // non-temporal
+    constexpr int kAuxQ = T2D ? 0 : kAux;
     const int64_t s0 = chunk0 * kChunk;
     int64_t s1 = (chunk0 + (int64_t)R * kChainWaves) * kChunk;
     s1 = s1 < V ? s1 : V;
     const uint32_t nbytes = (uint32_t)((s1 - s0) * 4);
     const __amdgpu_buffer_rsrc_t rsp = make_rsrc(pr + s0, nbytes);
-    const __amdgpu_buffer_rsrc_t rsq = make_rsrc((RESID ? qr : pr) + s0, nbytes);
+    const __amdgpu_buffer_rsrc_t rsq =
+        T2D ? make_rsrc(t2d + s0, nbytes) : make_rsrc((RESID ? qr : pr) + s0, nbytes);
     const int64_t lane_off = (int64_t)wid * kChunk + lane * 4;   // floats
     const uint32_t vo = (uint32_t)(lane_off * 4);
     u32x4 pv[DEPTH][4], qv[DEPTH][4];
@@ -285,7 +300,7 @@ __device__ __forceinline__ double stream_chunks_fast(const float* pr, const floa
                 __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsp, vo + k * kWave * 16, so, kAux));
             if constexpr (RESID)
                 qv[slot][k] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsq, vo + k * kWave * 16, so, kAux));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsq, vo + k * kWave * 16, so, kAuxQ));
         }
     };
     double mine = 0.0;
@@ -295,7 +310,12 @@ __device__ __forceinline__ double stream_chunks_fast(const float* pr, const floa
         for (int k = 0; k < 4; ++k) {
             float pf[4], qf[4] = {0.f, 0.f, 0.f, 0.f};
             unpack(p4[k], pf);
-            if constexpr (RESID) unpack(q4[k], qf);
+            if constexpr (RESID && T2D) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qf[e] = q4[k][e] < Vd ? qlds[q4[k][e]] : 0.0f;
+            } else if constexpr (RESID) {
+                unpack(q4[k], qf);
+            }
             double rr[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) rr[e] = rval(pf[e], qf[e], RESID);
@@ -334,19 +354,63 @@ __device__ __forceinline__ double stream_chunks_fast(const float* pr, const floa
     return mine;
 }
 
+// Copy n floats from global memory to LDS, U loads in flight per thread:
+// 16-byte loads when the source is 16-byte aligned and n a multiple of 4.
+template <int U>
+__device__ __forceinline__ void stage_row(const float* __restrict__ src, int64_t n, float* dst) {
+    const int tid = threadIdx.x;
+    if ((uintptr_t)src % 16 == 0 && (n & 3) == 0) {
+        const int64_t n4 = n / 4;
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+        u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+        for (int64_t i0 = 0; i0 < n4; i0 += (int64_t)U * kChainBlock) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * kChainBlock + tid;
+                v[u] = i < n4 ? s4[i] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * kChainBlock + tid;
+                if (i < n4) d4[i] = v[u];
+            }
+        }
+    } else {
+        for (int64_t i0 = 0; i0 < n; i0 += (int64_t)U * kChainBlock) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * kChainBlock + tid;
+                v[u] = i < n ? src[i] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * kChainBlock + tid;
+                if (i < n) dst[i] = v[u];
+            }
+        }
+    }
+}
+
 // Draft mode: kNoDraft (D = 0), kDraftProbs (draft distributions given) or
 // kPointDraft (no draft distributions: each draft is a point mass at its id,
 // so q(x) = 1 and the residual is p with the rejected id weighing max(0, p - 1)).
+// kStaged: a separate instantiation for draft rows over a draft vocabulary
+// that fits LDS, so the other kernels' code is untouched by it.
 constexpr int kNoDraft = 0, kDraftProbs = 1, kPointDraft = 2;
-template <int kMode>
+template <int kMode, bool kStaged = false>
 __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const float* __restrict__ q, const int32_t* __restrict__ x, const float* __restrict__ p,
     const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
     const int32_t* __restrict__ qo_indptr, int64_t n_rows, const int32_t* __restrict__ t2d, int64_t Vd,
     const int32_t* __restrict__ req_index, int64_t n_req, int C, int R, int64_t per_xcd,
     int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len, double* __restrict__ partial,
-    uint32_t* __restrict__ counter) {
+    uint32_t* __restrict__ counter, int64_t qcap) {
     __shared__ ChainShared sh;
+    // a draft row over the draft vocabulary, staged when it fits (qcap entries
+    // of dynamic LDS; 0 when the launch has none)
+    extern __shared__ float qlds[];
     // XCD-aware mapping: workgroups are dispatched round-robin over the 8 XCDs,
     // so consecutive virtual ids (one request's segments) share an XCD's L2.
     const int64_t vid = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -457,7 +521,17 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     // keeps round r's chunk sum.
     const int64_t chunk0 = (int64_t)c * R * kChainWaves;
     double mine = 0.0;
-    if (aligned && (V & 3) == 0 && V < ((int64_t)1 << 29) && !(resid && t2d)) {
+    const bool fast = aligned && (V & 3) == 0 && V < ((int64_t)1 << 29);
+    const bool staged = kStaged && fast && resid && t2d && Vd <= qcap;
+    if (staged) {
+        // the draft row (read once) goes to LDS, 16 loads in flight per thread
+        stage_row<16>(qr, Vd, qlds);
+        __syncthreads();
+    }
+    if (staged) {
+        mine = stream_chunks_fast<true, SV_CHAIN_DEPTH, false, true>(pr, nullptr, V, chunk0, R, -1, t2d,
+                                                                      (uint32_t)Vd, qlds);
+    } else if (fast && !(resid && t2d)) {
         if (resid) mine = stream_chunks_fast<true, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
         else if (point) mine = stream_chunks_fast<false, SV_CHAIN_DEPTH, true>(pr, qr, V, chunk0, R, xo);
         else mine = stream_chunks_fast<false, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
@@ -601,9 +675,19 @@ hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_id
     if (grid > 2147483647LL) return hipErrorInvalidValue;
     auto* kernel = D == 0 ? chain_reject_kernel<kNoDraft>
                           : (draft_probs ? chain_reject_kernel<kDraftProbs> : chain_reject_kernel<kPointDraft>);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kChainBlock), 0, stream, draft_probs, draft_ids,
+    // a draft row over a draft vocabulary small enough for LDS is staged there
+    size_t lds = 0;
+    if (D > 0 && draft_probs && t2d && Vd >= 1 && Vd * 4 <= kMaxStagedBytes) {
+        kernel = chain_reject_kernel<kDraftProbs, true>;
+        lds = (size_t)((Vd * 4 + 15) / 16 * 16);
+        const hipError_t e =
+            hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t qcap = (int64_t)(lds / 4);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kChainBlock), lds, stream, draft_probs, draft_ids,
                        target_probs, seed, offset, B, D, V, qo_indptr, n_rows, t2d, Vd, req_index, n_req, C, R,
-                       per_xcd, accepted, accept_len, partial, counter);
+                       per_xcd, accepted, accept_len, partial, counter, qcap);
     return hipGetLastError();
 }
 
