@@ -378,12 +378,18 @@ def test_ragged_verify_with_reduced_draft_vocab(sv):
     """The reduced-vocabulary drafter end to end: d2t placement then the
     ragged chain verify, and the verify reading the draft rows through the
     inverse table, against the oracle's placement and ragged verify; split
-    and one-workgroup rows, aligned and odd V."""
+    and one-workgroup rows, aligned and odd V.  Draft rows that fit LDS are
+    staged there when a workgroup covers at least Vd target entries: an odd
+    Vd (unaligned draft rows, copied entry by entry), a shuffled table, Vd at
+    the staging limit (38400) and one past it (gathered from global memory)."""
     from workloads import make_d2t
-    for B, D, Vd, V in ((6, 3, 300, 1000), (260, 4, 3200, 12288), (5, 2, 333, 1001), (257, 3, 5000, 20001)):
+    for B, D, Vd, V, shuffled in ((6, 3, 300, 1000, False), (260, 4, 3200, 12288, False), (5, 2, 333, 1001, False),
+                                  (257, 3, 5000, 20001, False), (258, 3, 1003, 4096, False),
+                                  (260, 3, 3000, 12288, True), (256, 1, 38400, 40000, False),
+                                  (256, 1, 38401, 40000, True)):
         rng = np.random.default_rng(B + V)
         c = fuzz_case(1500 + B, B, D, V, "f32")
-        d2t = make_d2t(B, Vd, V)
+        d2t = make_d2t(B, Vd, V, shuffled)
         tgt = (np.arange(Vd) + d2t) % V
         # draft distributions over the draft vocabulary: the fuzz draft rows restricted to the mapped ids
         qd = c["draft_probs"][:, :, tgt].astype(np.float64)
@@ -391,7 +397,7 @@ def test_ragged_verify_with_reduced_draft_vocab(sv):
         x = tgt[rng.integers(0, Vd, (B, D))].astype(np.int32)          # draft ids are target ids
         lens = rng.integers(1, D + 2, B)
         rows, ind = _ragged_pack(c, lens)
-        log(f"ragged verify with a reduced draft vocabulary: B={B} D={D} Vd={Vd} V={V}")
+        log(f"ragged verify with a reduced draft vocabulary: B={B} D={D} Vd={Vd} V={V} shuffled={shuffled}")
         q_full = oracle.d2t_expand(qd, d2t, V)
         ref = oracle.chain_reject_ragged(q_full, x, rows, ind, c["seed"], c["offset"])
         t2d = sv.d2t_inverse(dev(d2t), Vd, V)

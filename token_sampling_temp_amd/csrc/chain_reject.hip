@@ -675,9 +675,12 @@ hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_id
     if (grid > 2147483647LL) return hipErrorInvalidValue;
     auto* kernel = D == 0 ? chain_reject_kernel<kNoDraft>
                           : (draft_probs ? chain_reject_kernel<kDraftProbs> : chain_reject_kernel<kPointDraft>);
-    // a draft row over a draft vocabulary small enough for LDS is staged there
+    // a draft row over a draft vocabulary small enough for LDS is staged there,
+    // when each workgroup's segment spans at least Vd target entries (every
+    // workgroup of a split row would stage the whole draft row)
     size_t lds = 0;
-    if (D > 0 && draft_probs && t2d && Vd >= 1 && Vd * 4 <= kMaxStagedBytes) {
+    if (D > 0 && draft_probs && t2d && Vd >= 1 && Vd * 4 <= kMaxStagedBytes &&
+        (int64_t)R * kChainWaves * kChunk >= Vd) {
         kernel = chain_reject_kernel<kDraftProbs, true>;
         lds = (size_t)((Vd * 4 + 15) / 16 * 16);
         const hipError_t e =
