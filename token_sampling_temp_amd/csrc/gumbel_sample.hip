@@ -82,6 +82,73 @@ __device__ __forceinline__ void load_group4<uint16_t>(const uint16_t* row, int64
     }
 }
 
+// Scores of group g (entries 4g .. 4g+3, those below Vi) folded into the
+// thread's (best, bi); entries arrive in increasing index order.
+__device__ __forceinline__ void gumbel_group(const float (&f)[4], int g, int Vi, float invT, uint64_t seed,
+                                             uint64_t subseq, float& best, int& bi) {
+    const int v0 = g * 4;
+    const uint4 w = philox_block_mad(seed, subseq, (uint64_t)g);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float sc = gumbel_score(f[e], invT, ws[e]);
+        if (v0 + e < Vi && sc > best) {
+            best = sc;
+            bi = v0 + e;
+        }
+    }
+}
+
+// Rows that are 4 * sizeof(T)-byte aligned with V a multiple of 4: each
+// thread keeps the loads of its next kPf groups in flight while it computes
+// the Philox block and the scores of the current one (consume a slot, refill
+// it), so the row's load latency hides behind the arithmetic.  Buffer loads
+// with the row as the range read zeros past its end.
+constexpr int kPf = 4;
+template <int BLOCK, typename T>
+__device__ __forceinline__ void row_gumbel_pipelined(const T* row, int Vi, float invT, uint64_t seed,
+                                                     uint64_t subseq, float& best, int& bi) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr bool kF32 = sizeof(T) == 4;
+    typedef typename std::conditional<kF32, u32x4, u32x2>::type Raw;
+    const int ngroups = (Vi + 3) / 4;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (uint32_t)((int64_t)Vi * (int64_t)sizeof(T)));
+    constexpr int kAux = 2;   // non-temporal: the row is read once
+    auto ld = [&](int g) -> Raw {
+        const uint32_t off = (uint32_t)g * (uint32_t)(4 * sizeof(T));
+        if constexpr (kF32) return __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kAux));
+        else return __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kAux));
+    };
+    auto unpack4 = [&](const Raw r, float (&f)[4]) {
+        if constexpr (kF32) {
+            f[0] = __uint_as_float(r[0]);
+            f[1] = __uint_as_float(r[1]);
+            f[2] = __uint_as_float(r[2]);
+            f[3] = __uint_as_float(r[3]);
+        } else {
+            f[0] = __uint_as_float(r[0] << 16);
+            f[1] = __uint_as_float(r[0] & 0xFFFF0000u);
+            f[2] = __uint_as_float(r[1] << 16);
+            f[3] = __uint_as_float(r[1] & 0xFFFF0000u);
+        }
+    };
+    const int tid = threadIdx.x;
+    Raw slot[kPf];
+#pragma unroll
+    for (int j = 0; j < kPf; ++j) slot[j] = ld(tid + j * BLOCK);
+    for (int g0 = tid; g0 < ngroups; g0 += kPf * BLOCK) {
+#pragma unroll
+        for (int j = 0; j < kPf; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int g = g0 + j * BLOCK;
+            float f[4];
+            unpack4(slot[j], f);
+            slot[j] = ld(g + kPf * BLOCK);
+            if (g < ngroups) gumbel_group(f, g, Vi, invT, seed, subseq, best, bi);
+        }
+    }
+}
+
 template <int BLOCK, typename T>
 __device__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed, uint64_t subseq,
                               ArgmaxShared<BLOCK>& sh) {
@@ -92,6 +159,14 @@ __device__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed
     // increasing index order, so a strict comparison keeps the lowest index
     float best = -INFINITY;
     int bi = (int)threadIdx.x * 4 < Vi ? (int)threadIdx.x * 4 : -1;
+    // whole groups only (V a multiple of 4), so no load straddles the row's end
+    if (aligned && (Vi & 3) == 0 &&
+        V * (int64_t)sizeof(T) + (int64_t)(kPf + 1) * BLOCK * 4 * (int64_t)sizeof(T) < ((int64_t)1 << 32)) {
+        row_gumbel_pipelined<BLOCK, T>(row, Vi, invT, seed, subseq, best, bi);
+        const uint64_t key = bi < 0 ? 0 : pack_key_index(float_key(best), (int64_t)bi);
+        const uint64_t m = block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
+        return packed_index(m);
+    }
     for (int g = threadIdx.x; g < ngroups; g += BLOCK) {
         const int v0 = g * 4;
         float f[4];
