@@ -41,6 +41,12 @@
 #ifndef SV_CHAIN_NT
 #define SV_CHAIN_NT 1              // stream rows with non-temporal loads
 #endif
+#ifndef SV_CHAIN_T2D_AUX
+#define SV_CHAIN_T2D_AUX 0         // the inverse table: temporal loads (shared by every request)
+#endif
+#ifndef SV_CHAIN_STAGE_U
+#define SV_CHAIN_STAGE_U 4         // loads in flight per thread while staging a draft row
+#endif
 
 namespace sv {
 
@@ -281,7 +287,7 @@ __device__ __forceinline__ double stream_chunks_fast(const float* pr, const floa
                                                      uint32_t Vd = 0, const float* qlds = nullptr) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     constexpr int kAux = SV_CHAIN_NT ? 2 : 0;   // non-temporal
-    constexpr int kAuxQ = T2D ? 0 : kAux;
+    constexpr int kAuxQ = T2D ? SV_CHAIN_T2D_AUX : kAux;
     const int64_t s0 = chunk0 * kChunk;
     int64_t s1 = (chunk0 + (int64_t)R * kChainWaves) * kChunk;
     s1 = s1 < V ? s1 : V;
@@ -524,8 +530,8 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const bool fast = aligned && (V & 3) == 0 && V < ((int64_t)1 << 29);
     const bool staged = kStaged && fast && resid && t2d && Vd <= qcap;
     if (staged) {
-        // the draft row (read once) goes to LDS, 16 loads in flight per thread
-        stage_row<16>(qr, Vd, qlds);
+        // the draft row (read once) goes to LDS
+        stage_row<SV_CHAIN_STAGE_U>(qr, Vd, qlds);
         __syncthreads();
     }
     if (staged) {
