@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     __shared__ ChainShared sh;
     // a draft row over the draft vocabulary, staged when it fits (qcap entries
     // of dynamic LDS; 0 when the launch has none)
-    extern __shared__ float qlds[];
+    extern __shared__ __attribute__((aligned(16))) float qlds[];
     // XCD-aware mapping: workgroups are dispatched round-robin over the 8 XCDs,
     // so consecutive virtual ids (one request's segments) share an XCD's L2.
     const int64_t vid = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
