@@ -12,8 +12,10 @@ closed-form laws, library routines, brute force at tiny sizes).
 """
 from . import philox  # noqa: F401
 from .verify import (  # noqa: F401
+    CDF_BAND,
     GREEDY_TEMPERATURE,
     RNG_SLOT_SPAN,
+    cdf_sum_band,
     chain_reject,
     chain_reject_core,
     chain_reject_ragged,
@@ -21,6 +23,7 @@ from .verify import (  # noqa: F401
     d2t_expand,
     decode_logits,
     greedy_verify,
+    gumbel_band,
     gumbel_row,
     gumbel_sample,
     joint_filter_row,

@@ -41,8 +41,14 @@ design notes):
   uses word v of stream (seed_b, offset_b + 32 j) for vocabulary entry v.
 
 Decisions that floating point takes carry a margin; a decision inside its band
-flags the request (category and first affected output position).  The Gumbel
-scores are computed in float32, the precision the GPU decides them in.
+flags the request (category and first affected output position).  Two widths
+exist for the inverse-CDF boundary: ``CDF_BAND`` (1e-6) is the reporting
+category; a draw is excluded from bit-exact comparison only inside
+``cdf_sum_band(V)``, the rounding bound of two double-precision sums of V
+non-negative terms taken in different orders (see ``cdf_sum_band``), unless
+the draw's inputs were themselves rounded differently (the fused verify and
+single-step sampling, whose target probabilities a float32 implementation
+rounds: there the 1e-6 band is the exclusion).  Gumbel scores are float64.
 """
 from __future__ import annotations
 
@@ -59,6 +65,23 @@ CDF_BAND = 1e-6
 TOPP_BAND = 1e-5
 GUMBEL_BAND = 1e-4
 _MASK64 = (1 << 64) - 1
+_U53 = 2.0 ** -53          # unit roundoff of float64
+
+
+def cdf_sum_band(V: int) -> float:
+    """Exclusion band, relative to the total R, for an inverse-CDF draw over V exact double weights.
+
+    Any summation order of n non-negative doubles has relative error at most
+    (n - 1) u (u = 2^-53; Higham, Accuracy and Stability of Numerical
+    Algorithms, Sec. 4.2, for every summation tree).  Two implementations that
+    form the prefix C_j and the total R in different orders can therefore
+    decide ``C_j > u_f * R`` differently only when |C_j / R - u_f| <= 2 g + u
+    with g = V u (each side's C_j and R off by at most g R, plus one rounding
+    of the product).  The oracle's own margin |C_j / R - u_f| is off from the
+    exact one by at most another 2 g + u, so a draw whose oracle margin is at
+    least 4 g + 2 u cannot differ.  The band is twice that: 8 (V + 1) u.
+    """
+    return 8.0 * (int(V) + 1) * _U53
 
 
 # --------------------------------------------------------------------------- inputs
@@ -233,9 +256,9 @@ def sample(logits, dtype, temperature, top_k, top_p, min_p, seed, offset, reques
         wd = philox.words(int(seed[b]), int(offset[b]), 1)
         u = float(philox.uniform(wd)[0])
         code = int(philox.uniform_code(wd)[0])
-        y, near = residual_draw(r, r, u, code)
+        y, margin = residual_draw(r, r, u, code)
         tokens[b] = y
-        flagged[b] = fl or near
+        flagged[b] = fl or margin < CDF_BAND
     return dict(tokens=tokens, flagged=flagged)
 
 
@@ -255,7 +278,10 @@ def residual_draw(r: np.ndarray, fallback: np.ndarray, u_final: float, code: int
     in ascending index order).  If R is not positive the target row
     ``fallback`` is used instead; if that too has no positive mass the draw is
     uniform: floor(u * V) computed exactly from the uniform's code.
-    Returns (token, near_boundary).
+    Returns (token, margin): margin = min |u - C / R| over the two CDF values
+    that bracket the token (C_{y-1} and C_y), 0 when rounding left u * R past
+    every positive weight (the token is then the last positive entry), and
+    infinity for the uniform fallback (no float decision).
     """
     V = r.shape[0]
     c = np.cumsum(r)
@@ -265,28 +291,28 @@ def residual_draw(r: np.ndarray, fallback: np.ndarray, u_final: float, code: int
         c = np.cumsum(r)
         total = c[-1] if V else 0.0
     if not total > 0.0:
-        return int((code * V) >> 24), False
+        return int((code * V) >> 24), math.inf
     t = u_final * total
     y = int(np.searchsorted(c, t, side="right"))
-    near = False
     if y >= V:
-        y = int(np.nonzero(r > 0)[0][-1])
-        near = True
+        return int(np.nonzero(r > 0)[0][-1]), 0.0
     lo = c[y - 1] if y > 0 else 0.0
     hi = c[y]
-    near = near or abs(u_final - lo / total) < CDF_BAND or abs(u_final - hi / total) < CDF_BAND
-    return y, bool(near)
+    return y, float(min(abs(u_final - lo / total), abs(u_final - hi / total)))
 
 
 def chain_reject_core(q: np.ndarray, x: np.ndarray, p: np.ndarray,
-                      u_accept: np.ndarray, u_final: float, code: int):
+                      u_accept: np.ndarray, u_final: float, code: int, cdf_band=None):
     """Chain rejection of one request given its uniforms.
 
     q [D, V] draft probs, x [D] draft ids, p [D+1, V] target probs (float32 or
     float64 values).  For i = 0..D-1: accept x_i iff u_i * q_i(x_i) < p_i(x_i);
     stop at the first rejection and draw the correction from max(0, p_i - q_i);
     if all D are accepted draw the bonus from p_D.
-    Returns dict(tokens [D+1], L, near_accept (position or None), near_cdf).
+    Returns dict(tokens [D+1], L, near_accept (position or None), near_cdf
+    (the draw's margin is below the 1e-6 reporting band), cdf_excluded (below
+    ``cdf_band``; default ``cdf_sum_band(V)``, for inputs both sides hold as
+    the same float values), cdf_margin).
     """
     D = x.shape[0]
     V = p.shape[-1]
@@ -308,11 +334,13 @@ def chain_reject_core(q: np.ndarray, x: np.ndarray, p: np.ndarray,
         r = np.maximum(0.0, target_row - np.asarray(q[L], dtype=np.float64))
     else:
         r = target_row
-    y, near_cdf = residual_draw(r, target_row, u_final, code)
+    y, margin = residual_draw(r, target_row, u_final, code)
+    band = cdf_sum_band(V) if cdf_band is None else float(cdf_band)
     tokens = np.full(D + 1, -1, dtype=np.int64)
     tokens[:L] = x[:L]
     tokens[L] = y
-    return dict(tokens=tokens, L=L, near_accept=near_accept, near_cdf=near_cdf)
+    return dict(tokens=tokens, L=L, near_accept=near_accept, near_cdf=margin < CDF_BAND,
+                cdf_excluded=margin < band, cdf_margin=margin)
 
 
 def one_hot_drafts(x: np.ndarray, V: int) -> np.ndarray:
@@ -332,36 +360,45 @@ def one_hot_drafts(x: np.ndarray, V: int) -> np.ndarray:
     return q
 
 
-def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, requests=None):
+def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, requests=None, cdf_band=None):
     """Batch form of ``rejection_sampling_one_model``.
 
     ``draft_probs`` None is the target-only verify: every draft distribution is
-    one-hot at its draft id (``one_hot_drafts``).
+    one-hot at its draft id (``one_hot_drafts``).  ``cdf_band`` is the draw's
+    exclusion band (default ``cdf_sum_band(V)``: both sides hold the same
+    float32 rows; pass ``CDF_BAND`` when the other side's rows were rounded
+    from these, e.g. float32 probabilities against float64 ones).
 
     Returns accepted_tokens [B, D+1] (int64, -1 padded; rows not computed are
     -2), accept_length [B] (number of accepted drafts, -2 if not computed),
-    flag_pos [B] (first output position affected by a near-boundary float
-    decision; D+1 when none) and near_accept [B] (position of a near-threshold
-    accept test, -1 when none; accept tests are exact products, so this is
-    informational).
+    flag_pos [B] (first output position whose value a float decision inside
+    its exclusion band may change -- here only the drawn token at L, inside
+    ``cdf_sum_band(V)``; D+1 when none), near_accept [B] (position of an
+    accept test within 1e-6 of its threshold, -1 when none; accept tests are
+    exact products, so this is reported only) and near_cdf [B] (the draw lies
+    within the 1e-6 reporting band of a CDF boundary).  accept_length never
+    depends on a sum, so it is exact for every request.
     """
     B, D = np.asarray(draft_ids).shape
     tokens = np.full((B, D + 1), -2, dtype=np.int64)
     L = np.full(B, -2, dtype=np.int64)
     flag_pos = np.full(B, D + 1, dtype=np.int64)
     near_accept = np.full(B, -1, dtype=np.int64)
+    near_cdf = np.zeros(B, dtype=bool)
     reqs = range(B) if requests is None else [int(r) for r in requests]
     for b in reqs:
         ua, uf, code = chain_uniforms(int(seed[b]), int(offset[b]), D)
         q = one_hot_drafts(draft_ids[b], np.shape(target_probs)[-1]) if draft_probs is None else draft_probs[b]
-        res = chain_reject_core(q, draft_ids[b], target_probs[b], ua, uf, code)
+        res = chain_reject_core(q, draft_ids[b], target_probs[b], ua, uf, code, cdf_band=cdf_band)
         tokens[b] = res["tokens"]
         L[b] = res["L"]
-        if res["near_cdf"]:
+        near_cdf[b] = res["near_cdf"]
+        if res["cdf_excluded"]:
             flag_pos[b] = res["L"]
         if res["near_accept"] is not None:
             near_accept[b] = res["near_accept"]
-    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
+    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept,
+                near_cdf=near_cdf)
 
 
 # --------------------------------------------------------------------------- draft -> target vocabulary
@@ -369,10 +406,12 @@ def d2t_expand(draft_probs, d2t, V: int) -> np.ndarray:
     """Draft distributions over a reduced draft vocabulary, placed in the target vocabulary.
 
     TensorRT-LLM interface.py, one-model sampler: draft entry s goes to
-    target index (s + d2t[s]) mod V of a zero-filled row
-    (``target_indices = (source_indices + d2t) % vocab_size``); without a
-    d2t table the draft vocabulary is the first Vd target entries.  The
-    mapping is assumed one-to-one, as the page's scatter does.
+    target index (s + d2t[s]) mod V (a floor modulus, as torch's ``%``) of a
+    zero-filled row; without a d2t table the draft vocabulary is the first Vd
+    target entries.  The page's scatter assumes the mapping is one-to-one and
+    says nothing of shared targets; here the scatter runs in ascending draft
+    order, so when several draft entries share a target the highest-numbered
+    one is what that target holds.
     draft_probs [..., Vd] -> [..., V] (same dtype).
     """
     draft_probs = np.asarray(draft_probs)
@@ -380,9 +419,13 @@ def d2t_expand(draft_probs, d2t, V: int) -> np.ndarray:
     out = np.zeros(draft_probs.shape[:-1] + (V,), dtype=draft_probs.dtype)
     if d2t is None:
         out[..., :Vd] = draft_probs
+        return out
+    target = (np.arange(Vd, dtype=np.int64) + np.asarray(d2t, dtype=np.int64)) % V
+    if np.unique(target).size == Vd:
+        out[..., target] = draft_probs            # one-to-one: a single scatter
     else:
-        target = (np.arange(Vd, dtype=np.int64) + np.asarray(d2t, dtype=np.int64)) % V   # floor mod, as torch's %
-        out[..., target] = draft_probs
+        for s in range(Vd):                       # shared targets: each later entry overwrites
+            out[..., target[s]] = draft_probs[..., s]
     return out
 
 
@@ -435,11 +478,11 @@ def chain_reject_ragged(draft_probs, draft_ids, target_packed, qo_indptr, seed, 
 
     TensorRT-LLM interface.py, ragged branch of the one-model sampler: the
     packed rows are padded as ``ragged_pad`` states, the chain verify runs on
-    the padded rectangle, and the emitted count is clamped to verify_lens
-    ("accepting past it commits tokens the target never scored").  Returned
-    accept_length is the number of accepted draft tokens after the clamp
-    (emitted - 1); tokens after the emitted ones are -1.  Requests with an
-    invalid length get accept_length -1 and all tokens -1.
+    the padded rectangle, and the number of emitted tokens is capped at the
+    request's verify length, since positions past it were never scored by the
+    target.  Returned accept_length is the number of accepted draft tokens
+    after the cap (emitted - 1); tokens after the emitted ones are -1.
+    Requests with an invalid length get accept_length -1 and all tokens -1.
 
     Same return dict as ``chain_reject``.
     """
@@ -449,6 +492,7 @@ def chain_reject_ragged(draft_probs, draft_ids, target_packed, qo_indptr, seed, 
     L = np.full(B, -2, dtype=np.int64)
     flag_pos = np.full(B, D + 1, dtype=np.int64)
     near_accept = np.full(B, -1, dtype=np.int64)
+    near_cdf = np.zeros(B, dtype=bool)
     reqs = range(B) if requests is None else [int(r) for r in requests]
     for b in reqs:
         if lens[b] < 0:
@@ -462,11 +506,14 @@ def chain_reject_ragged(draft_probs, draft_ids, target_packed, qo_indptr, seed, 
         t[emitted:] = -1
         tokens[b] = t
         L[b] = emitted - 1
-        if res["near_cdf"] and res["L"] < emitted:
-            flag_pos[b] = res["L"]
+        if res["L"] < emitted:
+            near_cdf[b] = res["near_cdf"]
+            if res["cdf_excluded"]:
+                flag_pos[b] = res["L"]
         if res["near_accept"] is not None and res["near_accept"] < emitted:
             near_accept[b] = res["near_accept"]
-    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
+    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept,
+                near_cdf=near_cdf)
 
 
 # --------------------------------------------------------------------------- fused target rows + chain rejection
@@ -486,8 +533,9 @@ def verify_fused(logits, dtype, temperature, top_k, top_p, draft_probs, draft_id
     Returns the ``chain_reject`` dictionary.  Here ``flag_pos`` also covers
     the decisions a float32 implementation takes from differently rounded
     target probabilities: a near-threshold accept test at position i (from i
-    on), a top-p boundary flag on a row j <= L (from j on), and a near CDF
-    boundary (from L on).
+    on), a top-p boundary flag on a row j <= L (from j on), and a CDF boundary
+    within 1e-6 (from L on; the draw's weights are probabilities that a
+    float32 implementation rounds, so the double-sum band does not cover it).
     """
     B, N, V = np.shape(logits)
     D = N - 1
@@ -496,6 +544,7 @@ def verify_fused(logits, dtype, temperature, top_k, top_p, draft_probs, draft_id
     L = np.full(B, -2, dtype=np.int64)
     flag_pos = np.full(B, N, dtype=np.int64)
     near_accept = np.full(B, -1, dtype=np.int64)
+    near_cdf = np.zeros(B, dtype=bool)
     reqs = range(B) if requests is None else [int(r) for r in requests]
     for b in reqs:
         z = decode_logits(logits[b], dtype)
@@ -515,11 +564,12 @@ def verify_fused(logits, dtype, temperature, top_k, top_p, draft_probs, draft_id
                     break
         P = np.zeros((N, V))
         P[:len(rows)] = np.array(rows)
-        res = chain_reject_core(draft_probs[b], x[b], P, ua, uf, code)
+        res = chain_reject_core(draft_probs[b], x[b], P, ua, uf, code, cdf_band=CDF_BAND)
         tokens[b] = res["tokens"]
         L[b] = res["L"]
+        near_cdf[b] = res["near_cdf"]
         fp = N
-        if res["near_cdf"]:
+        if res["cdf_excluded"]:
             fp = res["L"]
         if res["near_accept"] is not None:
             near_accept[b] = res["near_accept"]
@@ -529,7 +579,8 @@ def verify_fused(logits, dtype, temperature, top_k, top_p, draft_probs, draft_id
                 fp = min(fp, j)
                 break
         flag_pos[b] = fp
-    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept)
+    return dict(accepted_tokens=tokens, accept_length=L, flag_pos=flag_pos, near_accept=near_accept,
+                near_cdf=near_cdf)
 
 
 # --------------------------------------------------------------------------- greedy verify
@@ -571,23 +622,39 @@ def greedy_verify(logits, dtype, draft_ids, requests=None):
 
 # --------------------------------------------------------------------------- Gumbel-max
 def gumbel_row(z32: np.ndarray, temperature: float, seed: int, subseq: int):
-    """Temperature sample of one row by Gumbel-max, in float32.
+    """Temperature sample of one row by Gumbel-max, in float64.
 
     s_v = z_v / T + G_v with G_v = -ln(-ln u_v), u_v = uniform of word v of
     stream (seed, subseq); token = lowest-index argmax of s.  Returns (token,
-    near_tie) where near_tie marks a top-two score gap below GUMBEL_BAND.
+    near_tie).  near_tie marks a gap between the two largest scores below
+    ``gumbel_band`` of those two entries: an implementation that forms the
+    scores in float32 is off by a few float32 ulps of |z/T| + |G| per score,
+    and only a gap that small can reorder the top two.
     """
-    z32 = np.asarray(z32, dtype=np.float32)
-    V = z32.shape[0]
-    u = philox.uniform(philox.words(seed, subseq, V)).astype(np.float32)
+    z = np.asarray(z32, dtype=np.float32).astype(np.float64)
+    V = z.shape[0]
+    u = philox.uniform(philox.words(seed, subseq, V))
     g = -np.log(-np.log(u))
-    s = z32 / np.float32(temperature) + g
+    zt = z / float(temperature)
+    s = zt + g
     y = int(np.argmax(s))
     near = False
     if V > 1:
-        top2 = np.partition(s, V - 2)[V - 2:]
-        near = bool(float(top2[1]) - float(top2[0]) < GUMBEL_BAND)
+        i2 = np.argpartition(s, V - 2)[V - 2:]
+        scale = float(np.max(np.abs(zt[i2]) + np.abs(g[i2])))
+        near = bool(abs(float(s[i2[1]]) - float(s[i2[0]])) < gumbel_band(scale))
     return y, near
+
+
+def gumbel_band(scale: float) -> float:
+    """Near-tie band of two Gumbel scores whose terms |z/T| + |G| are at most ``scale``.
+
+    1e-4 for scale <= 16, growing in proportion beyond: 1e-4 / 16 = 6.25e-6
+    of the scale is about 52 float32 ulps (2^-23 relative each), an order of
+    magnitude above the error of a float32 score from a correctly rounded
+    product and logarithms within a few ulps.
+    """
+    return GUMBEL_BAND * max(1.0, float(scale) / 16.0)
 
 
 def gumbel_sample(logits, dtype, temperature, draft_ids, seed, offset, requests=None,

@@ -8,6 +8,8 @@
 * Special cases: q = p accepts every draft; disjoint supports reject at 0;
   invalid ids reject; all-zero rows fall back to p, then to a uniform index.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -132,8 +134,8 @@ def test_zero_residual_falls_back_to_target_then_uniform():
     # all-zero target row: uniform index floor(u * V), exact from the uniform's code
     z = np.zeros((2, V), np.float32)
     for code in (1, 3, 2 ** 23 + 1, 2 ** 24 - 1):
-        y, near = residual_draw(np.zeros(V), np.zeros(V), code * 2.0 ** -24, code)
-        assert y == (code * V) >> 24 and 0 <= y < V and not near
+        y, margin = residual_draw(np.zeros(V), np.zeros(V), code * 2.0 ** -24, code)
+        assert y == (code * V) >> 24 and 0 <= y < V and margin == math.inf
     out = chain_reject_core(z[:1], np.array([2]), z, np.array([0.3]), 0.999, 2 ** 24 - 1)
     assert out["L"] == 0 and out["tokens"][0] == V - 1
 
@@ -245,3 +247,90 @@ def test_target_only_is_the_one_hot_draft_case():
         assert a["accept_length"][b] == L
         if L < D and 0 <= x[b, L] < V:
             assert a["accepted_tokens"][b, L] != x[b, L] or p[b, L, x[b, L]] > 1.0
+
+
+def test_draw_margin_worked_example():
+    """The margin is the distance of u to the two CDF values bracketing the token."""
+    r = np.array([0.25, 0.5, 0.25])
+    y, m = residual_draw(r, r, 0.3, 1)
+    assert y == 1 and abs(m - 0.05) < 1e-15
+    y, m = residual_draw(r, r, 0.74, 1)
+    assert y == 1 and abs(m - 0.01) < 1e-15
+    # u exactly on a boundary: the token moves past it and the margin is 0
+    y, m = residual_draw(r, r, 0.25, 1)
+    assert y == 1 and m == 0.0
+
+
+def _orders(r):
+    """Prefix sums and totals of r in four association orders: sequential,
+    blocked (per-1024 block sums, then a running sum of blocks), pairwise
+    (numpy's reduction inside blocks of 64) and reversed-within-block."""
+    V = r.size
+    seq = np.cumsum(r)
+    out = [(seq, seq[-1])]
+    for blk in (1024, 64):
+        n = (V + blk - 1) // blk
+        pad = np.zeros(n * blk)
+        pad[:V] = r
+        tiles = pad.reshape(n, blk)
+        sums = tiles.sum(axis=1)                        # pairwise inside a tile
+        base = np.concatenate([[0.0], np.cumsum(sums)[:-1]])
+        pre = (base[:, None] + np.cumsum(tiles, axis=1)).reshape(-1)[:V]
+        out.append((pre, float(np.cumsum(sums)[-1])))
+    rev = np.cumsum(r[::-1])[::-1]                       # suffix sums, converted to prefixes
+    tot = float(rev[0])
+    out.append((tot - np.concatenate([rev[1:], [0.0]]), tot))
+    return out
+
+
+def test_cdf_sum_band_covers_summation_order():
+    """The exclusion band is a real bound: across association orders the
+    normalised CDF values C_j / R never differ by more than a quarter of
+    cdf_sum_band(V) (the band keeps a factor 2 over the two-sided bound),
+    on row shapes with the largest rounding: many tiny weights behind a
+    large one, Zipf rows and rows with exact zeros."""
+    from oracle import cdf_sum_band
+    rng = np.random.default_rng(91)
+    for V in (1000, 32000, 128256):
+        rows = [rng.random(V) ** 6,
+                np.concatenate([[1.0], rng.random(V - 1) * 1e-12]),
+                1.0 / np.arange(1, V + 1) ** 1.1]
+        z = rng.random(V)
+        z[rng.random(V) < 0.5] = 0.0
+        rows.append(z)
+        band = cdf_sum_band(V)
+        for r in rows:
+            r = r.astype(np.float32).astype(np.float64)
+            ref, rt = _orders(r)[0]
+            for pre, tot in _orders(r)[1:]:
+                d = np.max(np.abs(pre / tot - ref / rt))
+                assert d <= band / 4, (V, d, band)
+    # the band grows with V: a constant band would be wrong for long rows
+    assert cdf_sum_band(2 ** 20) > 100 * cdf_sum_band(1000)
+
+
+def test_cdf_exclusion_band_is_sufficient_against_another_order():
+    """A draw outside the exclusion band gives the same token under a
+    different summation order (blocked sums, as an implementation that sums
+    per tile would form them); only draws inside the band may differ."""
+    from oracle import cdf_sum_band
+    rng = np.random.default_rng(92)
+    V = 4096
+    band = cdf_sum_band(V)
+    differ = 0
+    scale = V * 2.0 ** -53                      # the size of a worst-case summation error
+    for t in range(300):
+        r = (rng.random(V) ** 8).astype(np.float32).astype(np.float64)
+        tot_seq = np.cumsum(r)
+        # uniforms placed right at a boundary, then nudged by multiples of that size
+        j = int(rng.integers(0, V))
+        for k in (-8, -2, -0.5, -0.05, -0.005, 0.0, 0.005, 0.05, 0.5, 2, 8):
+            u = float(np.clip(tot_seq[j] / tot_seq[-1] + k * scale, 1e-12, 1 - 1e-12))
+            y, m = residual_draw(r, r, u, 1)
+            pre, tot = _orders(r)[1]
+            y2 = int(np.searchsorted(pre, u * tot, side="right"))
+            y2 = min(y2, V - 1)
+            if y2 != y:
+                differ += 1
+                assert m < band, (t, k, m, band)
+    print(f"draws that another order changes: {differ} (all inside the band)")

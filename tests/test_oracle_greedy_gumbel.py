@@ -117,6 +117,38 @@ def test_gumbel_greedy_rows_and_strict_accept():
     assert list(again["accept_length"]) == [D] * B
 
 
+def test_gumbel_band_covers_float32_scores():
+    """An implementation that forms the scores in float32 (division and
+    logarithms each correctly rounded) picks a different token than the
+    float64 oracle only on rows the oracle flags as near ties.  Rows mix
+    small and large |z/T| (T down to 0.02) so the scaled band is exercised;
+    most rows get a planted runner-up whose logit is set so its score trails
+    the best one by 0 to 1e-5 of its size, where float32 rounding decides."""
+    from oracle import philox
+    rng = np.random.default_rng(23)
+    diff = 0
+    for t in range(600):
+        V = int(rng.integers(2, 3000))
+        z = (rng.standard_normal(V) * rng.choice([0.5, 3.0, 30.0])).astype(np.float32)
+        T = np.float32(rng.choice([0.02, 0.3, 1.0, 1.7]))
+        seed, sub = int(rng.integers(1, 2 ** 40)), int(rng.integers(0, 2 ** 20))
+        u32 = philox.uniform(philox.words(seed, sub, V)).astype(np.float32)
+        if t % 4 and V > 2:
+            g64 = -np.log(-np.log(u32.astype(np.float64)))
+            s64 = z.astype(np.float64) / float(T) + g64
+            top = int(np.argmax(s64))
+            j2 = (top + 1 + int(rng.integers(0, V - 1))) % V
+            gap = abs(s64[top]) * float(rng.choice([0.0, 1e-8, 1e-7, 1e-6, 1e-5]))
+            z[j2] = np.float32((s64[top] - g64[j2] - gap) * float(T))
+        y, near = gumbel_row(z, float(T), seed, sub)
+        s32 = z / T + (-np.log(-np.log(u32)))
+        if int(np.argmax(s32)) != y:
+            diff += 1
+            assert near, (t, V, float(T))
+    assert diff > 0                                        # the planted runner-ups do reach the band
+    print(f"float32 choices that differ: {diff} (all flagged)")
+
+
 def test_gumbel_rows_use_distinct_streams():
     z = np.zeros((1, 8, 1000), np.float32)
     out = gumbel_sample(z, "f32", np.array([1.0], np.float32), np.zeros((1, 7), np.int32),

@@ -130,3 +130,23 @@ def test_d2t_expand_placement_and_mass():
     # without a table the draft vocabulary is the first Vd target entries
     out = d2t_expand(q, None, 11)
     assert np.array_equal(out[:, :8], q) and np.all(out[:, 8:] == 0)
+
+
+def test_d2t_shared_targets_keep_the_last_draft_entry():
+    """A table that sends several draft entries to one target: the target
+    holds the highest-numbered of them (computed here with np.maximum.at on
+    the draft index, independently of the oracle's scatter), every other
+    target holds its unique entry or 0."""
+    from oracle import d2t_expand
+    rng = np.random.default_rng(74)
+    for Vd, V in ((50, 60), (200, 200), (7, 5)):
+        tgt = rng.integers(0, V, Vd)                       # collisions certain at these sizes
+        d2t = (tgt - np.arange(Vd)).astype(np.int64)      # (s + d2t[s]) mod V = tgt[s]
+        if Vd == 7:
+            d2t = d2t - 3 * V                              # negative offsets wrap (floor modulus)
+        q = rng.random((3, Vd)).astype(np.float32)
+        out = d2t_expand(q, d2t, V)
+        winner = np.full(V, -1, np.int64)
+        np.maximum.at(winner, tgt, np.arange(Vd))
+        want = np.where(winner >= 0, q[:, np.maximum(winner, 0)], 0.0).astype(np.float32)
+        assert np.array_equal(out, want), (Vd, V)

@@ -8,7 +8,8 @@
   e^3 / (e^3 + e^2 + e + 1) = 0.644 < 0.7 and 0.644 + 0.237 >= 0.7, so the
   joint nucleus is {3, 2}, and with the top-2 set the joint filter keeps {3, 2}.
 * Min-p keeps exactly the tokens whose softmax probability (scipy) is at
-  least min_p times the largest.
+  least min_p times the largest; at min_p >= 1 that is the set of maximal
+  probabilities (ties included).
 * The sampled token follows the renormalised kept distribution (chi-square
   over Philox streams); greedy rows give the argmax.
 """
@@ -54,6 +55,27 @@ def test_min_p_matches_softmax_probabilities():
         if fl:
             continue
         assert np.array_equal(w > 0, p >= mp * p.max())
+
+
+def test_min_p_at_or_above_one_keeps_the_maximal_set():
+    """min_p = 1 keeps {p >= p_max}; min_p = 1.5 asks for p >= 1.5 p_max, which
+    no token meets, and the reading clamps it to the same set (the page's
+    name gives no formula past 1).  Rows with tied maxima keep every tie."""
+    rng = np.random.default_rng(83)
+    for t in range(40):
+        V = int(rng.integers(2, 50))
+        z = np.round(rng.standard_normal(V) * 2, 1)
+        if t % 2 == 0:
+            z[rng.integers(0, V, 3)] = z.max()          # tied maxima
+        T = float(rng.uniform(0.3, 1.5))
+        p = softmax(z / T)
+        want = p >= p.max()
+        for mp in (1.0, 1.5):
+            w, fl = joint_filter_row(z, T, 0, 1.0, mp)
+            assert np.array_equal(w > 0, want), (t, mp)
+            # combined with top-k = V - 1 and a top-p of 0.99 the maximal set survives unchanged
+            w2, _ = joint_filter_row(z, T, V - 1, 0.99, mp)
+            assert np.array_equal(w2 > 0, want & (w2 > 0)) and (w2 > 0).any()
 
 
 def test_sampled_law_and_greedy_rows():

@@ -116,8 +116,8 @@ def test_verify_fused_degenerate_rows(sv):
 
 def test_verify_fused_config5_filtered_rows(sv):
     """The mixed batch's top-k and top-p requests through req_index at the full
-    shape (B=1024, D=7, V=129280 bf16): identical to the two-call form for all
-    of them, and to the oracle on a sample."""
+    shape (B=1024, D=7, V=129280 bf16): identical to the two-call form and
+    to the oracle for all 512 of them."""
     torch = __import__("torch")
     c = make_config(5)
     B, D, V = 1024, 7, 129280
@@ -137,12 +137,13 @@ def test_verify_fused_config5_filtered_rows(sv):
     assert np.all(A[rest] == SENTINEL) and np.all(Ls[rest] == SENTINEL)
     A2, L2 = two_call(sv, z, T, k, p, q, x, seed, off, req=dev(filt), B=B, N=N, V=V)
     assert np.array_equal(A[filt], A2[filt]) and np.array_equal(Ls[filt], L2[filt])
-    rng = np.random.default_rng(9)
-    sample = rng.choice(filt, size=12, replace=False)
+    log("config 5 fused: all filtered requests against the oracle")
     ref = oracle.verify_fused(c["logits"], "bf16", c["temperature"], c["top_k"], c["top_p"], c["draft_probs"],
-                              c["draft_ids"], c["seed"], c["offset"], requests=sample)
-    flagged = assert_match(A, Ls, ref, sample, "cfg5 fused")
-    log(f"config 5 fused: mean L={Ls[filt].mean():.3f}, sampled flagged={flagged}")
+                              c["draft_ids"], c["seed"], c["offset"], requests=filt)
+    flagged = assert_match(A, Ls, ref, filt, "cfg5 fused")
+    assert flagged <= 1 + len(filt) // 50, flagged
+    log(f"config 5 fused: mean L={Ls[filt].mean():.3f}, flagged={flagged} of {len(filt)}, "
+        f"within 1e-6 of a CDF boundary {int(ref['near_cdf'][filt].sum())}")
 
 
 def test_verify_fused_other_row_paths(sv):

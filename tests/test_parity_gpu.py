@@ -1,10 +1,15 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
 Integer results (tokens, accept lengths, predict, accept_index, argmax) must be
-bit-exact except decisions the oracle flags as falling inside a float band
-(CDF boundary 1e-6, top-p boundary 1e-5 of the top-k mass, Gumbel near tie
-1e-4); flagged requests are compared up to the flagged position.  Probabilities
-must agree within 1e-5 absolute.  Every test prints its case before launching.
+bit-exact except decisions the oracle flags as falling inside their exclusion
+band: an inverse-CDF draw within the double-sum rounding bound of a boundary
+(8 (V + 1) 2^-53 of the row mass when both sides sum the same float32 rows;
+1e-6 when one side's rows are float64), a top-p boundary within 1e-5 of the
+top-k mass, a Gumbel near tie (1e-4, scaled with the scores' size).  Flagged
+requests are compared up to the flagged position.  Chain-rejection accept
+lengths come from exact products and are compared for every request.
+Probabilities must agree within 1e-5 absolute.  Every test prints its case
+before launching.
 """
 import itertools
 
@@ -31,18 +36,27 @@ def sv():
 
 
 # --------------------------------------------------------------------------- comparison helpers
-def assert_chain_match(gpu_tok, gpu_len, ref, reqs, ctx, check_flags=True):
-    """Bit-exact tokens/accept lengths except from a flagged position on."""
+def assert_chain_match(gpu_tok, gpu_len, ref, reqs, ctx, len_exact=True, max_excluded=None):
+    """Accept lengths and tokens bit-exact, except tokens from the oracle's
+    flagged position on.  len_exact: every accept length must match (chain
+    rejection, where L follows from exact products); otherwise a flag at or
+    before L may move it (Gumbel rows).  max_excluded bounds the number of
+    requests with an excluded decision (default: 1 + 1% of them).  Returns
+    that number."""
+    reqs = list(reqs)
     flagged = 0
     for b in reqs:
         L = int(ref["accept_length"][b])
         fp = int(ref["flag_pos"][b])
-        assert int(gpu_len[b]) == L or fp <= L, (ctx, b, int(gpu_len[b]), L)
-        n = min(fp, L + 1) if check_flags else L + 1
+        if len_exact or fp > L:
+            assert int(gpu_len[b]) == L, (ctx, b, int(gpu_len[b]), L, fp)
+        n = min(fp, L + 1)
         assert list(gpu_tok[b, :n]) == list(ref["accepted_tokens"][b, :n]), (ctx, b, gpu_tok[b], ref["accepted_tokens"][b])
         if int(gpu_len[b]) == L:
             assert np.all(gpu_tok[b, L + 1:] == -1), (ctx, b)
         flagged += fp <= L
+    bound = 1 + len(reqs) // 100 if max_excluded is None else max_excluded
+    assert flagged <= bound, (ctx, "excluded decisions", flagged, bound)
     return flagged
 
 
@@ -513,15 +527,24 @@ def test_chain_reject_request_subset_and_determinism(sv):
 
 
 def test_chain_reject_config3_full(sv):
+    """The large-vocab batch in full, at the four Philox offsets the benchmark
+    rotates through (4096 r): every accept length exact, every token exact
+    outside the double-sum exclusion band; the 1e-6 CDF category is counted."""
     c = make_config(3)
     B, D, V = 256, 5, 128256
-    log("chain config 3 full: B=256 D=5 V=128256 f32")
-    ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
-    acc, alen = sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]),
-                                dev(c["seed"]), dev(c["offset"]))
-    flagged = assert_chain_match(np_i(acc), np_i(alen), ref, range(B), "cfg3")
-    L = np_i(alen)
-    log(f"config 3: mean L={L.mean():.3f} P(L=D)={np.mean(L == D):.3f} flagged={flagged}")
+    args = [dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]), dev(c["seed"])]
+    near, excl, Ls = 0, 0, []
+    for r in range(4):
+        off = np.full(B, 4096 * r, np.uint64)
+        log(f"chain config 3 full: B=256 D=5 V=128256 f32, offset {4096 * r}")
+        ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], off)
+        acc, alen = sv.chain_reject(*args, dev(off))
+        excl += assert_chain_match(np_i(acc), np_i(alen), ref, range(B), ("cfg3", r), max_excluded=1)
+        near += int(ref["near_cdf"].sum())
+        Ls.append(np_i(alen))
+    L = np.concatenate(Ls)
+    log(f"config 3: mean L={L.mean():.3f} P(L=D)={np.mean(L == D):.3f} within 1e-6 of a CDF boundary={near} "
+        f"excluded={excl} of {4 * B}")
     assert 2.0 < L.mean() < 4.5
 
 
@@ -628,7 +651,8 @@ def test_softmax_then_chain_config2_full(sv):
     ref_c = oracle.chain_reject(c["draft_probs"], c["draft_ids"], g, c["seed"], c["offset"])
     assert_chain_match(np_i(acc), np_i(alen), ref_c, range(B), "cfg2 stage")
     # end to end: the oracle chain on the oracle's probabilities (near-threshold accepts flagged)
-    ref_e = oracle.chain_reject(c["draft_probs"], c["draft_ids"], ref, c["seed"], c["offset"])
+    ref_e = oracle.chain_reject(c["draft_probs"], c["draft_ids"], ref, c["seed"], c["offset"],
+                                cdf_band=oracle.CDF_BAND)
     ok = [b for b in range(B) if not fl[b].any() and ref_e["near_accept"][b] < 0]
     assert_chain_match(np_i(acc), np_i(alen), ref_e, ok, "cfg2 end-to-end")
     log(f"config 2: mean L={np_i(alen).mean():.3f}")
@@ -675,14 +699,20 @@ def test_gumbel_sample_fuzz(sv):
             fp = int(ref["flag_pos"][b])
             assert list(s_gpu[b, :fp]) == list(ref["sampled"][b, :fp]), (V, D, dt, b, s_gpu[b], ref["sampled"][b])
             flagged += fp < D + 1
-        assert_chain_match(np_i(out["accepted_tokens"]), np_i(out["accept_length"]), ref, range(B), (V, D, dt))
+        assert_chain_match(np_i(out["accepted_tokens"]), np_i(out["accept_length"]), ref, range(B), (V, D, dt),
+                           len_exact=False, max_excluded=B)
         out2 = sv.gumbel_sample(dev_logits(c["logits"], dt), dev(T), dev(x), dev(c["seed"]), dev(c["offset"]))
         assert np.array_equal(np_i(out2["accepted_tokens"]), np_i(out["accepted_tokens"]))
     log(f"gumbel fuzz flagged requests: {flagged}")
 
 
 # --------------------------------------------------------------------------- config 5 (mixed modes)
-def test_config5_mixed_modes_sampled(sv):
+def test_config5_mixed_modes_full(sv):
+    """The mixed batch (B=1024 D=7 V=129280 bf16), each mode through
+    req_index into shared outputs, compared with the oracle for every
+    request: all 256 greedy requests, all 256 Gumbel requests, the chain
+    stage of all 512 top-k/top-p requests on the GPU's probabilities, and the
+    renormalised probabilities of 128 of those requests (every row)."""
     torch = __import__("torch")
     c = make_config(5)
     B, D, V = 1024, 7, 129280
@@ -708,20 +738,24 @@ def test_config5_mixed_modes_sampled(sv):
     assert np.all((Ls >= 0) & (Ls <= D))
     for b in range(B):
         assert np.all(A[b, Ls[b] + 1:] == -1) and np.all(A[b, :Ls[b] + 1] >= 0)
-    rng = np.random.default_rng(5)
-    sample = {m: rng.choice(idx[m], size=6, replace=False) for m in range(4)}
-    rg = oracle.greedy_verify(c["logits"], "bf16", c["draft_ids"], requests=sample[MODE_GREEDY])
-    for b in sample[MODE_GREEDY]:
-        assert list(A[b]) == list(rg["accepted_tokens"][b]) and Ls[b] == rg["accept_length"][b]
+    log("config 5: greedy requests against the oracle (256)")
+    rg = oracle.greedy_verify(c["logits"], "bf16", c["draft_ids"], requests=idx[MODE_GREEDY])
+    for b in idx[MODE_GREEDY]:
+        assert list(A[b]) == list(rg["accepted_tokens"][b]) and Ls[b] == rg["accept_length"][b], b
+    log("config 5: Gumbel requests against the oracle (256)")
     ru = oracle.gumbel_sample(c["logits"], "bf16", c["temperature"], c["draft_ids"], c["seed"], c["offset"],
-                              requests=sample[MODE_TEMPERATURE])
-    assert_chain_match(A, Ls, ru, sample[MODE_TEMPERATURE], "cfg5 gumbel")
-    sreq = np.concatenate([sample[MODE_TOPK], sample[MODE_TOPP]])
-    rp, fl = oracle.softmax_renorm(c["logits"], "bf16", c["temperature"], c["top_k"], c["top_p"], requests=sreq)
+                              requests=idx[MODE_TEMPERATURE])
+    ng = assert_chain_match(A, Ls, ru, idx[MODE_TEMPERATURE], "cfg5 gumbel", len_exact=False, max_excluded=3)
+    log("config 5: chain stage against the oracle on the GPU's probabilities (512)")
     gp = probs.cpu().numpy()
-    assert_probs_match(gp[sreq].astype(np.float64), rp, fl, "cfg5 softmax")
-    rc = oracle.chain_reject(c["draft_probs"], c["draft_ids"], gp, c["seed"], c["offset"], requests=sreq)
-    assert_chain_match(A, Ls, rc, sreq, "cfg5 chain stage")
+    rc = oracle.chain_reject(c["draft_probs"], c["draft_ids"], gp, c["seed"], c["offset"], requests=filt)
+    nc = assert_chain_match(A, Ls, rc, filt, "cfg5 chain stage", max_excluded=1)
+    sreq = np.concatenate([idx[MODE_TOPK][:64], idx[MODE_TOPP][:64]])
+    log(f"config 5: renormalised probabilities against the oracle ({len(sreq)} requests x {N} rows)")
+    rp, fl = oracle.softmax_renorm(c["logits"], "bf16", c["temperature"], c["top_k"], c["top_p"], requests=sreq)
+    nf = assert_probs_match(gp[sreq].astype(np.float64), rp, fl, "cfg5 softmax")
+    log(f"config 5: excluded Gumbel near ties {ng}, excluded CDF draws {nc}, "
+        f"within 1e-6 of a CDF boundary {int(rc['near_cdf'][filt].sum())}, top-p flagged rows {nf}")
     for m, name in ((MODE_GREEDY, "greedy"), (MODE_TEMPERATURE, "temperature"), (MODE_TOPK, "top-k"),
                     (MODE_TOPP, "top-p")):
         log(f"config 5 {name}: mean L={Ls[idx[m]].mean():.3f}")
