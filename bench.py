@@ -28,7 +28,15 @@ draft rows of a 32000-entry draft vocabulary placed in V=128256) and
 ``sample`` (single-step sampling of 1024 bf16 rows of V=129280).
 
 The CPU baseline is the numpy oracle timed on this host on the same inputs
-(whole batches repeated for --cpu-seconds), single threaded.
+(whole batches repeated for --cpu-seconds), single threaded.  For the chain
+workloads that leg also compares the oracle's outputs with the GPU's outputs
+of the same replicas and reports the counts (``parity``).
+
+Beside the 8 TB/s data-sheet peak, the roofline reports the fraction of a
+read rate measured on the same GPU in the same run by a plain read-stream
+kernel (``libsvprobe.so``, best of a small sweep of grid sizes and loads in
+flight), and the per-call time distribution (p10 / median / p90, one HIP
+event pair per call).
 """
 from __future__ import annotations
 
@@ -119,6 +127,91 @@ def load_traffic(summary, digest):
     return float(m_b.group(1))
 
 
+def cpu_info():
+    """Host CPU facts for the baseline: logical CPUs, CPUs this process may run on, model name."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_count": os.cpu_count(), "affinity": affinity, "cpu_model": model}
+
+
+class ParityCount:
+    """Request-level comparison of GPU chain outputs with the oracle's: accept lengths always
+    exact (they follow from exact products), tokens exact up to the oracle's excluded position."""
+
+    def __init__(self):
+        self.requests = self.exact = self.near_accept = self.near_cdf = self.excluded = self.mismatches = 0
+
+    def add(self, acc, alen, ref, reqs=None):
+        reqs = range(len(alen)) if reqs is None else reqs
+        for b in reqs:
+            L, fp = int(ref["accept_length"][b]), int(ref["flag_pos"][b])
+            ok = int(alen[b]) == L
+            n = min(fp, L + 1)
+            ok = ok and list(acc[b, :n]) == list(ref["accepted_tokens"][b, :n]) and bool(np.all(acc[b, L + 1:] == -1))
+            self.requests += 1
+            self.mismatches += not ok
+            self.exact += bool(ok and list(acc[b]) == list(ref["accepted_tokens"][b]))
+            self.near_accept += int(ref["near_accept"][b]) >= 0
+            self.near_cdf += bool(ref["near_cdf"][b])
+            self.excluded += fp <= L
+
+    def report(self):
+        return {"requests": self.requests, "exact": self.exact, "flagged_accept": self.near_accept,
+                "flagged_cdf": self.near_cdf, "excluded": self.excluded, "mismatches": self.mismatches,
+                "bands": "flagged_*: within 1e-6 of an accept threshold / CDF boundary (reported); excluded: "
+                         "draws within 8 (V + 1) 2^-53 of a CDF boundary, tokens from there not compared"}
+
+
+def stream_peak(dev):
+    """The HBM read rate a plain read-stream kernel reaches here (GB/s): best over grids of 256..2048
+    workgroups and 4..16 loads in flight, four 1 GiB buffers rotating so nothing is served from the
+    256 MB Infinity Cache."""
+    import ctypes
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "token_sampling_temp_amd", "libsvprobe.so"))
+    L.svprobe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    L.svprobe_read_stream.restype = ctypes.c_int
+    nbytes = 1 << 30
+    bufs = [torch.zeros(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(4)]
+    sink = torch.zeros(4 * 4096, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    best = (0.0, None)
+    for grid in (256, 512, 1024, 2048):
+        for loads in (4, 8, 16):
+            def run(i):
+                st = L.svprobe_read_stream(ctypes.c_void_p(bufs[i % 4].data_ptr()), nbytes, grid, loads,
+                                           ctypes.c_void_p(sink.data_ptr()), sp)
+                assert st == 0, st
+            for i in range(4):
+                run(i)
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            n = 12
+            for i in range(n):
+                run(i)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            gbs = nbytes * n / (s0.elapsed_time(s1) * 1e-3) / 1e9
+            if gbs > best[0]:
+                best = (gbs, {"grid": grid, "loads_in_flight": loads})
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
 # --------------------------------------------------------------------------- workloads
 class ChainWorkload:
     """B=256 D=5 V=128256 chain rejection on float32 probabilities."""
@@ -157,15 +250,23 @@ class ChainWorkload:
         """Bytes the method must move per call, from each replica's realised accept lengths."""
         per = []
         self.L = []
+        self.gpu_out = []
         for i in range(self.R):
             self.step(i)
             L = self.alen.cpu().numpy().astype(np.int64)
             self.L.append(L)
+            self.gpu_out.append((self.acc.cpu().numpy().astype(np.int64), L))
             D, V = self.D, self.V
             rows = np.where(L < D, 8 * V, 4 * V)
             probes = 2 * PROBE_GRANULE * np.minimum(L + 1, D)
             per.append(int(rows.sum() + probes.sum() + self.B * (8 * D + 24)))
         return float(np.mean(per))
+
+    def oracle_call(self, r):
+        import oracle
+        h = self.host
+        return oracle.chain_reject(h["draft_probs"], h["draft_ids"], h["target_probs"], h["seed"],
+                                   self.reps[r]["off_host"])
 
     def extra(self):
         L = np.concatenate(self.L)
@@ -179,20 +280,25 @@ class ChainWorkload:
                 "input": "float32 target/draft probabilities", "replicas": self.R}
 
     def cpu_baseline(self, seconds):
-        import oracle
-        h = self.host
+        """The oracle on whole batches, replicas rotating, for ``seconds``; each replica's first pass is
+        also compared with the GPU's outputs of that replica (timed all the same: the comparison is a
+        few ms against ~0.1 s of oracle work per batch)."""
+        par = ParityCount()
         rows, t0, passes = 0, time.perf_counter(), 0
         while True:
-            off = self.reps[passes % self.R]["off_host"]
-            oracle.chain_reject(h["draft_probs"], h["draft_ids"], h["target_probs"], h["seed"], off)
+            r = passes % self.R
+            ref = self.oracle_call(r)
+            if passes < self.R:
+                par.add(*self.gpu_out[r], ref)
             rows += self.rows
             passes += 1
             el = time.perf_counter() - t0
-            if el >= seconds:
+            if el >= seconds and passes >= self.R:
                 break
-        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
-                          f"{el:.1f}s single-threaded numpy"}
+        self.parity = par.report()
+        return dict({"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                     "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
+                               f"{el:.1f}s single-threaded numpy"}, **cpu_info())
 
 
 class TargetOnlyWorkload(ChainWorkload):
@@ -208,10 +314,12 @@ class TargetOnlyWorkload(ChainWorkload):
         """Per request: one target line per probed position, one target row (p_L or the bonus row p_D)."""
         per = []
         self.L = []
+        self.gpu_out = []
         for i in range(self.R):
             self.step(i)
             L = self.alen.cpu().numpy().astype(np.int64)
             self.L.append(L)
+            self.gpu_out.append((self.acc.cpu().numpy().astype(np.int64), L))
             D, V = self.D, self.V
             probes = PROBE_GRANULE * np.minimum(L + 1, D)
             per.append(int(4 * V * self.B + probes.sum() + self.B * (8 * D + 24)))
@@ -222,21 +330,10 @@ class TargetOnlyWorkload(ChainWorkload):
         c["input"] = "float32 target probabilities, draft ids only (no draft probabilities)"
         return c
 
-    def cpu_baseline(self, seconds):
+    def oracle_call(self, r):
         import oracle
         h = self.host
-        rows, t0, passes = 0, time.perf_counter(), 0
-        while True:
-            off = self.reps[passes % self.R]["off_host"]
-            oracle.chain_reject(None, h["draft_ids"], h["target_probs"], h["seed"], off)
-            rows += self.rows
-            passes += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
-                          f"{el:.1f}s single-threaded numpy"}
+        return oracle.chain_reject(None, h["draft_ids"], h["target_probs"], h["seed"], self.reps[r]["off_host"])
 
 
 class RaggedWorkload:
@@ -279,11 +376,13 @@ class RaggedWorkload:
         per = []
         self.L = []
         d = self.host["verify_lens"] - 1
+        self.gpu_out = []
         for i in range(self.R):
             self.step(i)
             L = self.alen.cpu().numpy().astype(np.int64)
             tok = self.acc.cpu().numpy()
             self.L.append(L)
+            self.gpu_out.append((tok.astype(np.int64), L))
             D, V = self.D, self.V
             at_d = tok[np.arange(self.B), np.minimum(L, D)]
             rows = np.where(L < d, 8 * V, np.where((d < D) & (at_d == 0), 0, 4 * V))
@@ -301,22 +400,13 @@ class RaggedWorkload:
                 "verified_rows": self.rows, "input": "float32 packed target rows, per-request verify lengths "
                 "U{1..6}, float32 draft probabilities", "replicas": self.R}
 
-    def cpu_baseline(self, seconds):
+    def oracle_call(self, r):
         import oracle
         h = self.host
-        rows, t0, passes = 0, time.perf_counter(), 0
-        while True:
-            off = self.reps[passes % self.R]["off_host"]
-            oracle.chain_reject_ragged(h["draft_probs"], h["draft_ids"], h["target_rows"], h["qo_indptr"], h["seed"],
-                                       off)
-            rows += self.rows
-            passes += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                "sample": f"{passes} full batches of {self.B} requests (replica offsets rotating), "
-                          f"{el:.1f}s single-threaded numpy"}
+        return oracle.chain_reject_ragged(h["draft_probs"], h["draft_ids"], h["target_rows"], h["qo_indptr"],
+                                          h["seed"], self.reps[r]["off_host"])
+
+    cpu_baseline = ChainWorkload.cpu_baseline
 
 
 class RaggedD2tWorkload(RaggedWorkload):
@@ -359,11 +449,13 @@ class RaggedD2tWorkload(RaggedWorkload):
         per = []
         self.L = []
         d = self.host["verify_lens"] - 1
+        self.gpu_out = []
         for i in range(self.R):
             self.step(i)
             L = self.alen.cpu().numpy().astype(np.int64)
             tok = self.acc.cpu().numpy()
             self.L.append(L)
+            self.gpu_out.append((tok.astype(np.int64), L))
             D, V, Vd = self.D, self.V, self.Vd
             at_d = tok[np.arange(self.B), np.minimum(L, D)]
             rows = np.where(L < d, 4 * V + 4 * Vd, np.where((d < D) & (at_d == 0), 0, 4 * V))
@@ -377,22 +469,12 @@ class RaggedD2tWorkload(RaggedWorkload):
                       "32000-entry draft vocabulary read through the inverse d2t table")
         return c
 
-    def cpu_baseline(self, seconds):
+    def oracle_call(self, r):
         import oracle
         h = self.host
-        rows, t0, passes = 0, time.perf_counter(), 0
-        while True:
-            off = self.reps[passes % self.R]["off_host"]
-            q_full = oracle.d2t_expand(h["draft_probs_d"], h["d2t"], self.V)
-            oracle.chain_reject_ragged(q_full, h["draft_ids"], h["target_rows"], h["qo_indptr"], h["seed"], off)
-            rows += self.rows
-            passes += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                "sample": f"{passes} full batches of {self.B} requests (placement + ragged verify), "
-                          f"{el:.1f}s single-threaded numpy"}
+        q_full = oracle.d2t_expand(h["draft_probs_d"], h["d2t"], self.V)
+        return oracle.chain_reject_ragged(q_full, h["draft_ids"], h["target_rows"], h["qo_indptr"], h["seed"],
+                                          self.reps[r]["off_host"])
 
 
 class DraftVocabWorkload:
@@ -647,12 +729,15 @@ class TopkToppWorkload:
 
 
 class MixedWorkload:
-    """B=1024 D=7 V=129280 bf16 logits, 256 requests per mode, each mode through req_index."""
+    """B=1024 D=7 V=129280 bf16 logits, 256 requests per mode, each mode through req_index.  R = 4
+    replicas (logits, draft rows and probability buffers at distinct addresses, Philox offsets
+    4096 r apart) rotate so that no call finds the previous call's rows in the Infinity Cache."""
     name = "mixed"
     kernel = "softmax_renorm_rr_kernel"
     sources = ("softmax_renorm.hip", "sv_softmax.hpp", "sv_argmax.hpp", "sv_common.hpp")
     counters = "softmax_renorm_mixed_counters.txt"
     dtype = "bf16"
+    needs_probs = True
 
     def __init__(self, dev, replicas):
         from workloads import MODE_GREEDY, MODE_TEMPERATURE, MODE_TOPK, MODE_TOPP, make_config
@@ -665,15 +750,19 @@ class MixedWorkload:
         self.host = h
         self.B, self.D, self.V = h["B"], h["D"], h["V"]
         N = self.D + 1
-        self.R = 1
-        self.z = _bf16(h["logits"], dev)
-        self.q = _t(h["draft_probs"], dev)
+        self.R = replicas or 4
         self.x = _t(h["draft_ids"], dev)
         self.T = _t(h["temperature"], dev)
         self.k = _t(h["top_k"], dev)
         self.p = _t(h["top_p"], dev)
         self.seed = _t(h["seed"], dev)
-        self.off = _t(h["offset"], dev)
+        self.reps = []
+        for r in range(self.R):
+            off = (h["offset"] + np.uint64(4096 * r)).astype(np.uint64)
+            rep = dict(z=_bf16(h["logits"], dev), q=_t(h["draft_probs"], dev), off=_t(off, dev), off_host=off)
+            if self.needs_probs:
+                rep["probs"] = torch.zeros((self.B, N, self.V), dtype=torch.float32, device=dev)
+            self.reps.append(rep)
         modes = h["modes"]
         self.idx_host = {m: np.nonzero(modes == m)[0].astype(np.int32) for m in range(4)}
         self.greedy_idx = _t(self.idx_host[MODE_GREEDY], dev)
@@ -681,7 +770,6 @@ class MixedWorkload:
         filt = np.concatenate([self.idx_host[MODE_TOPK], self.idx_host[MODE_TOPP]]).astype(np.int32)
         self.filt_host = filt
         self.filt_idx = _t(filt, dev)
-        self.probs = torch.zeros((self.B, N, self.V), dtype=torch.float32, device=dev)
         self.acc = torch.empty((self.B, N), dtype=torch.int32, device=dev)
         self.alen = torch.empty((self.B,), dtype=torch.int32, device=dev)
         self.out = {"accepted_tokens": self.acc, "accept_length": self.alen}
@@ -690,17 +778,21 @@ class MixedWorkload:
                       "softmax_renorm": self.softmax, "chain_reject": self.chain}
 
     def greedy(self, i=0):
-        self.sv.greedy_verify(self.z, self.x, req_index=self.greedy_idx, predict=False, accept_index=False,
+        r = self.reps[i % self.R]
+        self.sv.greedy_verify(r["z"], self.x, req_index=self.greedy_idx, predict=False, accept_index=False,
                               out=self.out)
 
     def gumbel(self, i=0):
-        self.sv.gumbel_sample(self.z, self.T, self.x, self.seed, self.off, req_index=self.temp_idx, out=self.out)
+        r = self.reps[i % self.R]
+        self.sv.gumbel_sample(r["z"], self.T, self.x, self.seed, r["off"], req_index=self.temp_idx, out=self.out)
 
     def softmax(self, i=0):
-        self.sv.softmax_renorm(self.z, self.T, self.k, self.p, req_index=self.filt_idx, out=self.probs)
+        r = self.reps[i % self.R]
+        self.sv.softmax_renorm(r["z"], self.T, self.k, self.p, req_index=self.filt_idx, out=r["probs"])
 
     def chain(self, i=0):
-        self.sv.chain_reject(self.q, self.x, self.probs, self.seed, self.off, req_index=self.filt_idx,
+        r = self.reps[i % self.R]
+        self.sv.chain_reject(r["q"], self.x, r["probs"], self.seed, r["off"], req_index=self.filt_idx,
                              out=(self.acc, self.alen))
 
     def step(self, i):
@@ -709,27 +801,36 @@ class MixedWorkload:
         self.softmax(i)
         self.chain(i)
 
+    def _lengths(self):
+        """Realised accept lengths of every replica (one step each)."""
+        Ls = []
+        for i in range(self.R):
+            self.step(i)
+            Ls.append(self.alen.cpu().numpy().astype(np.int64))
+        self.L = np.concatenate(Ls)
+        return Ls
+
     def algorithmic_bytes(self):
         from workloads import MODE_GREEDY, MODE_TEMPERATURE
-        self.step(0)
-        L = self.alen.cpu().numpy().astype(np.int64)
-        self.L = L
         D, V, N = self.D, self.V, self.D + 1
         g = self.idx_host[MODE_GREEDY]
         t = self.idx_host[MODE_TEMPERATURE]
         f = self.filt_host
-        self.bytes_by_call = {
-            "greedy_verify": float(((L[g] + 1) * V * 2).sum()),
-            "gumbel_sample": float(((L[t] + 1) * V * 2).sum()),
-            "softmax_renorm": float(f.size * N * V * (2 + 4)),
-            "chain_reject": float((np.where(L[f] < D, 8 * V, 4 * V) + 2 * PROBE_GRANULE * np.minimum(L[f] + 1, D)).sum()),
-        }
+        by = {"greedy_verify": [], "gumbel_sample": [], "softmax_renorm": [], "chain_reject": []}
+        for L in self._lengths():
+            by["greedy_verify"].append(((L[g] + 1) * V * 2).sum())
+            by["gumbel_sample"].append(((L[t] + 1) * V * 2).sum())
+            by["softmax_renorm"].append(f.size * N * V * (2 + 4))
+            by["chain_reject"].append((np.where(L[f] < D, 8 * V, 4 * V)
+                                       + 2 * PROBE_GRANULE * np.minimum(L[f] + 1, D)).sum())
+        self.bytes_by_call = {k: float(np.mean(v)) for k, v in by.items()}
         return self.bytes_by_call["softmax_renorm"]
 
     def extra(self):
         from workloads import MODE_GREEDY, MODE_TEMPERATURE, MODE_TOPK, MODE_TOPP
+        L = self.L.reshape(-1, self.B)
         return {"mean_accept_length_by_mode": {
-            name: round(float(self.L[self.idx_host[m]].mean()), 4)
+            name: round(float(L[:, self.idx_host[m]].mean()), 4)
             for m, name in ((MODE_GREEDY, "greedy"), (MODE_TEMPERATURE, "temperature"), (MODE_TOPK, "top_k"),
                             (MODE_TOPP, "top_p"))}}
 
@@ -773,13 +874,15 @@ class MixedFusedWorkload(MixedWorkload):
     kernel = "verify_fused_kernel"
     sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_common.hpp")
     counters = "verify_fused_mixed_counters.txt"
+    needs_probs = False
 
     def __init__(self, dev, replicas):
         super().__init__(dev, replicas)
         self.calls = {"greedy_verify": self.greedy, "gumbel_sample": self.gumbel, "verify_fused": self.fused}
 
     def fused(self, i=0):
-        self.sv.verify_fused(self.z, self.T, self.q, self.x, self.seed, self.off, top_k=self.k, top_p=self.p,
+        r = self.reps[i % self.R]
+        self.sv.verify_fused(r["z"], self.T, r["q"], self.x, self.seed, r["off"], top_k=self.k, top_p=self.p,
                              req_index=self.filt_idx, out=(self.acc, self.alen))
 
     def step(self, i):
@@ -789,20 +892,18 @@ class MixedFusedWorkload(MixedWorkload):
 
     def algorithmic_bytes(self):
         from workloads import MODE_GREEDY, MODE_TEMPERATURE
-        self.step(0)
-        L = self.alen.cpu().numpy().astype(np.int64)
-        self.L = L
         D, V = self.D, self.V
         g = self.idx_host[MODE_GREEDY]
         t = self.idx_host[MODE_TEMPERATURE]
         f = self.filt_host
+        by = {"greedy_verify": [], "gumbel_sample": [], "verify_fused": []}
         # logit rows 0..L, the draft row q_L on a rejection, q at the ids probed
-        self.bytes_by_call = {
-            "greedy_verify": float(((L[g] + 1) * V * 2).sum()),
-            "gumbel_sample": float(((L[t] + 1) * V * 2).sum()),
-            "verify_fused": float(((L[f] + 1) * V * 2 + np.where(L[f] < D, 4 * V, 0)
-                                   + PROBE_GRANULE * np.minimum(L[f] + 1, D)).sum()),
-        }
+        for L in self._lengths():
+            by["greedy_verify"].append(((L[g] + 1) * V * 2).sum())
+            by["gumbel_sample"].append(((L[t] + 1) * V * 2).sum())
+            by["verify_fused"].append(((L[f] + 1) * V * 2 + np.where(L[f] < D, 4 * V, 0)
+                                       + PROBE_GRANULE * np.minimum(L[f] + 1, D)).sum())
+        self.bytes_by_call = {k: float(np.mean(v)) for k, v in by.items()}
         return self.bytes_by_call["verify_fused"]
 
 
@@ -812,47 +913,36 @@ WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorklo
                                  MixedFusedWorkload)}
 
 
-def stock_reduction_read(dev):
-    """Read bandwidth of a stock framework reduction on this GPU (torch's sum over 1 GiB of float32, four
-    buffers rotating): a reference point beside the roofline, not a peak and not a library kernel."""
-    import torch
-    bufs = [torch.ones(1 << 28, dtype=torch.float32, device=dev) for _ in range(4)]
-    for b in bufs:
-        b.sum()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 20
-    s.record()
-    for i in range(n):
-        bufs[i % 4].sum()
-    e.record()
-    torch.cuda.synchronize()
-    gbs = (4 << 28) * n / (s.elapsed_time(e) * 1e-3) / 1e9
-    del bufs
-    torch.cuda.empty_cache()
-    return gbs
+def _spread(us):
+    us = np.asarray(us)
+    return {"p10_us": round(float(np.percentile(us, 10)), 2), "median_us": round(float(np.median(us)), 2),
+            "p90_us": round(float(np.percentile(us, 90)), 2)}
 
 
-def per_call_times(wl, steps):
-    """Average time of each call type of a multi-call step (each timed alone)."""
+def timed_calls(fn, steps, stream):
+    """Per-call times (us) of `steps` calls, one HIP event pair per call on `stream`."""
     import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+
+
+def per_call_times(wl, steps, stream):
+    """Time of each call type of a multi-call step, each call type timed alone with replicas rotating."""
     out = {}
     for name, fn in getattr(wl, "calls", {}).items():
         for i in range(3):
             fn(i)
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for i in range(steps):
-            fn(i)
-        e.record()
-        torch.cuda.synchronize()
-        us = s.elapsed_time(e) / steps * 1e3
-        entry = {"us": round(us, 2)}
+        us = timed_calls(fn, steps, stream)
+        entry = {"us": round(float(np.mean(us)), 2), **_spread(us)}
         b = getattr(wl, "bytes_by_call", {}).get(name)
         if b is not None:
-            entry["algorithmic_GBps"] = round(b / (us * 1e-6) / 1e9, 1)
-            entry["frac_of_peak"] = round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+            entry["algorithmic_GBps"] = round(b / (entry["us"] * 1e-6) / 1e9, 1)
+            entry["frac_of_peak"] = round(b / (entry["us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
         out[name] = entry
     return out
 
@@ -887,15 +977,22 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     log(f"timed {args.steps} steps: {ms * 1e3:.2f} us/step")
+    spread = _spread(timed_calls(wl.step, args.steps, stream))
+    log(f"per-step spread: {spread}")
     rows_per_s = wl.rows / (ms * 1e-3)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
-    calls = per_call_times(wl, max(5, args.steps // 4)) if hasattr(wl, "calls") else None
+    calls = per_call_times(wl, max(5, args.steps // 4), stream) if hasattr(wl, "calls") else None
     digest = _source_digest(*wl.sources)
     traffic = load_traffic(wl.counters, digest)
+    log("measuring the read-stream ceiling")
+    peak_read, peak_cfg = stream_peak(dev)
+    log(f"read stream: {peak_read:.0f} GB/s at {peak_cfg}")
     cpu = None
     if args.cpu_seconds > 0:
         log("timing the CPU oracle baseline")
         cpu = wl.cpu_baseline(args.cpu_seconds)
+        for k, v in cpu_info().items():
+            cpu.setdefault(k, v)
     out = {
         "metric": METRIC,
         "value": rows_per_s,
@@ -913,6 +1010,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": wl.kernel, "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes, "kernel_source_digest": digest},
+        "per_step": spread,
         "cpu_baseline": cpu,
     }
     if calls:
@@ -922,9 +1020,11 @@ def main():
             us = dom["us"]
             out["roofline"]["achieved"] = alg_bytes / (us * 1e-6) / 1e9
             out["roofline"]["frac"] = out["roofline"]["achieved"] / PEAK_HBM_GBS
-    sread = stock_reduction_read(dev)
-    out["roofline"]["torch_sum_read_GBps"] = sread
-    out["roofline"]["achieved_vs_torch_sum_read"] = out["roofline"]["achieved"] / sread
+    out["roofline"]["measured_read_stream_GBps"] = round(peak_read, 1)
+    out["roofline"]["read_stream_config"] = peak_cfg
+    out["roofline"]["frac_of_stream_peak"] = out["roofline"]["achieved"] / peak_read
+    if getattr(wl, "parity", None) is not None:
+        out["parity"] = wl.parity
     out.update(wl.extra())
     print(json.dumps(out), flush=True)
 

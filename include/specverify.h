@@ -31,11 +31,9 @@
  *   rejection_sampling_one_model docstring).
  * - stream is a hipStream_t passed as void*; NULL is the default stream.
  *   Calls are asynchronous; nothing is read back to the host.  The library
- *   never synchronises.  specverify_softmax_renorm, specverify_greedy_verify,
- *   specverify_gumbel_sample, specverify_verify_fused, specverify_sample,
- *   specverify_d2t_inverse and specverify_d2t_expand use no device memory
- *   besides their arguments; specverify_chain_reject and
- *   specverify_chain_reject_ragged keep a library-owned workspace (see there).
+ *   never synchronises and never allocates device memory: every call uses
+ *   only its arguments (chain rejection takes a caller-owned workspace when
+ *   a request's row is split over several workgroups; see there).
  * - Host-side validation runs before any HIP call.  Return codes:
  *   SPECVERIFY_OK, SPECVERIFY_INVALID_ARGUMENT (nothing launched),
  *   SPECVERIFY_UNSUPPORTED (current device is not gfx950),
@@ -66,7 +64,7 @@ extern "C" {
 
 #define SPECVERIFY_MAX_DRAFT 16
 #define SPECVERIFY_RNG_SLOT_SPAN 32
-#define SPECVERIFY_VERSION 100
+#define SPECVERIFY_VERSION 200
 
 /*
  * Temperature softmax followed by top-k then top-p renormalisation.
@@ -125,22 +123,45 @@ int specverify_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t 
  * u_i < p_i(x_i), and the correction is drawn from p_i with x_i weighing
  * max(0, p_i(x_i) - 1).
  *
- * Memory: when a request's row is split over several workgroups (small
- * batches), they hand their partial sums over through a workspace the
- * library owns, one per (device, stream): one 32-bit counter per request and
- * one double per 1024 vocabulary entries per request.  It is allocated with
- * hipMalloc on the first call that needs more than the current one (grown
- * geometrically; replaced buffers are kept until the process ends) and its
- * counters are zeroed once with hipMemsetAsync on the call's stream; every
- * kernel leaves them at zero.  Calls on one stream use it in stream order;
- * calls on different streams use different workspaces.  A failed allocation
- * returns SPECVERIFY_HIP_ERROR with nothing launched.
+ * workspace, workspace_bytes
+ *                 caller-owned device memory, or NULL when
+ *                 specverify_chain_workspace_bytes(n_req, V) is 0 (then
+ *                 workspace_bytes is ignored).  Small batches split each
+ *                 request's row over several workgroups, which hand their
+ *                 partial sums over through it: one 32-bit counter per request
+ *                 (padded to 256 bytes), then one double per 1024 vocabulary
+ *                 entries per request.  8-byte aligned, at least the queried
+ *                 size.  It must be all zero when a call starts, and every
+ *                 call leaves the bytes it used zero, so zero a new
+ *                 workspace once (any fill) and reuse it for any later chain
+ *                 call it is large enough for; calls that share a workspace
+ *                 must not run concurrently (issue them on one stream).  A missing,
+ *                 short or misaligned workspace returns
+ *                 SPECVERIFY_INVALID_ARGUMENT with nothing launched.  The
+ *                 pages ask for the same: "tokenspeed flashinfer.py",
+ *                 FlashInferSamplingBackend.__init__, keeps persistent buffers
+ *                 and allocates nothing per step; "TensorRT-LLM interface.py"
+ *                 checks its rejection buffers on the host so the step can be
+ *                 captured in a graph.
  */
 int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids,
                             const float* target_probs, const uint64_t* seed,
                             const uint64_t* offset, int64_t B, int64_t D, int64_t V,
                             const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
-                            int32_t* accept_length, void* stream);
+                            int32_t* accept_length, void* workspace, int64_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Workspace size of specverify_chain_reject / specverify_chain_reject_ragged.
+ *
+ * *bytes = the workspace a call with n_req processed requests over V
+ * vocabulary entries needs: 0 when every request's row is handled by one
+ * workgroup that keeps its chunk sums on chip (n_req >= 256 and
+ * V <= 262144), else the size described at specverify_chain_reject.
+ * Depends on (n_req, V) only.  Host-only: touches no device.
+ * n_req >= 0, 1 <= V < 2^31, bytes non-NULL; else SPECVERIFY_INVALID_ARGUMENT.
+ */
+int specverify_chain_workspace_bytes(int64_t n_req, int64_t V, int64_t* bytes);
 
 /*
  * Ragged chain rejection: each request verifies its own number of positions.
@@ -176,33 +197,37 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids,
  * padding).  When len_b = D+1 the request is verified exactly as by
  * specverify_chain_reject.  A request whose length is outside [1, D+1] or
  * whose rows fall outside [0, n_rows) gets accept_length -1 and all tokens
- * -1; nothing of it is read.  Memory: the workspace of specverify_chain_reject.
+ * -1; nothing of it is read.  workspace, workspace_bytes: as in
+ * specverify_chain_reject (sized by specverify_chain_workspace_bytes(n_req, V)).
  */
 int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* t2d, int64_t Vd,
                                    const int32_t* draft_ids, const float* target_probs,
                                    const int32_t* qo_indptr, int64_t n_rows, const uint64_t* seed,
                                    const uint64_t* offset, int64_t B, int64_t D, int64_t V,
                                    const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
-                                   int32_t* accept_length, void* stream);
+                                   int32_t* accept_length, void* workspace, int64_t workspace_bytes,
+                                   void* stream);
 
 /*
  * Draft -> target vocabulary placement of draft distributions.
  *
  * Passage: "TensorRT-LLM _torch/speculative/interface.py", one-model sampler
- * (draft vocabulary smaller than the target's): target_indices =
- * (source_indices + d2t) % vocab_size, computed once and kept in the
- * speculative metadata, and the draft probabilities are scattered into a
- * zero-filled full_draft_probs; without a d2t table they fill the first Vd
- * entries.  The result is the draft_probs argument of specverify_chain_reject
+ * (draft vocabulary smaller than the target's): draft entry s belongs to
+ * target entry (s + d2t[s]) mod V, an index list computed once and kept in
+ * the speculative metadata, and the draft probabilities are scattered into a
+ * zero-filled full-vocabulary row; without a d2t table they fill the first
+ * Vd entries.  The result is the draft_probs argument of specverify_chain_reject
  * / specverify_chain_reject_ragged (draft ids are target-vocabulary ids).
  *
  * specverify_d2t_inverse builds, once per table, the inverse map
- *   d2t  [Vd] int64 offsets or NULL (then Vd <= V); draft entry s belongs to
- *        target entry (s + d2t[s]) mod V, a floor modulus (negative offsets wrap)
+ *   d2t  [Vd] int64 offsets or NULL; draft entry s belongs to target entry
+ *        (s + d2t[s]) mod V, a floor modulus (negative offsets wrap)
  *   t2d  [V] int32 output: the draft entry of each target entry, -1 for none
- * The mapping must send distinct draft entries to distinct target entries,
- * as the page's scatter assumes; otherwise which entry a shared target keeps
- * is unspecified.
+ * Vd <= V (a larger draft vocabulary cannot map one-to-one; INVALID_ARGUMENT).
+ * The page's scatter assumes distinct draft entries land on distinct
+ * targets; when several share a target, the highest-numbered draft entry is
+ * the one kept (what a scatter in ascending draft order leaves), independent
+ * of thread timing.
  *
  * specverify_d2t_expand places the rows (a gather: every output row is
  * written once, in order)

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = sv.lib()
-    assert sv.version() == 100
+    assert sv.version() == 200
     assert L.specverify_status_string(0) == b"SPECVERIFY_OK"
     assert L.specverify_status_string(1) == b"SPECVERIFY_INVALID_ARGUMENT"
     assert L.specverify_status_string(2) == b"SPECVERIFY_UNSUPPORTED"
@@ -41,10 +41,10 @@ def test_version_and_status_strings():
 
 
 def _chain(**kw):
-    a = dict(q=P, x=P, p=P, seed=P, off=P, B=4, D=3, V=100, req=None, n=4, acc=P, alen=P)
+    a = dict(q=P, x=P, p=P, seed=P, off=P, B=4, D=3, V=100, req=None, n=4, acc=P, alen=P, ws=None, wsb=0)
     a.update(kw)
     return sv.lib().specverify_chain_reject(a["q"], a["x"], a["p"], a["seed"], a["off"], a["B"], a["D"], a["V"],
-                                            a["req"], a["n"], a["acc"], a["alen"], None)
+                                            a["req"], a["n"], a["acc"], a["alen"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,msg", [
@@ -80,6 +80,42 @@ def test_chain_reject_zero_draft_allows_null_draft_buffers_and_empty_batch_is_no
     # D = 0: draft buffers may be NULL (the failure is then a missing target buffer)
     assert _chain(D=0, q=None, x=None, p=None) == sv.INVALID_ARGUMENT
     assert "target_probs" in sv.lib().specverify_last_error().decode()
+
+
+def _ws_bytes(n_req, V):
+    out = ctypes.c_int64(-1)
+    st = sv.lib().specverify_chain_workspace_bytes(n_req, V, ctypes.byref(out))
+    return st, out.value
+
+
+def test_chain_workspace_query():
+    # one workgroup per request with chunk sums on chip: no workspace
+    assert _ws_bytes(256, 128256) == (sv.OK, 0)
+    assert _ws_bytes(1024, 4096) == (sv.OK, 0)
+    assert _ws_bytes(0, 100) == (sv.OK, 0)
+    # small batches split rows: 256 bytes of counters, then one double per 1024 entries per request
+    assert _ws_bytes(64, 32000) == (sv.OK, 256 + 64 * 32 * 8)
+    assert _ws_bytes(65, 32000) == (sv.OK, 512 + 65 * 32 * 8)
+    # rows longer than 262144 entries split even for large batches
+    assert _ws_bytes(256, 262144) == (sv.OK, 0)
+    assert _ws_bytes(256, 262145)[1] == 1024 + 256 * 257 * 8
+    assert _ws_bytes(-1, 10)[0] == sv.INVALID_ARGUMENT
+    assert _ws_bytes(4, 0)[0] == sv.INVALID_ARGUMENT
+    assert sv.lib().specverify_chain_workspace_bytes(4, 10, None) == sv.INVALID_ARGUMENT
+    assert sv.chain_workspace_bytes(40, 60000) == 256 + 40 * 59 * 8
+
+
+def test_chain_reject_workspace_validation():
+    # B = 4 over V = 100000 splits each row: the call needs the caller's workspace
+    assert _chain(V=100000) == sv.INVALID_ARGUMENT
+    assert "workspace is NULL" in sv.lib().specverify_last_error().decode()
+    need = _ws_bytes(4, 100000)[1]
+    assert _chain(V=100000, ws=P, wsb=need - 8) == sv.INVALID_ARGUMENT
+    assert "needs %d" % need in sv.lib().specverify_last_error().decode()
+    assert _chain(V=100000, ws=ctypes.c_void_p(0x1004), wsb=need) == sv.INVALID_ARGUMENT
+    assert "8-byte aligned" in sv.lib().specverify_last_error().decode()
+    # a large batch needs none, and the empty batch never looks at it
+    assert _chain(B=0, n=0, ws=None) == sv.OK
 
 
 def test_greedy_and_gumbel_and_softmax_invalid_arguments():
@@ -121,27 +157,38 @@ def test_verify_fused_invalid_arguments():
 
 def test_chain_reject_ragged_invalid_arguments():
     L = sv.lib()
-    # (q, t2d, Vd, x, p, qo_indptr, n_rows, seed, offset, B, D, V, req_index, n_req, acc, alen, stream)
-    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, None, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    # (q, t2d, Vd, x, p, qo_indptr, n_rows, seed, offset, B, D, V, req_index, n_req, acc, alen, workspace,
+    #  workspace_bytes, stream)
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, None, 8, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "qo_indptr" in L.specverify_last_error().decode()
-    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, P, -1, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, P, -1, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "n_rows" in L.specverify_last_error().decode()
-    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, P, 8, P, P, 4, 17, 10, None, 4, P, P, None) == 1
-    assert L.specverify_chain_reject_ragged(P, None, 0, None, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, P, 8, P, P, 4, 17, 10, None, 4, P, P, None, 0, None) == 1
+    assert L.specverify_chain_reject_ragged(P, None, 0, None, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "draft_ids" in L.specverify_last_error().decode()
-    assert L.specverify_chain_reject_ragged(P, None, 0, P, None, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
-    assert L.specverify_chain_reject_ragged(None, P, 5, P, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, None, P, 8, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
+    assert L.specverify_chain_reject_ragged(None, P, 5, P, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "t2d needs draft_probs" in L.specverify_last_error().decode()
-    assert L.specverify_chain_reject_ragged(P, P, 0, P, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_chain_reject_ragged(P, P, 0, P, P, P, 8, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "Vd=0" in L.specverify_last_error().decode()
     assert L.specverify_chain_reject_ragged(None, None, 0, None, None, None, 0, None, None, 4, 3, 10, P, 0, None,
-                                            None, None) == 0
+                                            None, None, 0, None) == 0
+    # a split launch needs the caller's workspace: missing, short or misaligned is an argument error
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, P, 8, P, P, 4, 3, 100000, None, 4, P, P, None, 0,
+                                            None) == 1
+    assert "workspace is NULL" in L.specverify_last_error().decode()
+    assert L.specverify_chain_reject_ragged(P, None, 0, P, P, P, 8, P, P, 4, 3, 100000, None, 4, P, P, P, 8,
+                                            None) == 1
+    assert "needs" in L.specverify_last_error().decode()
 
 
 def test_d2t_invalid_arguments():
     L = sv.lib()
     # inverse: (d2t, Vd, V, t2d, stream)
     assert L.specverify_d2t_inverse(None, 12, 10, P, None) == 1
+    assert "Vd=12" in L.specverify_last_error().decode()
+    # a table cannot map more draft entries than the target has one-to-one
+    assert L.specverify_d2t_inverse(P, 12, 10, P, None) == 1
     assert "Vd=12" in L.specverify_last_error().decode()
     assert L.specverify_d2t_inverse(P, 0, 10, P, None) == 1
     assert L.specverify_d2t_inverse(P, 8, 0, P, None) == 1

@@ -286,6 +286,70 @@ def test_chain_reject_target_only(sv):
     log(f"chain target-only flagged requests: {flagged}")
 
 
+def test_chain_workspace_reuse_and_zero_after_use(sv):
+    """One caller workspace serves split launches of different layouts (the
+    counter region of a later call overlaps where an earlier call kept
+    partial sums): every call leaves it all zero, and results match the
+    oracle.  Also the ragged call through the same workspace."""
+    torch = __import__("torch")
+    cases = ((10, 3, 60000), (100, 2, 20000), (7, 5, 100003), (200, 1, 40000), (40, 5, 60000))
+    ws = torch.zeros(max(sv.chain_workspace_bytes(B, V) for B, _, V in cases), dtype=torch.uint8, device="cuda")
+    for B, D, V in cases:
+        c = fuzz_case(1700 + B, B, D, V, "f32")
+        log(f"chain with a shared caller workspace: B={B} D={D} V={V} need={sv.chain_workspace_bytes(B, V)}")
+        ref = oracle.chain_reject(c["draft_probs"], c["draft_ids"], c["target_probs"], c["seed"], c["offset"])
+        acc, alen = sv.chain_reject(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]),
+                                    dev(c["seed"]), dev(c["offset"]), workspace=ws)
+        assert_chain_match(np_i(acc), np_i(alen), ref, range(B), ("shared workspace", B, V))
+        assert not bool((ws != 0).any().item()), ("workspace not zero after the call", B, V)
+        lens = np.random.default_rng(B).integers(1, D + 2, B)
+        rows, ind = _ragged_pack(c, lens)
+        refr = oracle.chain_reject_ragged(c["draft_probs"], c["draft_ids"], rows, ind, c["seed"], c["offset"])
+        acc, alen = sv.chain_reject_ragged(dev(c["draft_probs"]), dev(c["draft_ids"]), dev(rows), dev(ind),
+                                           dev(c["seed"]), dev(c["offset"]), workspace=ws)
+        assert_chain_match(np_i(acc), np_i(alen), refr, range(B), ("shared workspace ragged", B, V))
+        assert not bool((ws != 0).any().item()), ("workspace not zero after the ragged call", B, V)
+
+
+def test_chain_reject_graph_capture_and_replay(sv):
+    """Split-row chain rejection captured in a HIP graph with a caller
+    workspace (no allocation or memset inside the call): three replays,
+    with eager work and synchronisation between them, each equal to the
+    eager result."""
+    torch = __import__("torch")
+    B, D, V = 40, 5, 60000
+    c = fuzz_case(1777, B, D, V, "f32")
+    args = [dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["target_probs"]), dev(c["seed"]), dev(c["offset"])]
+    ws = sv.chain_workspace(B, V, "cuda")
+    assert ws is not None
+    log("chain graph capture: B=40 D=5 V=60000 (split rows), eager reference")
+    acc0, len0 = sv.chain_reject(*args, workspace=ws)
+    eager = (np_i(acc0), np_i(len0))
+    acc = torch.empty((B, D + 1), dtype=torch.int32, device="cuda")
+    alen = torch.empty((B,), dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sv.chain_reject(*args, workspace=ws, out=(acc, alen))        # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sv.chain_reject(*args, workspace=ws, out=(acc, alen))
+    for r in range(3):
+        acc.fill_(-7)
+        alen.fill_(-7)
+        torch.cuda.synchronize()
+        log(f"chain graph replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np_i(acc), eager[0]) and np.array_equal(np_i(alen), eager[1]), r
+        assert not bool((ws != 0).any().item())
+        # eager work between replays, on the same workspace
+        a2, l2 = sv.chain_reject(*args, workspace=ws)
+        assert np.array_equal(np_i(a2), eager[0])
+
+
 def _ragged_pack(c, lens):
     """Packed target rows and qo_indptr from a dense fuzz case and per-request lengths."""
     p = c["target_probs"]
@@ -386,6 +450,25 @@ def test_d2t_expand(sv):
     assert np.array_equal(out.cpu().numpy(), oracle.d2t_expand(q, d2t, V))
     f = flat.cpu().numpy()
     assert np.all(f[:3] == 7.0) and np.all(f[3 + rows * V:] == 7.0)
+
+
+def test_d2t_shared_targets(sv):
+    """A table whose draft entries share targets: the inverse table keeps the
+    highest-numbered draft entry per target (the oracle's in-order scatter),
+    on every launch, and the expansion matches the oracle's placement."""
+    rng = np.random.default_rng(1402)
+    for Vd, V in ((50, 60), (3000, 3000), (20000, 25000)):
+        tgt = rng.integers(0, V, Vd)
+        d2t = (tgt - np.arange(Vd)).astype(np.int64)
+        q = rng.random((4, Vd)).astype(np.float32)
+        log(f"d2t shared targets: Vd={Vd} V={V}")
+        want = np.full(V, -1, np.int64)
+        np.maximum.at(want, tgt, np.arange(Vd))
+        for rep in range(3):
+            t2d = sv.d2t_inverse(dev(d2t), Vd, V)
+            assert np.array_equal(np_i(t2d), want), (Vd, V, rep)
+        out = sv.d2t_expand(dev(q), t2d)
+        assert np.array_equal(out.cpu().numpy(), oracle.d2t_expand(q, d2t, V)), (Vd, V)
 
 
 def test_ragged_verify_with_reduced_draft_vocab(sv):

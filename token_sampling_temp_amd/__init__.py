@@ -10,9 +10,11 @@ a missing library raises.
 Functions mirror the C entry points:
 
 * ``softmax_renorm(logits, temperature, top_k=None, top_p=None, req_index=None)``
-* ``chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None)``
-* ``chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None)``:
-  per-request verify lengths over packed target rows
+* ``chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None, workspace=None)``
+* ``chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None,
+  workspace=None)``: per-request verify lengths over packed target rows
+* ``chain_workspace_bytes(n_req, V)`` and ``chain_workspace(n_req, V, device)``: the caller-owned
+  workspace the two chain calls need when rows are split over workgroups (small batches)
 * ``sample(logits, temperature, seed, offset, top_k=None, top_p=None, min_p=None, req_index=None)``:
   single-step sampling with the joint top-k/top-p filter and min-p
 * ``d2t_inverse(d2t, Vd, V)`` and ``d2t_expand(draft_probs, t2d)``: draft distributions over a
@@ -41,6 +43,7 @@ RNG_SLOT_SPAN = 32
 SYMBOLS = (
     "specverify_softmax_renorm",
     "specverify_chain_reject",
+    "specverify_chain_workspace_bytes",
     "specverify_chain_reject_ragged",
     "specverify_d2t_inverse",
     "specverify_d2t_expand",
@@ -76,16 +79,18 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     L.specverify_softmax_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp, vp]
-    L.specverify_chain_reject.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.specverify_chain_reject.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp]
+    L.specverify_chain_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_int64)]
     L.specverify_chain_reject_ragged.argtypes = [vp, vp, i64, vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, i64, vp,
-                                                 vp, vp]
+                                                 vp, vp, i64, vp]
     L.specverify_d2t_inverse.argtypes = [vp, i64, i64, vp, vp]
     L.specverify_d2t_expand.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
     L.specverify_sample.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, i64, vp, vp]
-    for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_chain_reject_ragged",
+    for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_chain_workspace_bytes",
+                 "specverify_chain_reject_ragged",
                  "specverify_d2t_inverse", "specverify_d2t_expand", "specverify_greedy_verify",
                  "specverify_gumbel_sample", "specverify_verify_fused", "specverify_sample"):
         getattr(L, name).restype = ctypes.c_int
@@ -158,6 +163,47 @@ def _u64(t, name, B, device):
     return t
 
 
+def chain_workspace_bytes(n_req, V) -> int:
+    """Bytes of workspace a chain call over n_req requests and V entries needs (0: none)."""
+    out = ctypes.c_int64(0)
+    _check("specverify_chain_workspace_bytes", lib().specverify_chain_workspace_bytes(int(n_req), int(V),
+                                                                                       ctypes.byref(out)))
+    return int(out.value)
+
+
+def chain_workspace(n_req, V, device):
+    """A zero-filled workspace for chain calls over n_req requests and V entries (None when none is
+    needed).  Every call leaves the bytes it used zero, so it can be reused by any later chain call
+    on the same stream that fits in it."""
+    torch = _torch()
+    n = chain_workspace_bytes(n_req, V)
+    if n == 0:
+        return None
+    return torch.zeros((n,), dtype=torch.uint8, device=device)
+
+
+# Workspaces made for callers that pass none, one per (device, stream), replaced by a larger one when a
+# call needs more.  A replaced tensor goes back to torch's stream-ordered caching allocator, so kernels
+# already queued on that stream finish with it before its memory is handed out again there.
+_workspaces = {}
+
+
+def _workspace(workspace, n_req, V, device):
+    torch = _torch()
+    n = chain_workspace_bytes(n_req, V)
+    if n == 0:
+        return None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,), device, 1)
+        return workspace, int(workspace.numel())
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < n:
+        ws = torch.zeros((n,), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws, int(ws.numel())
+
+
 # --------------------------------------------------------------------------- entry points
 def softmax_renorm(logits, temperature, top_k=None, top_p=None, req_index=None, out=None):
     """Temperature softmax then top-k then top-p renormalisation: [B, npos, V] -> float32 probs."""
@@ -187,10 +233,12 @@ def softmax_renorm(logits, temperature, top_k=None, top_p=None, req_index=None, 
     return out
 
 
-def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None, out=None):
+def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=None, out=None, workspace=None):
     """Chain rejection sampling; returns (accepted_tokens [B, D+1] int32, accept_length [B] int32).
 
-    ``draft_probs`` None is the target-only verify: each draft is a point mass at its id."""
+    ``draft_probs`` None is the target-only verify: each draft is a point mass at its id.
+    ``workspace``: a uint8 tensor from ``chain_workspace`` (zero-filled once, reused); when None and
+    the call needs one, a zero-filled tensor kept per (device, stream) is used."""
     torch = _torch()
     _need(target_probs, "target_probs", (torch.float32,), None, 3)
     dev = target_probs.device
@@ -211,9 +259,10 @@ def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=N
         alen = torch.empty((B,), dtype=torch.int32, device=dev)
     else:
         acc, alen = out
+    ws, ws_bytes = _workspace(workspace, n_req, V, dev)
     st = lib().specverify_chain_reject(
         _ptr(draft_probs), _ptr(draft_ids), _ptr(target_probs), _ptr(seed), _ptr(offset), B, D, V,
-        _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
+        _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _ptr(ws), ws_bytes, _stream_ptr(dev))
     _check("specverify_chain_reject", st)
     return acc, alen
 
@@ -256,7 +305,7 @@ def verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offse
 
 
 def chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, offset, req_index=None, out=None,
-                        t2d=None):
+                        t2d=None, workspace=None):
     """Ragged chain rejection over packed target rows [n_rows, V]; request b owns rows
     [qo_indptr[b], qo_indptr[b+1]).  Returns (accepted_tokens [B, D+1] int32,
     accept_length [B] int32); ``draft_probs`` None means point-mass drafts.  With ``t2d``
@@ -290,9 +339,11 @@ def chain_reject_ragged(draft_probs, draft_ids, target_probs, qo_indptr, seed, o
         alen = torch.empty((B,), dtype=torch.int32, device=dev)
     else:
         acc, alen = out
+    ws, ws_bytes = _workspace(workspace, n_req, V, dev)
     st = lib().specverify_chain_reject_ragged(
         _ptr(draft_probs), _ptr(t2d), Vd, _ptr(draft_ids), _ptr(target_probs), _ptr(qo_indptr), n_rows, _ptr(seed),
-        _ptr(offset), B, D, V, _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
+        _ptr(offset), B, D, V, _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _ptr(ws), ws_bytes,
+        _stream_ptr(dev))
     _check("specverify_chain_reject_ragged", st)
     return acc, alen
 

@@ -20,6 +20,9 @@ LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "chain_reject.hip", "greedy_verify.hip", "softmax_renorm.hip", "gumbel_sample.hip",
            "fused_verify.hip", "d2t_expand.hip"]
+# the benchmark's read-stream probe: a separate library, not part of the verification ABI
+PROBE_SOURCE = "stream_probe.hip"
+PROBE_PATH = os.path.join(HERE, "libsvprobe.so")
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [
@@ -52,20 +55,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every HIP source and link libspecverify.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every HIP source and link libspecverify.so (and the benchmark's libsvprobe.so);
+    returns the library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + [PROBE_SOURCE]
+    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB_PATH)
+    _link(objs[-1:], PROBE_PATH)
     if verbose:
-        print(f"built {LIB_PATH}", file=sys.stderr)
+        print(f"built {LIB_PATH} and {PROBE_PATH}", file=sys.stderr)
     return LIB_PATH
 
 

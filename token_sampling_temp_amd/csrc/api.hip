@@ -5,12 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <algorithm>
-#include <map>
-#include <mutex>
 #include <string>
-#include <utility>
-#include <vector>
 
 #include "specverify.h"
 #include "sv_launch.hpp"
@@ -98,50 +93,22 @@ int check_dtype(const char* fn, int dtype) {
         if (_s != SPECVERIFY_OK) return _s; \
     } while (0)
 
-// Chain-rejection workspace, one per (device, stream) so that calls on
-// different streams never share counters.  Allocated on first use and grown
-// geometrically; a replaced buffer is kept (a queued kernel may still use it)
-// until process exit.  The counter region is zeroed once; every kernel leaves
-// its counters at zero.
-struct ChainWorkspace {
-    char* ptr = nullptr;
-    int64_t cap_req = 0;         // counters available
-    int64_t cap_partial = 0;     // doubles available
-};
-std::mutex g_ws_mu;
-std::map<std::pair<int, void*>, ChainWorkspace> g_ws;
-std::vector<void*> g_ws_retired;
-
-int64_t counter_region(int64_t cap_req) { return ((cap_req * 4 + 255) / 256) * 256; }
-
-int chain_workspace(const char* fn, hipStream_t stream, int64_t n_req, int64_t V, uint32_t** counter,
-                    double** partial) {
-    const int64_t need_partial = n_req * sv::chain_partials_per_request(V);
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(SPECVERIFY_HIP_ERROR, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    ChainWorkspace& w = g_ws[{dev, static_cast<void*>(stream)}];
-    if (!w.ptr || n_req > w.cap_req || need_partial > w.cap_partial) {
-        const int64_t cap_req = std::max<int64_t>(n_req, 2 * w.cap_req);
-        const int64_t cap_partial = std::max<int64_t>(need_partial, 2 * w.cap_partial);
-        const size_t bytes = (size_t)(counter_region(cap_req) + cap_partial * 8);
-        void* ptr = nullptr;
-        e = hipMalloc(&ptr, bytes);
-        if (e != hipSuccess)
-            return fail(SPECVERIFY_HIP_ERROR, "%s: workspace hipMalloc(%zu): %s", fn, bytes, hipGetErrorString(e));
-        e = hipMemsetAsync(ptr, 0, (size_t)counter_region(cap_req), stream);
-        if (e != hipSuccess) {
-            (void)hipFree(ptr);
-            return fail(SPECVERIFY_HIP_ERROR, "%s: workspace hipMemsetAsync: %s", fn, hipGetErrorString(e));
-        }
-        if (w.ptr) g_ws_retired.push_back(w.ptr);
-        w.ptr = static_cast<char*>(ptr);
-        w.cap_req = cap_req;
-        w.cap_partial = cap_partial;
-    }
-    *counter = reinterpret_cast<uint32_t*>(w.ptr);
-    *partial = reinterpret_cast<double*>(w.ptr + counter_region(w.cap_req));
+// A chain call's workspace: what the launch needs for (n_req, V), present,
+// large enough and 8-byte aligned.  NULL is accepted when nothing is needed.
+int check_chain_workspace(const char* fn, int64_t n_req, int64_t V, const void* workspace,
+                          int64_t workspace_bytes) {
+    const int64_t need = sv::chain_workspace_bytes(n_req, V);
+    if (need == 0) return SPECVERIFY_OK;
+    if (!workspace)
+        return fail(SPECVERIFY_INVALID_ARGUMENT,
+                    "%s: n_req=%lld V=%lld splits rows over workgroups and needs a workspace of %lld bytes "
+                    "(specverify_chain_workspace_bytes); workspace is NULL",
+                    fn, (long long)n_req, (long long)V, (long long)need);
+    if (workspace_bytes < need)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace_bytes=%lld, n_req=%lld V=%lld needs %lld", fn,
+                    (long long)workspace_bytes, (long long)n_req, (long long)V, (long long)need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace must be 8-byte aligned", fn);
     return SPECVERIFY_OK;
 }
 
@@ -172,10 +139,23 @@ int specverify_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t 
                                                   n_req, probs_out, static_cast<hipStream_t>(stream)));
 }
 
+int specverify_chain_workspace_bytes(int64_t n_req, int64_t V, int64_t* bytes) {
+    const char* fn = "specverify_chain_workspace_bytes";
+    SV_REQUIRE(bytes, "bytes");
+    if (n_req < 0) return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: n_req=%lld must be >= 0", fn, (long long)n_req);
+    if (V < 1 || V > kMaxV)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: V=%lld must be in [1, 2^31)", fn, (long long)V);
+    if ((long double)n_req * (long double)V > 4.0e18L)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: size overflows", fn);
+    *bytes = sv::chain_workspace_bytes(n_req, V);
+    g_last_error.clear();
+    return SPECVERIFY_OK;
+}
+
 int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
                             const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D, int64_t V,
                             const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
-                            int32_t* accept_length, void* stream) {
+                            int32_t* accept_length, void* workspace, int64_t workspace_bytes, void* stream) {
     const char* fn = "specverify_chain_reject";
     SV_TRY(check_draft(fn, D));
     SV_TRY(check_sizes(fn, B, D + 1, V, req_index, n_req, 4));
@@ -186,20 +166,18 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids, 
     SV_REQUIRE(offset, "offset");
     SV_REQUIRE(accepted_tokens, "accepted_tokens");
     SV_REQUIRE(accept_length, "accept_length");
+    SV_TRY(check_chain_workspace(fn, n_req, V, workspace, workspace_bytes));
     SV_TRY(check_device());
-    uint32_t* counter = nullptr;
-    double* partial = nullptr;
-    SV_TRY(chain_workspace(fn, static_cast<hipStream_t>(stream), n_req, V, &counter, &partial));
     return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, nullptr, 0, nullptr, V, seed,
                                                 offset, B, (int)D, V, req_index, n_req, accepted_tokens,
-                                                accept_length, counter, partial, static_cast<hipStream_t>(stream)));
+                                                accept_length, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* t2d, int64_t Vd,
                                    const int32_t* draft_ids, const float* target_probs, const int32_t* qo_indptr,
                                    int64_t n_rows, const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D,
                                    int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
-                                   int32_t* accept_length, void* stream) {
+                                   int32_t* accept_length, void* workspace, int64_t workspace_bytes, void* stream) {
     const char* fn = "specverify_chain_reject_ragged";
     SV_TRY(check_draft(fn, D));
     if (t2d && !draft_probs)
@@ -221,13 +199,11 @@ int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* t2d,
     SV_REQUIRE(offset, "offset");
     SV_REQUIRE(accepted_tokens, "accepted_tokens");
     SV_REQUIRE(accept_length, "accept_length");
+    SV_TRY(check_chain_workspace(fn, n_req, V, workspace, workspace_bytes));
     SV_TRY(check_device());
-    uint32_t* counter = nullptr;
-    double* partial = nullptr;
-    SV_TRY(chain_workspace(fn, static_cast<hipStream_t>(stream), n_req, V, &counter, &partial));
     return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, qo_indptr, n_rows, t2d,
                                                 t2d ? Vd : V, seed, offset, B, (int)D, V, req_index, n_req,
-                                                accepted_tokens, accept_length, counter, partial,
+                                                accepted_tokens, accept_length, workspace,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -237,9 +213,10 @@ int specverify_d2t_inverse(const int64_t* d2t, int64_t Vd, int64_t V, int32_t* t
         return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: V=%lld must be in [1, 2^31)", fn, (long long)V);
     if (Vd < 1 || Vd > kMaxV)
         return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: Vd=%lld must be in [1, 2^31)", fn, (long long)Vd);
-    if (!d2t && Vd > V)
-        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: without a d2t table Vd=%lld must not exceed V=%lld", fn,
-                    (long long)Vd, (long long)V);
+    if (Vd > V)
+        return fail(SPECVERIFY_INVALID_ARGUMENT,
+                    "%s: Vd=%lld exceeds V=%lld (draft entries cannot map one-to-one into the target vocabulary)",
+                    fn, (long long)Vd, (long long)V);
     SV_REQUIRE(t2d, "t2d");
     SV_TRY(check_device());
     return launched(fn, sv::launch_d2t_inverse(d2t, Vd, V, t2d, static_cast<hipStream_t>(stream)));

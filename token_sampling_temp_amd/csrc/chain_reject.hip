@@ -252,21 +252,18 @@ __device__ int64_t draw_row_single(const float* pr, int64_t V, double uf, ChainS
     return sh.y;
 }
 
-// Cross-workgroup hand-off without cache-maintenance fences: partial sums are
-// published and read back with device-scope atomic read-modify-writes, which
-// are performed at the memory-side coherence point.  The publishing lane
-// consumes the RMW's return value before the workgroup barrier, so the value
-// is globally performed before thread 0 increments the request's counter.
-__device__ __forceinline__ void publish_partial(double* dst, double v) {
-    const unsigned long long old = __hip_atomic_exchange(reinterpret_cast<unsigned long long*>(dst),
-                                                         (unsigned long long)__double_as_longlong(v),
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("" ::"v"(old));   // wait for the exchange to complete
-}
-__device__ __forceinline__ double read_partial(double* src) {
-    const unsigned long long v = __hip_atomic_fetch_or(reinterpret_cast<unsigned long long*>(src), 0ull,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __longlong_as_double((long long)v);
+// Cross-workgroup hand-off of chunk sums (LLVM AMDGPU memory model, agent
+// scope).  Every workgroup of a request stores its sums with plain stores;
+// after a workgroup barrier, thread 0 adds one to the request's counter with
+// an acquire-release RMW at agent scope.  The release half orders the whole
+// workgroup's stores (they happen before it through the barrier) ahead of the
+// increment; the workgroup whose increment returns C - 1 is the last one, and
+// the acquire half of that same RMW, followed by a barrier, orders its loads
+// of every other workgroup's sums after their stores.  On gfx950 the compiler
+// implements the release with an L2 write-back (buffer_wbl2) and the acquire
+// with an L2 invalidate (buffer_inv): each split workgroup pays both once.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int C) {
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(C - 1);
 }
 
 // Segment pass for rows that are 16-byte aligned with V a multiple of 4 (and
@@ -411,7 +408,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
     const int32_t* __restrict__ qo_indptr, int64_t n_rows, const int32_t* __restrict__ t2d, int64_t Vd,
     const int32_t* __restrict__ req_index, int64_t n_req, int C, int R, int64_t per_xcd,
-    int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len, double* __restrict__ partial,
+    int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len, double* partial,
     uint32_t* __restrict__ counter, int64_t qcap) {
     __shared__ ChainShared sh;
     // a draft row over the draft vocabulary, staged when it fits (qcap entries
@@ -585,14 +582,12 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
         const int64_t ch = chunk0 + (int64_t)lane * kChainWaves + wid;
         if (lane < R && ch < nchunks) {
             if (solo) sh.chunk[ch] = mine;
-            else publish_partial(&partial[slot * nchunks + ch], mine);
+            else partial[slot * nchunks + ch] = mine;
         }
     }
     __syncthreads();
     if (!solo) {
-        if (tid == 0)
-            sh.last = (__hip_atomic_fetch_add(&counter[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                       (uint32_t)(C - 1)) ? 1 : 0;
+        if (tid == 0) sh.last = arrive_last(&counter[slot], C) ? 1 : 0;
         __syncthreads();
         if (!sh.last) return;
     }
@@ -601,14 +596,14 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     // first copied to LDS by every thread at once (one round trip), then wave
     // 0 picks the chunk and searches it.
     const double uf = (double)sh.code * 0x1p-24;
-    double* part = partial + slot * nchunks;
+    const double* part = partial + slot * nchunks;
     if (sums_in_lds && !solo) {
         constexpr int kPer = (kFallbackChunks + kChainBlock - 1) / kChainBlock;
         double v[kPer];
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t i = tid + (int64_t)k * kChainBlock;
-            v[k] = i < nchunks ? read_partial(&part[i]) : 0.0;
+            v[k] = i < nchunks ? part[i] : 0.0;
         }
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
@@ -622,8 +617,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
         int force_last;
         const int cstar =
             sums_in_lds ? wave_pick((int)nchunks, [&](int i) { return sh.chunk[i]; }, R_tot, uf, base, force_last)
-                        : wave_pick((int)nchunks, [&](int i) { return read_partial(&part[i]); }, R_tot, uf, base,
-                                    force_last);
+                        : wave_pick((int)nchunks, [&](int i) { return part[i]; }, R_tot, uf, base, force_last);
         int64_t y = -1;
         if (cstar >= 0) {
             int64_t lastpos;
@@ -635,6 +629,13 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
         if (lane == 0) sh.y = y;
     }
     __syncthreads();
+    if (!solo) {
+        // every workspace byte this call used goes back to zero (its counter
+        // below), so the workspace can serve any later call whatever its
+        // layout; the next kernel boundary orders these stores
+        double* mine_part = partial + slot * nchunks;
+        for (int64_t i = tid; i < nchunks; i += kChainBlock) mine_part[i] = 0.0;
+    }
     int64_t y = sh.y;
     if (y < 0 && (resid || point)) y = draw_row_single(pr, V, uf, sh);
     if (y < 0) y = (int64_t)(((uint64_t)sh.code * (uint64_t)V) >> 24);
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     }
     if (tid == 0) {
         accept_len[b] = L;
-        // ready for the next call on this workspace (kernel boundary orders it)
+        // ready for the next call on this workspace (the kernel boundary orders it)
         if (!solo) __hip_atomic_store(&counter[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -667,14 +668,36 @@ static void chain_split(int64_t n_req, int64_t V, int& C, int& R) {
     R = (int)r;
 }
 
+// Workspace layout: n_req 32-bit counters (padded to 256 bytes), then
+// n_req * chain_partials_per_request(V) doubles.  Needed only when a
+// request's row is split over several workgroups or its chunk sums exceed
+// the LDS table.  Every call returns the bytes it used to zero.
+static int64_t chain_counter_bytes(int64_t n_req) { return (n_req * 4 + 255) / 256 * 256; }
+
+int64_t chain_workspace_bytes(int64_t n_req, int64_t V) {
+    if (n_req <= 0) return 0;
+    int C, R;
+    chain_split(n_req, V, C, R);
+    const int64_t nchunks = chain_partials_per_request(V);
+    if (C == 1 && nchunks <= kFallbackChunks) return 0;
+    return chain_counter_bytes(n_req) + n_req * nchunks * 8;
+}
+
 hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
                                const int32_t* qo_indptr, int64_t n_rows, const int32_t* t2d, int64_t Vd,
                                const uint64_t* seed,
                                const uint64_t* offset, int64_t B, int D, int64_t V, const int32_t* req_index,
-                               int64_t n_req, int32_t* accepted, int32_t* accept_len, uint32_t* counter,
-                               double* partial, hipStream_t stream) {
+                               int64_t n_req, int32_t* accepted, int32_t* accept_len, void* workspace,
+                               hipStream_t stream) {
     int C, R;
     chain_split(n_req, V, C, R);
+    uint32_t* counter = nullptr;
+    double* partial = nullptr;
+    if (chain_workspace_bytes(n_req, V) > 0) {
+        if (!workspace) return hipErrorInvalidValue;
+        counter = static_cast<uint32_t*>(workspace);
+        partial = reinterpret_cast<double*>(static_cast<char*>(workspace) + chain_counter_bytes(n_req));
+    }
     const int64_t total = n_req * C;
     const int64_t per_xcd = (total + 7) / 8;
     const int64_t grid = per_xcd * 8;

@@ -26,13 +26,15 @@ __global__ __launch_bounds__(kD2tBlock) void d2t_fill_kernel(int32_t* __restrict
 }
 
 // t2d[(s + d2t[s]) mod V] = s, a floor modulus; the offsets are reduced first
-// so nothing overflows.
+// so nothing overflows.  A target shared by several draft entries keeps the
+// highest-numbered one (an atomic maximum over the -1 fill), as an in-order
+// scatter would leave it; the result does not depend on thread timing.
 __global__ __launch_bounds__(kD2tBlock) void d2t_scatter_kernel(const int64_t* __restrict__ d2t, int64_t Vd, int64_t V,
                                                                 int32_t* __restrict__ t2d) {
     for (int64_t s = (int64_t)blockIdx.x * kD2tBlock + threadIdx.x; s < Vd; s += (int64_t)gridDim.x * kD2tBlock) {
         int64_t t = (s % V + d2t[s] % V) % V;
         if (t < 0) t += V;
-        t2d[t] = (int32_t)s;
+        __hip_atomic_fetch_max(&t2d[t], (int32_t)s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -16,10 +16,11 @@ hipError_t launch_greedy_verify(const void* logits, int dtype, const int32_t* dr
                                 int32_t* accept_len, int32_t* predict, int32_t* accept_index,
                                 int32_t* argmax_out, hipStream_t stream);
 
-// Chain rejection needs a workspace: n_req uint32 counters that are zero
-// between calls (the kernel resets them) and n_req * chain_partials_per_request(V)
-// doubles of partial sums.
+// Chain rejection's workspace in bytes for n_req requests over V entries (0:
+// none).  It holds n_req 32-bit counters, zero before and after every call
+// (the kernel resets the ones it used), then the partial sums.
 int64_t chain_partials_per_request(int64_t V);
+int64_t chain_workspace_bytes(int64_t n_req, int64_t V);
 // qo_indptr NULL: dense target rows [B, D+1, V]; else packed rows [n_rows, V],
 // request b owning rows [qo_indptr[b], qo_indptr[b+1]).  t2d NULL: draft rows
 // [B, D, V]; else [B, D, Vd] over a smaller draft vocabulary, target entry v
@@ -28,8 +29,8 @@ hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_id
                                const int32_t* qo_indptr, int64_t n_rows, const int32_t* t2d, int64_t Vd,
                                const uint64_t* seed,
                                const uint64_t* offset, int64_t B, int D, int64_t V, const int32_t* req_index,
-                               int64_t n_req, int32_t* accepted, int32_t* accept_len, uint32_t* counter,
-                               double* partial, hipStream_t stream);
+                               int64_t n_req, int32_t* accepted, int32_t* accept_len, void* workspace,
+                               hipStream_t stream);
 
 // Draft -> target vocabulary placement.  launch_d2t_inverse builds t2d [V]
 // (draft entry of each target entry, -1 for none) from the offset table
