@@ -63,6 +63,7 @@ extern "C" {
 #define SPECVERIFY_BF16 1
 
 #define SPECVERIFY_MAX_DRAFT 16
+#define SPECVERIFY_STATIC_SCRATCH_BYTES (4 << 20)
 #define SPECVERIFY_RNG_SLOT_SPAN 32
 #define SPECVERIFY_VERSION 200
 
@@ -150,6 +151,31 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids,
                             const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
                             int32_t* accept_length, void* workspace, int64_t workspace_bytes,
                             void* stream);
+
+/*
+ * Chain rejection with no workspace argument and no allocation, for callers
+ * that cannot allocate device memory or pass one: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, results and errors are those of specverify_chain_reject without
+ * workspace / workspace_bytes.  Split launches use the library's static
+ * scratch instead: one array of SPECVERIFY_STATIC_SCRATCH_BYTES (4 MiB) per
+ * device, held until the process ends.  A call whose workspace size
+ * (specverify_chain_workspace_bytes) exceeds it returns
+ * SPECVERIFY_INVALID_ARGUMENT with nothing launched; calls that need none
+ * (n_req >= 256, V <= 262144) never touch it.  The first call on a device
+ * resolves the array's address and clears it with a fill kernel on that
+ * call's stream; every call returns the bytes it used to zero.  All calls on
+ * a device share its array, so calls that overlap in time on one device
+ * (different streams, or different host threads without ordering) race on
+ * it and give undefined results: issue them on one stream.  Calls no
+ * hipMalloc, hipFree or hipMemset.
+ */
+int specverify_chain_reject_noalloc(const float* draft_probs, const int32_t* draft_ids,
+                                    const float* target_probs, const uint64_t* seed,
+                                    const uint64_t* offset, int64_t B, int64_t D, int64_t V,
+                                    const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
+                                    int32_t* accept_length, void* stream);
 
 /*
  * Workspace size of specverify_chain_reject / specverify_chain_reject_ragged.

@@ -15,6 +15,8 @@ Functions mirror the C entry points:
   workspace=None)``: per-request verify lengths over packed target rows
 * ``chain_workspace_bytes(n_req, V)`` and ``chain_workspace(n_req, V, device)``: the caller-owned
   workspace the two chain calls need when rows are split over workgroups (small batches)
+* ``chain_reject_noalloc(draft_probs, draft_ids, target_probs, seed, offset, req_index=None)``:
+  chain rejection that allocates nothing, using the library's static scratch
 * ``sample(logits, temperature, seed, offset, top_k=None, top_p=None, min_p=None, req_index=None)``:
   single-step sampling with the joint top-k/top-p filter and min-p
 * ``d2t_inverse(d2t, Vd, V)`` and ``d2t_expand(draft_probs, t2d)``: draft distributions over a
@@ -38,12 +40,14 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 OK, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR = 0, 1, 2, 3
 F32, BF16 = 0, 1
 MAX_DRAFT = 16
+STATIC_SCRATCH_BYTES = 4 << 20
 RNG_SLOT_SPAN = 32
 
 SYMBOLS = (
     "specverify_softmax_renorm",
     "specverify_chain_reject",
     "specverify_chain_workspace_bytes",
+    "specverify_chain_reject_noalloc",
     "specverify_chain_reject_ragged",
     "specverify_d2t_inverse",
     "specverify_d2t_expand",
@@ -81,6 +85,7 @@ def lib() -> ctypes.CDLL:
     L.specverify_softmax_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp, vp]
     L.specverify_chain_reject.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp]
     L.specverify_chain_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    L.specverify_chain_reject_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
     L.specverify_chain_reject_ragged.argtypes = [vp, vp, i64, vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, i64, vp,
                                                  vp, vp, i64, vp]
     L.specverify_d2t_inverse.argtypes = [vp, i64, i64, vp, vp]
@@ -90,7 +95,7 @@ def lib() -> ctypes.CDLL:
     L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
     L.specverify_sample.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, i64, vp, vp]
     for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_chain_workspace_bytes",
-                 "specverify_chain_reject_ragged",
+                 "specverify_chain_reject_noalloc", "specverify_chain_reject_ragged",
                  "specverify_d2t_inverse", "specverify_d2t_expand", "specverify_greedy_verify",
                  "specverify_gumbel_sample", "specverify_verify_fused", "specverify_sample"):
         getattr(L, name).restype = ctypes.c_int
@@ -264,6 +269,37 @@ def chain_reject(draft_probs, draft_ids, target_probs, seed, offset, req_index=N
         _ptr(draft_probs), _ptr(draft_ids), _ptr(target_probs), _ptr(seed), _ptr(offset), B, D, V,
         _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _ptr(ws), ws_bytes, _stream_ptr(dev))
     _check("specverify_chain_reject", st)
+    return acc, alen
+
+
+def chain_reject_noalloc(draft_probs, draft_ids, target_probs, seed, offset, req_index=None, out=None):
+    """Chain rejection through the entry point that allocates nothing (the library's static scratch of
+    STATIC_SCRATCH_BYTES per device; calls overlapping on one device race).  ``out`` must be given to
+    allocate nothing here either."""
+    torch = _torch()
+    _need(target_probs, "target_probs", (torch.float32,), None, 3)
+    dev = target_probs.device
+    B, N, V = target_probs.shape
+    D = N - 1
+    if draft_probs is not None:
+        _need(draft_probs, "draft_probs", (torch.float32,), dev, 3)
+        if tuple(draft_probs.shape) != (B, D, V):
+            raise ValueError(f"draft_probs must be [{B},{D},{V}]")
+    _need(draft_ids, "draft_ids", (torch.int32,), dev, 2)
+    if tuple(draft_ids.shape) != (B, D):
+        raise ValueError(f"draft_ids must be [{B},{D}]")
+    _u64(seed, "seed", B, dev)
+    _u64(offset, "offset", B, dev)
+    req_index, n_req = _req(req_index, B, dev)
+    if out is None:
+        acc = torch.empty((B, N), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        acc, alen = out
+    st = lib().specverify_chain_reject_noalloc(
+        _ptr(draft_probs), _ptr(draft_ids), _ptr(target_probs), _ptr(seed), _ptr(offset), B, D, V,
+        _ptr(req_index), n_req, _ptr(acc), _ptr(alen), _stream_ptr(dev))
+    _check("specverify_chain_reject_noalloc", st)
     return acc, alen
 
 

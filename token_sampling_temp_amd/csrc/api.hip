@@ -10,6 +10,9 @@
 #include "specverify.h"
 #include "sv_launch.hpp"
 
+static_assert(SPECVERIFY_STATIC_SCRATCH_BYTES == sv::kChainStaticScratchBytes,
+              "the header's static scratch size must match the library's");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -171,6 +174,37 @@ int specverify_chain_reject(const float* draft_probs, const int32_t* draft_ids, 
     return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, nullptr, 0, nullptr, V, seed,
                                                 offset, B, (int)D, V, req_index, n_req, accepted_tokens,
                                                 accept_length, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int specverify_chain_reject_noalloc(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,
+                                    const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D, int64_t V,
+                                    const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
+                                    int32_t* accept_length, void* stream) {
+    const char* fn = "specverify_chain_reject_noalloc";
+    SV_TRY(check_draft(fn, D));
+    SV_TRY(check_sizes(fn, B, D + 1, V, req_index, n_req, 4));
+    if (n_req == 0) return SPECVERIFY_OK;
+    if (D > 0) SV_REQUIRE(draft_ids, "draft_ids");
+    SV_REQUIRE(target_probs, "target_probs");
+    SV_REQUIRE(seed, "seed");
+    SV_REQUIRE(offset, "offset");
+    SV_REQUIRE(accepted_tokens, "accepted_tokens");
+    SV_REQUIRE(accept_length, "accept_length");
+    const int64_t need = sv::chain_workspace_bytes(n_req, V);
+    if (need > SPECVERIFY_STATIC_SCRATCH_BYTES)
+        return fail(SPECVERIFY_INVALID_ARGUMENT,
+                    "%s: n_req=%lld V=%lld needs %lld bytes of scratch; the static scratch holds %lld "
+                    "(use specverify_chain_reject with a caller workspace)",
+                    fn, (long long)n_req, (long long)V, (long long)need, (long long)SPECVERIFY_STATIC_SCRATCH_BYTES);
+    SV_TRY(check_device());
+    void* ptr = nullptr;
+    if (need > 0) {
+        const hipError_t e = sv::chain_static_scratch(static_cast<hipStream_t>(stream), &ptr);
+        if (e != hipSuccess) return fail(SPECVERIFY_HIP_ERROR, "%s: static scratch: %s", fn, hipGetErrorString(e));
+    }
+    return launched(fn, sv::launch_chain_reject(draft_probs, draft_ids, target_probs, nullptr, 0, nullptr, V, seed,
+                                                offset, B, (int)D, V, req_index, n_req, accepted_tokens,
+                                                accept_length, ptr, static_cast<hipStream_t>(stream)));
 }
 
 int specverify_chain_reject_ragged(const float* draft_probs, const int32_t* t2d, int64_t Vd,

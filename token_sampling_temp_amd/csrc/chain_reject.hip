@@ -29,6 +29,8 @@
 // t2d) are copied whole into LDS when they fit (a separate instantiation with
 // dynamic LDS); the residual pass then streams p_L and t2d and looks the draft
 // entries up in LDS instead of gathering them from global memory.
+#include <mutex>
+
 #include "sv_draw.hpp"
 #include "sv_launch.hpp"
 
@@ -681,6 +683,48 @@ int64_t chain_workspace_bytes(int64_t n_req, int64_t V) {
     const int64_t nchunks = chain_partials_per_request(V);
     if (C == 1 && nchunks <= kFallbackChunks) return 0;
     return chain_counter_bytes(n_req) + n_req * nchunks * 8;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (specverify_chain_reject_noalloc):
+// a file-scope device array with the layout of the caller workspace.  Each
+// device holds its own copy at its own address, so host code never passes
+// the array's name to a kernel: the address comes from hipGetSymbolAddress,
+// once per device, and is kept.  The first call on a device also clears the
+// array with a fill kernel on that call's stream; every later call finds the
+// bytes it needs at zero because every call returns what it used to zero.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kChainStaticScratchBytes];
+
+__global__ __launch_bounds__(256) void scratch_clear_kernel(u32x4* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+namespace {
+constexpr int kScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t chain_static_scratch(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        constexpr int64_t n = kChainStaticScratchBytes / 16;
+        hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, stream, static_cast<u32x4*>(ptr), n);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_chain_reject(const float* draft_probs, const int32_t* draft_ids, const float* target_probs,

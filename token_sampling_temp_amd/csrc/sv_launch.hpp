@@ -21,6 +21,11 @@ hipError_t launch_greedy_verify(const void* logits, int dtype, const int32_t* dr
 // (the kernel resets the ones it used), then the partial sums.
 int64_t chain_partials_per_request(int64_t V);
 int64_t chain_workspace_bytes(int64_t n_req, int64_t V);
+// The library's static scratch for chain rejection without a caller workspace
+// (same layout, at most kChainStaticScratchBytes): this device's address,
+// resolved and cleared (a fill kernel on `stream`) on the first call per device.
+constexpr int64_t kChainStaticScratchBytes = 4 << 20;
+hipError_t chain_static_scratch(hipStream_t stream, void** out);
 // qo_indptr NULL: dense target rows [B, D+1, V]; else packed rows [n_rows, V],
 // request b owning rows [qo_indptr[b], qo_indptr[b+1]).  t2d NULL: draft rows
 // [B, D, V]; else [B, D, Vd] over a smaller draft vocabulary, target entry v
