@@ -14,10 +14,10 @@
 //    several rounds of 16-byte loads in flight, one sum per chunk.
 // 3. A workgroup that owns the whole row keeps its chunk sums in LDS.
 //    Otherwise the sums are published and the last workgroup of the request
-//    to finish (device-scope atomic counter, reset afterwards; no
-//    cache-flushing fences) collects them.  The locating workgroup
-//    prefix-sums the chunk sums in order, finds the chunk holding u_f * R,
-//    re-reads it and finishes with a 64-lane scan.  Zero-mass entries are
+//    to finish (agent-scope acquire-release counter, reset afterwards)
+//    collects them.  The locating workgroup prefix-sums the chunk sums in
+//    order (one wave, four sums per lane), finds the chunk holding u_f * R,
+//    re-reads it and scans its sub-tiles lane by lane.  Zero-mass entries are
 //    never selected.  Sums use fixed reduction trees, so results are
 //    reproducible run to run.
 // 4. Degenerate rows (residual mass not positive) fall back to a draw from the
@@ -38,11 +38,18 @@
 #define SV_CHAIN_TARGET_WGS 256    // one 256-thread workgroup per CU on 256 CUs
 #endif
 #ifndef SV_CHAIN_DEPTH
-#define SV_CHAIN_DEPTH 2           // rounds of loads in flight per wave
+#define SV_CHAIN_DEPTH 3           // rounds of loads in flight per wave
+#endif
+#ifndef SV_CHAIN_DEPTH_ONE_ROW
+#define SV_CHAIN_DEPTH_ONE_ROW 1   // the same for a row streamed alone beside two-row requests
+#endif
+#ifndef SV_CHAIN_DEPTH_ALL_ONE_ROW
+#define SV_CHAIN_DEPTH_ALL_ONE_ROW 2   // when every request streams one row
 #endif
 #ifndef SV_CHAIN_NT
 #define SV_CHAIN_NT 1              // stream rows with non-temporal loads
 #endif
+
 #ifndef SV_CHAIN_T2D_AUX
 #define SV_CHAIN_T2D_AUX 0         // the inverse table: temporal loads (shared by every request)
 #endif
@@ -64,7 +71,7 @@ constexpr int kFallbackChunks = 512;
 constexpr int64_t kMaxStagedBytes = 150 * 1024;
 
 struct ChainShared {
-    double chunk[kFallbackChunks];
+    alignas(16) double chunk[kFallbackChunks];
     uint32_t code;
     int L;
     int32_t xL;   // point-mass drafts: the rejected id (-1 if none or out of range)
@@ -139,7 +146,7 @@ __device__ __forceinline__ void load_q_run(const float* qr, const int32_t* t2d, 
 // positive entries.  Wave-uniform result; -1 if not found.  `lastpos`
 // receives the last positive entry of the run (wave-uniform); `total`
 // receives the run's mass.
-template <int NSUB>
+template <int NSUB, bool LAZY_LAST = false>
 __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int64_t V, bool aligned,
                                int64_t base, double run, double T, bool force_last, int64_t& lastpos,
                                double& total, int64_t xo = -1, const int32_t* t2d = nullptr, int64_t Vd = 0) {
@@ -159,15 +166,22 @@ __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int
         const double r = rval(pf[k][e], qf[k][e], resid);
         return base + (k * kWave + lane) * 4 + e == xo ? fmax(0.0, (double)pf[k][e] - 1.0) : r;
     };
-    int64_t mylast = -1;
+    auto last_positive = [&]() {
+        int64_t mylast = -1;
 #pragma unroll
-    for (int k = 0; k < NSUB; ++k)
+        for (int k = 0; k < NSUB; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (rv(k, e) > 0.0) mylast = base + (k * kWave + lane) * 4 + e;
-    lastpos = wave_allreduce(mylast, [](int64_t a, int64_t b) { return a > b ? a : b; });
+            for (int e = 0; e < 4; ++e)
+                if (rv(k, e) > 0.0) mylast = base + (k * kWave + lane) * 4 + e;
+        return wave_allreduce(mylast, [](int64_t a, int64_t b) { return a > b ? a : b; });
+    };
+    // LAZY_LAST: the last positive entry is found only when it is the answer
+    lastpos = LAZY_LAST ? -1 : last_positive();
     total = 0.0;
-    if (force_last) return -1;
+    if (force_last) {
+        if (LAZY_LAST) lastpos = last_positive();
+        return -1;
+    }
 #pragma unroll
     for (int k = 0; k < NSUB; ++k) {
         double r[4];
@@ -200,7 +214,66 @@ __device__ int64_t wave_search(const float* pr, const float* qr, bool resid, int
         run += tot;
         total += tot;
     }
+    if (LAZY_LAST) lastpos = last_positive();
     return -1;
+}
+
+// One wave picks the chunk holding the draw when the row has at most 256
+// chunk sums (in LDS): lane l reads chunks 4l..4l+3 with two 16-byte LDS
+// reads and keeps them in registers for its walk.  Same contract as
+// wave_pick (index and mass before it; force_last when rounding left
+// T = uf * R beyond every positive chunk; -1 when R is not positive), with
+// its own fixed association order.
+__device__ int pick_chunk256(const double* sums, int n, double uf, double& R, double& base, int& force_last) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double v[4];
+    {
+        const double2* s2 = reinterpret_cast<const double2*>(sums) + lane * 2;
+        const double2 a = s2[0], c = s2[1];
+        v[0] = a.x;
+        v[1] = a.y;
+        v[2] = c.x;
+        v[3] = c.y;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (lane * 4 + k >= n) v[k] = 0.0;
+    const double lt = ((v[0] + v[1]) + v[2]) + v[3];
+    const double incl = wave_incl_scan(lt);
+    const double ex = wave_shift_up1(incl);
+    R = read_lane(incl, kWave - 1);
+    base = 0.0;
+    force_last = 0;
+    if (!(R > 0.0)) return -1;
+    const double T = uf * R;
+    const uint64_t ball = __ballot(incl > T && lt > 0.0);
+    int pick = -1, lastp = -1;
+    if (ball) {
+        const int ls = __ffsll((unsigned long long)ball) - 1;
+        double run = ex, b = 0.0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (pick < 0 && v[k] > 0.0) {
+                lastp = lane * 4 + k;
+                if (run + v[k] > T) {
+                    pick = lane * 4 + k;
+                    b = run;
+                }
+            }
+            run += v[k];
+        }
+        const int fl = pick < 0;
+        if (fl) pick = lastp;
+        pick = read_lane(pick, ls);
+        base = read_lane(b, ls);
+        force_last = read_lane(fl, ls);
+        return pick;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (v[k] > 0.0) lastp = lane * 4 + k;
+    force_last = 1;
+    return wave_allreduce(lastp, [](int a, int c) { return a > c ? a : c; });
 }
 
 // Single-workgroup inverse-CDF draw over a whole row (only for the
@@ -537,9 +610,18 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
         mine = stream_chunks_fast<true, SV_CHAIN_DEPTH, false, true>(pr, nullptr, V, chunk0, R, -1, t2d,
                                                                       (uint32_t)Vd, qlds);
     } else if (fast && !(resid && t2d)) {
+        // With draft distributions a batch mixes two-row (residual) and
+        // one-row (bonus) requests, and the two-row ones set the kernel's end:
+        // a one-row workgroup keeps fewer loads in flight, so it takes a
+        // smaller share of HBM while both kinds stream and finishes closer to
+        // the two-row ones (measured on the large-vocab batch: 36.3 -> 35.5 us
+        // together with the pick and the lazy last-positive search).  Without
+        // draft distributions every request streams one row: two rounds in
+        // flight measured best there (24.7 us against 25.3 with three).
+        constexpr int kOneRowDepth = kMode == kDraftProbs ? SV_CHAIN_DEPTH_ONE_ROW : SV_CHAIN_DEPTH_ALL_ONE_ROW;
         if (resid) mine = stream_chunks_fast<true, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
-        else if (point) mine = stream_chunks_fast<false, SV_CHAIN_DEPTH, true>(pr, qr, V, chunk0, R, xo);
-        else mine = stream_chunks_fast<false, SV_CHAIN_DEPTH>(pr, qr, V, chunk0, R);
+        else if (point) mine = stream_chunks_fast<false, kOneRowDepth, true>(pr, qr, V, chunk0, R, xo);
+        else mine = stream_chunks_fast<false, kOneRowDepth>(pr, qr, V, chunk0, R);
     } else {
         float pa[4][4], qa[4][4], pb[4][4], qb[4][4];
         auto load_chunk = [&](int r, float (&pf)[4][4], float (&qf)[4][4]) {
@@ -618,14 +700,15 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
         double R_tot, base;
         int force_last;
         const int cstar =
-            sums_in_lds ? wave_pick((int)nchunks, [&](int i) { return sh.chunk[i]; }, R_tot, uf, base, force_last)
-                        : wave_pick((int)nchunks, [&](int i) { return part[i]; }, R_tot, uf, base, force_last);
+            nchunks <= 256 ? pick_chunk256(sh.chunk, (int)nchunks, uf, R_tot, base, force_last)
+            : sums_in_lds  ? wave_pick((int)nchunks, [&](int i) { return sh.chunk[i]; }, R_tot, uf, base, force_last)
+                           : wave_pick((int)nchunks, [&](int i) { return part[i]; }, R_tot, uf, base, force_last);
         int64_t y = -1;
         if (cstar >= 0) {
             int64_t lastpos;
             double tot;
-            y = wave_search<4>(pr, qr, resid, V, aligned, (int64_t)cstar * kChunk, base, uf * R_tot,
-                               force_last != 0, lastpos, tot, xo, t2d, Vd);
+            y = wave_search<4, true>(pr, qr, resid, V, aligned, (int64_t)cstar * kChunk, base, uf * R_tot,
+                                     force_last != 0, lastpos, tot, xo, t2d, Vd);
             if (y < 0) y = lastpos;
         }
         if (lane == 0) sh.y = y;
