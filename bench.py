@@ -900,14 +900,31 @@ class MixedFusedWorkload(MixedWorkload):
         t = self.idx_host[MODE_TEMPERATURE]
         f = self.filt_host
         by = {"greedy_verify": [], "gumbel_sample": [], "verify_fused": []}
-        # logit rows 0..L, the draft row q_L on a rejection, q at the ids probed
-        for L in self._lengths():
+        # logit rows 0..L; on a rejection the draft row q_L at the entries row L keeps (the residual
+        # max(0, p - q) is zero wherever p is), one 64-byte line per kept entry, at most the whole row;
+        # q at the ids probed
+        kept = self._kept_counts()
+        for r, L in enumerate(self._lengths()):
+            qbytes = np.minimum(4 * V, PROBE_GRANULE * kept[r][np.arange(self.B), np.minimum(L, D)][f])
             by["greedy_verify"].append(((L[g] + 1) * V * 2).sum())
             by["gumbel_sample"].append(((L[t] + 1) * V * 2).sum())
-            by["verify_fused"].append(((L[f] + 1) * V * 2 + np.where(L[f] < D, 4 * V, 0)
+            by["verify_fused"].append(((L[f] + 1) * V * 2 + np.where(L[f] < D, qbytes, 0)
                                        + PROBE_GRANULE * np.minimum(L[f] + 1, D)).sum())
         self.bytes_by_call = {k: float(np.mean(v)) for k, v in by.items()}
         return self.bytes_by_call["verify_fused"]
+
+    def _kept_counts(self):
+        """Entries each target row keeps after top-k/top-p, per replica [B, N] (rows of other modes: 0),
+        counted on the library's own renormalised rows (setup only, not timed)."""
+        import torch
+        out = []
+        for r in self.reps:
+            probs = torch.zeros((self.B, self.D + 1, self.V), dtype=torch.float32, device=r["z"].device)
+            self.sv.softmax_renorm(r["z"], self.T, self.k, self.p, req_index=self.filt_idx, out=probs)
+            out.append((probs > 0).sum(-1).cpu().numpy().astype(np.int64))
+            del probs
+        torch.cuda.empty_cache()
+        return out
 
 
 WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, RaggedD2tWorkload,

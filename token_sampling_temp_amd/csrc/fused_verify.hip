@@ -28,9 +28,18 @@ constexpr int kFvWaves = kFvBlock / kWave;
 constexpr int64_t kFvChunk = 1024;   // entries per chunk sum
 constexpr int kFvMaxChunks = 512;    // V <= 524288
 
+constexpr int kCompactCap = kFvBlock;   // kept entries a compacted draw handles (one per thread)
+
 struct FusedShared {
     RrShared rr;                  // histogram / probability table / streamed and argmax state
     double chunk[kFvMaxChunks];   // chunk sums of the drawn row
+    // compacted draw: the kept entries of a register-resident row
+    uint64_t clist[kCompactCap];  // (index << 16) | key, in arrival order
+    uint32_t cidx[kCompactCap];   // indices, ascending
+    float cp[kCompactCap];        // target probabilities, same order
+    float cq[kCompactCap];        // draft probabilities at the same indices (residual draws)
+    double wsum[kFvWaves];        // per-wave totals of the block scan
+    int32_t whit[kFvWaves];       // per-wave counts, then first crossing / last positive entry
     int32_t xs[kMaxDraft];        // draft ids
     float qx[kMaxDraft];          // q_i(x_i), 0 for an id outside [0, V)
     uint32_t zx[kMaxDraft];       // bits of the logit z_i(x_i)
@@ -275,6 +284,147 @@ __device__ __forceinline__ int64_t fused_draw(FusedShared& sh, const RowProb rp,
     return sh.y;
 }
 
+// Probability of a kept key under register-resident statistics: the value
+// row_prob gives the logit with that key.
+__device__ __forceinline__ float key_prob(const RowProb rp, const RrShared& sh, uint32_t key) {
+    if (rp.mode == kProbTable) return sh.u.lut[max((int)key + 1 - (int)rp.kmin, 0)];
+    return key >= rp.kmin ? fast_exp2((key_to_float(key) - rp.m) * rp.scale) * rp.inv : 0.0f;
+}
+
+// Inverse-CDF draw over the kept entries of a register-resident row: every
+// weight outside the kept set (keys below kmin) is zero, for the bonus draw
+// (p) and the residual (max(0, p - q)) alike, so only the kept entries are
+// visited.  The statistics pass recorded each thread vector's largest key
+// (vmax); the vectors whose largest key reaches kmin are listed, one thread
+// per listed vector re-reads it (16 bytes) and appends its kept entries
+// (index, key) to LDS, the entries are ranked by index (each counts the
+// smaller indices, reading the list as LDS broadcasts), the draft
+// probabilities are gathered at the kept indices only (issued before the
+// ranking, so the gather overlaps it), and one block-wide scan in index
+// order finds y = min{ j : sum_{v <= j} r_v > u_f * R }.  Whole workgroup.
+// Nothing is drawn (used = false) when more than kCompactCap vectors or kept
+// entries would be involved.
+struct CompactDraw {
+    int64_t y;   // the drawn index, -1 when the weights have no positive mass
+    bool used;   // false: nothing drawn (too many vectors or kept entries)
+};
+
+template <int NV>
+__device__ __forceinline__ CompactDraw compact_draw(FusedShared& sh, const RowProb rp,
+                                                    const uint16_t* __restrict__ row,
+                                                    const uint32_t (&vmax)[(NV + 1) / 2], int64_t V,
+                                                    const float* __restrict__ qr, double uf, int tid) {
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    const uint32_t kmin = rp.kmin;
+    // block-wide exclusive scan of per-thread counts through sh.whit
+    auto block_offsets = [&](uint32_t c, uint32_t& total) {
+        const uint32_t inc = wave_inclusive_sum(c, lane);
+        lds_barrier();   // earlier readers of whit are done
+        if (lane == kWave - 1) sh.whit[wid] = (int32_t)inc;
+        lds_barrier();
+        uint32_t off = inc - c;
+        total = 0;
+#pragma unroll
+        for (int i = 0; i < kFvWaves; ++i) {
+            const uint32_t t = (uint32_t)sh.whit[i];
+            if (i < wid) off += t;
+            total += t;
+        }
+        return off;
+    };
+    // ---- the vectors that hold kept keys
+    uint32_t nvq = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) nvq += ((vmax[v >> 1] >> (16 * (v & 1))) & 0xFFFFu) >= kmin ? 1u : 0u;
+    uint32_t Q;
+    uint32_t vpos = block_offsets(nvq, Q);
+    if (!(Q > 0 && Q <= (uint32_t)kCompactCap)) return CompactDraw{-1, false};   // uniform
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        if (((vmax[v >> 1] >> (16 * (v & 1))) & 0xFFFFu) >= kmin) sh.cidx[vpos++] = (uint32_t)(v * kRrBlock + tid);
+    lds_barrier();
+    // ---- one listed vector per thread: re-read, count and append its kept entries
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(row, (uint32_t)(V * 2));
+    uint32_t keys[4] = {0u, 0u, 0u, 0u}, cnt = 0, vid = 0;
+    if ((uint32_t)tid < Q) {
+        vid = sh.cidx[tid];
+        const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, vid * 16, 0, 0));
+        keys[0] = keys_of_pair(x.x);
+        keys[1] = keys_of_pair(x.y);
+        keys[2] = keys_of_pair(x.z);
+        keys[3] = keys_of_pair(x.w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t key = (keys[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+            cnt += (key >= kmin && (int64_t)vid * 8 + i < V) ? 1u : 0u;
+        }
+    }
+    uint32_t n;
+    uint32_t epos = block_offsets(cnt, n);
+    if (!(n > 0 && n <= (uint32_t)kCompactCap)) return CompactDraw{-1, false};   // uniform
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t key = (keys[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const int64_t idx = (int64_t)vid * 8 + i;
+        if (cnt && key >= kmin && idx < V) sh.clist[epos++] = ((uint64_t)idx << 16) | key;
+    }
+    lds_barrier();
+    // ---- rank by index; gather the draft probabilities meanwhile
+    if ((uint32_t)tid < n) {
+        const uint64_t e = sh.clist[tid];
+        const uint32_t idx = (uint32_t)(e >> 16);
+        const float qv = qr ? qr[idx] : 0.0f;   // waited for only after the ranking loop
+        uint32_t rank = 0;
+        const uint32_t n2 = n & ~1u;
+        for (uint32_t j = 0; j < n2; j += 2) {
+            const uint64_t a = sh.clist[j], c = sh.clist[j + 1];
+            rank += (a < e ? 1u : 0u) + (c < e ? 1u : 0u);
+        }
+        if (n & 1u) rank += sh.clist[n - 1] < e ? 1u : 0u;
+        sh.cidx[rank] = idx;
+        sh.cp[rank] = key_prob(rp, sh.rr, (uint32_t)(e & 0xFFFFu));
+        sh.cq[rank] = qv;
+    }
+    lds_barrier();
+    // ---- block-wide inclusive scan of the weights in index order
+    const bool in = (uint32_t)tid < n;
+    const double r = in ? rval(sh.cp[tid], sh.cq[tid], qr != nullptr) : 0.0;
+    const double winc = wave_inclusive_sum(r, lane);
+    if (lane == kWave - 1) sh.wsum[wid] = winc;
+    lds_barrier();
+    double off = 0.0, R = 0.0;
+#pragma unroll
+    for (int i = 0; i < kFvWaves; ++i) {
+        const double t = sh.wsum[i];
+        if (i < wid) off += t;
+        R += t;
+    }
+    if (!(R > 0.0)) return CompactDraw{-1, true};   // uniform
+    const double T = uf * R;
+    const double incl = off + winc;
+    const uint64_t hit = __ballot(in && r > 0.0 && incl > T);
+    const uint64_t posv = __ballot(in && r > 0.0);
+    // per wave: the first crossing (>= 0), else -2 - its last positive entry,
+    // else -1
+    if (lane == 0) {
+        sh.whit[wid] = hit    ? wid * kWave + (__ffsll((unsigned long long)hit) - 1)
+                       : posv ? -2 - (wid * kWave + (63 - __clzll((unsigned long long)posv)))
+                              : -1;
+    }
+    lds_barrier();
+    int first = -1, last = -1;
+#pragma unroll
+    for (int i = 0; i < kFvWaves; ++i) {
+        const int h = sh.whit[i];
+        if (h >= 0 && first < 0) first = h;
+        if (h <= -2) last = -2 - h;   // waves in order: the last one seen is the largest
+    }
+    // no crossing: rounding left T beyond every partial sum, so the draw is
+    // the last positive entry
+    const int t = first >= 0 ? first : last;
+    return CompactDraw{t >= 0 ? (int64_t)sh.cidx[t] : -1, true};
+}
+
 // NV > 0: bf16 logits whose rows are 16-byte aligned with V a multiple of 8
 // and V <= 8192 * NV take the register-resident statistics (as the softmax
 // kernel does); NV = 0: streamed statistics for every temperature row.
@@ -310,32 +460,17 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_kernel(
     }
     __syncthreads();
 
-    // ---- rows 0..L: statistics, then the accept test at the draft id
+    // ---- rows 0..L: statistics, then the accept test at the draft id.  The
+    // row where the chain stops (a rejection, or the bonus row D) is drawn
+    // from; a register-resident row with a small kept set is drawn right
+    // here, from the keys still in registers.
+    const double uf = (double)sh.code[D] * 0x1p-24;
     RowProb rp{kProbOneHot, 0.0f, 0.0f, 0.0f, 0u, 0};
     int L = D;
-    for (int j = 0; j <= D; ++j) {
-        const T* row = logits + ((int64_t)b * N + j) * V;
-        if ((double)Tm < kGreedyTemperature) {
-            __syncthreads();   // the previous row's table may still be read
-            rp.mode = kProbOneHot;
-            rp.y = row_argmax<kFvBlock, false>(row, V, sh.rr.u.sm.am);
-        } else {
-            bool done = false;
-            if constexpr (NV > 0) {
-                u32x4 w[NV];
-                RrStats st;
-                if (rr_stats<NV>(sh.rr, reinterpret_cast<const uint16_t*>(row), V, Tm, k, tp, tid, w, st)) {
-                    rp = RowProb{st.table ? kProbTable : kProbRrExp, st.m, st.scale, st.inv, st.kmin, 0};
-                    done = true;
-                }
-            }
-            if (!done) {
-                __syncthreads();
-                const StreamStats ss = streamed_stats<T>(row, V, Tm, k, tp, sh.rr.u.sm);
-                rp = RowProb{kProbStreamed, ss.m, ss.scale, ss.inv, ss.kmin, 0};
-            }
-        }
-        if (j == D) break;
+    bool drawn = false;
+    int64_t y = -1;
+    // accept test at position j (block-uniform result)
+    auto accepted_at = [&](int j) {
         if (tid == 0) {
             const int32_t xj = sh.xs[j];
             bool ok = false;
@@ -349,21 +484,62 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_kernel(
             sh.acc = ok ? 1 : 0;
         }
         __syncthreads();
-        if (!sh.acc) {
+        return sh.acc != 0;
+    };
+    for (int j = 0; j <= D; ++j) {
+        const T* row = logits + ((int64_t)b * N + j) * V;
+        bool stop = false, done = false;
+        // the thread index is made opaque per row, so nothing derived from it
+        // is hoisted out of the row loop and held in registers across rows
+        int rtid = threadIdx.x;
+        asm volatile("" : "+v"(rtid));
+        if ((double)Tm < kGreedyTemperature) {
+            __syncthreads();   // the previous row's table may still be read
+            rp.mode = kProbOneHot;
+            rp.y = row_argmax<kFvBlock, false>(row, V, sh.rr.u.sm.am);
+        } else {
+            if constexpr (NV > 0) {
+                u32x4 w[NV];
+                uint32_t vmax[(NV + 1) / 2];
+                RrStats st;
+                const uint16_t* row16 = reinterpret_cast<const uint16_t*>(row);
+                if (rr_stats<NV, false, true>(sh.rr, row16, V, Tm, k, tp, rtid, w, st, 0.0f, vmax)) {
+                    rp = RowProb{st.table ? kProbTable : kProbRrExp, st.m, st.scale, st.inv, st.kmin, 0};
+                    done = true;
+                    stop = j == D || !accepted_at(j);
+                    if (stop) {
+                        // a small kept set is drawn by revisiting only the vectors that hold it
+                        const float* qj = j < D ? q + ((int64_t)b * D + j) * V : nullptr;
+                        CompactDraw cd = compact_draw<NV>(sh, rp, row16, vmax, V, qj, uf, rtid);
+                        // an empty residual falls back to the target row
+                        if (cd.used && cd.y < 0 && qj) cd = compact_draw<NV>(sh, rp, row16, vmax, V, nullptr, uf, rtid);
+                        y = cd.y;
+                        drawn = cd.used;
+                    }
+                }
+            }
+            if (!done) {
+                __syncthreads();
+                const StreamStats ss = streamed_stats<T>(row, V, Tm, k, tp, sh.rr.u.sm);
+                rp = RowProb{kProbStreamed, ss.m, ss.scale, ss.inv, ss.kmin, 0};
+            }
+        }
+        if (!done) stop = j == D || !accepted_at(j);
+        if (stop) {
             L = j;
             break;
         }
     }
 
-    // ---- draw from row L's residual (or the bonus row), then from the
-    // target row, then floor(u_f * V)
+    // ---- otherwise draw from row L's residual (or the bonus row) by
+    // re-reading it, then from the target row, then floor(u_f * V)
     const bool resid = L < D;
     const T* zr = logits + ((int64_t)b * N + L) * V;
     const float* qr = resid ? q + ((int64_t)b * D + L) * V : nullptr;
-    const double uf = (double)sh.code[D] * 0x1p-24;
-    int64_t y = resid ? fused_draw<T, true>(sh, rp, zr, qr, V, uf)
-                      : fused_draw<T, false>(sh, rp, zr, nullptr, V, uf);
-    if (y < 0 && resid) y = fused_draw<T, false>(sh, rp, zr, nullptr, V, uf);
+    if (!drawn) {
+        y = resid ? fused_draw<T, true>(sh, rp, zr, qr, V, uf) : fused_draw<T, false>(sh, rp, zr, nullptr, V, uf);
+        if (y < 0 && resid) y = fused_draw<T, false>(sh, rp, zr, nullptr, V, uf);
+    }
     if (y < 0) y = (int64_t)(((uint64_t)sh.code[D] * (uint64_t)V) >> 24);
     if (tid < N) {
         int32_t t;
@@ -404,13 +580,20 @@ __global__ __launch_bounds__(kFvBlock) void sample_kernel(
     const float tp = top_p ? top_p[b] : 1.0f;
     const float mp = min_p ? min_p[b] : 0.0f;
     RowProb rp{kProbStreamed, 0.0f, 0.0f, 0.0f, 0u, 0};
-    bool done = false;
+    bool done = false, drawn = false;
+    int64_t y = -1;
     if constexpr (NV > 0) {
         u32x4 w[NV];
+        uint32_t vmax[(NV + 1) / 2];
         RrStats st;
-        if (rr_stats<NV, true>(sh.rr, reinterpret_cast<const uint16_t*>(row), V, Tm, k, tp, tid, w, st, mp)) {
+        const uint16_t* row16 = reinterpret_cast<const uint16_t*>(row);
+        if (rr_stats<NV, true, true>(sh.rr, row16, V, Tm, k, tp, tid, w, st, mp, vmax)) {
             rp = RowProb{st.table ? kProbTable : kProbRrExp, st.m, st.scale, st.inv, st.kmin, 0};
             done = true;
+            // a small kept set is drawn by revisiting only the vectors that hold it
+            const CompactDraw cd = compact_draw<NV>(sh, rp, row16, vmax, V, nullptr, (double)sh.code[0] * 0x1p-24, tid);
+            y = cd.y;
+            drawn = cd.used;
         }
     }
     if (!done) {
@@ -421,7 +604,7 @@ __global__ __launch_bounds__(kFvBlock) void sample_kernel(
     }
     __syncthreads();
     const double uf = (double)sh.code[0] * 0x1p-24;
-    int64_t y = fused_draw<T, false>(sh, rp, row, nullptr, V, uf);
+    if (!drawn) y = fused_draw<T, false>(sh, rp, row, nullptr, V, uf);
     if (y < 0) y = (int64_t)(((uint64_t)sh.code[0] * (uint64_t)V) >> 24);
     if (tid == 0) tokens[b] = (int32_t)y;
 }

@@ -705,10 +705,14 @@ struct RrStats {
 // keeps the keys whose value v satisfies (v - m) >= T ln(min(mp, 1)) in
 // double, the smallest such key found by binary search (keys order like their
 // values); the kept key is the largest of the three thresholds.
-template <int NV, bool JOINT = false>
+//
+// vmax (not NULL): receives the largest key of each of the thread's vectors,
+// two 16-bit keys per word (vector v in bits 16 * (v & 1) of word v / 2), so
+// that a caller can revisit only the vectors that hold kept keys.
+template <int NV, bool JOINT = false, bool VMAX = false>
 __device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restrict__ row, int64_t V, float Tm,
-                                         int32_t k, float tp, int tid, u32x4 (&w)[NV], RrStats& st,
-                                         float mp = 0.0f) {
+                                         int32_t k, float tp, int tid, u32x4 (&w)[NV], RrStats& st, float mp,
+                                         uint32_t (&vmax)[(NV + 1) / 2]) {
     const __amdgpu_buffer_rsrc_t rin = make_rsrc(row, (uint32_t)(V * 2));
     const int vfull = (int)(V / (kRrBlock * 8));   // vectors in range for every thread
     auto ebase = [&](int v) { return (v * kRrBlock + tid) * 8; };
@@ -737,7 +741,12 @@ __device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restric
         x.y = keys_of_pair(x.y);
         x.z = keys_of_pair(x.z);
         x.w = keys_of_pair(x.w);
-        lk = max(lk, vec_max_key(x));
+        const uint32_t vk = vec_max_key(x);
+        lk = max(lk, vk);
+        if constexpr (VMAX) {
+            if (v & 1) vmax[v >> 1] |= vk << 16;
+            else vmax[v >> 1] = vk;
+        }
         visit8(x, [&](uint32_t key, int) { hist_add(sh, key); });
         w[v] = x;
         SV_VEC_FENCE();
@@ -845,6 +854,14 @@ __device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restric
 
     st = RrStats{m, scale, inv, kmin, table};
     return true;
+}
+
+template <int NV, bool JOINT = false>
+__device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restrict__ row, int64_t V, float Tm,
+                                         int32_t k, float tp, int tid, u32x4 (&w)[NV], RrStats& st,
+                                         float mp = 0.0f) {
+    uint32_t unused[(NV + 1) / 2];
+    return rr_stats<NV, JOINT, false>(sh, row, V, Tm, k, tp, tid, w, st, mp, unused);
 }
 
 // One register-resident row (rr_stats), then the output written with 16-byte
