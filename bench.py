@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--workload", default="large_vocab_chain_reject",
                     choices=["large_vocab_chain_reject", "large_vocab_target_only", "large_vocab_ragged",
                              "large_vocab_ragged_d2t", "d2t_expand",
-                             "sample", "topk_topp_chain", "greedy",
+                             "sample", "topk_topp_chain", "topk_topp_fused", "greedy",
                              "mixed", "mixed_fused"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
@@ -731,6 +731,49 @@ class TopkToppWorkload:
                 "sample": f"{n} requests, {el:.1f}s single-threaded numpy"}
 
 
+class TopkToppFusedWorkload(TopkToppWorkload):
+    """The top-k/top-p batch (B=64 D=3 V=32000 bf16, T 0.7, k 50, top_p 0.9) through the fused call: target rows
+    from logits and chain rejection in one call, no probabilities stored.  64 x 4 rows fit one per CU, so the
+    call evaluates every row of a request at once and assembles the chain in a second, tiny kernel."""
+    name = "topk_topp_fused"
+    kernel = "verify_fused_rows_kernel"
+    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_common.hpp")
+    counters = "verify_fused_topk_topp_counters.txt"
+
+    def __init__(self, dev, replicas):
+        super().__init__(dev, replicas)
+        self.calls = {"verify_fused": self.fused}
+
+    def fused(self, i):
+        r = self.reps[i % self.R]
+        self.sv.verify_fused(r["z"], r["T"], r["q"], r["x"], r["seed"], r["off"], top_k=r["k"], top_p=r["p"],
+                             out=(self.acc, self.alen))
+
+    def step(self, i):
+        self.fused(i)
+
+    def algorithmic_bytes(self):
+        """The method's bytes: logit rows 0..L, the draft row at the entries row L keeps (one 64-byte line
+        each) on a rejection, q at the probed ids.  (The call reads every row of a request to evaluate them at
+        once; the counters show that.)"""
+        import torch
+        N, D, V = self.D + 1, self.D, self.V
+        self.step(0)
+        L = self.alen.cpu().numpy().astype(np.int64)
+        r = self.reps[0]
+        probs = self.sv.softmax_renorm(r["z"], r["T"], r["k"], r["p"])
+        kept = (probs > 0).sum(-1).cpu().numpy().astype(np.int64)[np.arange(self.B), np.minimum(L, D)]
+        del probs
+        torch.cuda.empty_cache()
+        self.bytes_by_call = {"verify_fused": float(((L + 1) * V * 2 + np.where(L < D, np.minimum(
+            4 * V, PROBE_GRANULE * kept), 0) + PROBE_GRANULE * np.minimum(L + 1, D)).sum())}
+        self.L = L
+        return self.bytes_by_call["verify_fused"]
+
+    def extra(self):
+        return {"mean_accept_length": round(float(self.L.mean()), 4)}
+
+
 class MixedWorkload:
     """B=1024 D=7 V=129280 bf16 logits, 256 requests per mode, each mode through req_index.  R = 4
     replicas (logits, draft rows and probability buffers at distinct addresses, Philox offsets
@@ -929,8 +972,8 @@ class MixedFusedWorkload(MixedWorkload):
 
 WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, RaggedD2tWorkload,
                                  DraftVocabWorkload,
-                                 SampleWorkload, GreedyWorkload, TopkToppWorkload, MixedWorkload,
-                                 MixedFusedWorkload)}
+                                 SampleWorkload, GreedyWorkload, TopkToppWorkload, TopkToppFusedWorkload,
+                                 MixedWorkload, MixedFusedWorkload)}
 
 
 def _spread(us):

@@ -32,8 +32,8 @@
  * - stream is a hipStream_t passed as void*; NULL is the default stream.
  *   Calls are asynchronous; nothing is read back to the host.  The library
  *   never synchronises and never allocates device memory: every call uses
- *   only its arguments (chain rejection takes a caller-owned workspace when
- *   a request's row is split over several workgroups; see there).
+ *   only its arguments (chain rejection and the fused verify take a
+ *   caller-owned workspace for small batches; see there).
  * - Host-side validation runs before any HIP call.  Return codes:
  *   SPECVERIFY_OK, SPECVERIFY_INVALID_ARGUMENT (nothing launched),
  *   SPECVERIFY_UNSUPPORTED (current device is not gfx950),
@@ -375,18 +375,40 @@ int specverify_gumbel_sample(const void* target_logits, int dtype, const float* 
  * accepted_tokens [B, D+1] int32   output
  * accept_length   [B] int32        output
  *
+ * workspace, workspace_bytes
+ *                 caller-owned device memory or NULL.  Small batches (D > 0
+ *                 and n_req * (D + 1) at most 256 and at most the device's
+ *                 compute units) evaluate every target row of a request at
+ *                 once, one workgroup per row, and need
+ *                 specverify_verify_fused_workspace_bytes(n_req, D) bytes of
+ *                 per-request counters (4-byte aligned, all zero when a call
+ *                 starts; every call leaves them zero, so zero it once and
+ *                 reuse it; calls sharing it must not overlap).  With NULL,
+ *                 those batches evaluate a request's rows in order instead
+ *                 (same results, longer latency).  A short or misaligned
+ *                 workspace returns SPECVERIFY_INVALID_ARGUMENT.
+ *
  * Equivalent to specverify_softmax_renorm on the logits followed by
  * specverify_chain_reject on its output (same tokens whenever that output
- * buffer is 16-byte aligned), except that only logit rows 0..L of a request
- * are read and no probability is stored.  V <= 524288.  Uses no device
- * memory besides its arguments.
+ * buffer is 16-byte aligned, except draws within the double-rounding band of
+ * a CDF boundary, whose sums may associate differently).  Requests evaluated
+ * row by row read logit rows 0..L only; no probability is stored.
+ * V <= 524288.
  */
 int specverify_verify_fused(const void* target_logits, int dtype, const float* temperature,
                             const int32_t* top_k, const float* top_p, const float* draft_probs,
                             const int32_t* draft_ids, const uint64_t* seed, const uint64_t* offset,
                             int64_t B, int64_t D, int64_t V, const int32_t* req_index,
                             int64_t n_req, int32_t* accepted_tokens, int32_t* accept_length,
-                            void* stream);
+                            void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Workspace size of specverify_verify_fused: 4 bytes per request, rounded up
+ * to 256, when D > 0 and n_req * (D + 1) <= 256; else 0 (no workspace used).
+ * Host-only.  n_req >= 0, 0 <= D <= 16, bytes non-NULL; else
+ * SPECVERIFY_INVALID_ARGUMENT.
+ */
+int specverify_verify_fused_workspace_bytes(int64_t n_req, int64_t D, int64_t* bytes);
 
 /* Human-readable name of a status code (static string). */
 const char* specverify_status_string(int status);

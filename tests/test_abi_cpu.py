@@ -138,21 +138,41 @@ def test_greedy_and_gumbel_and_softmax_invalid_arguments():
 
 def test_verify_fused_invalid_arguments():
     L = sv.lib()
-    # (logits, dtype, T, top_k, top_p, q, x, seed, offset, B, D, V, req_index, n_req, acc, alen, stream)
-    assert L.specverify_verify_fused(P, 3, P, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    # (logits, dtype, T, top_k, top_p, q, x, seed, offset, B, D, V, req_index, n_req, acc, alen, workspace,
+    #  workspace_bytes, stream)
+    assert L.specverify_verify_fused(P, 3, P, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "dtype=3" in L.specverify_last_error().decode()
-    assert L.specverify_verify_fused(P, 1, None, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_verify_fused(P, 1, None, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "temperature" in L.specverify_last_error().decode()
-    assert L.specverify_verify_fused(P, 1, P, None, None, None, P, P, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_verify_fused(P, 1, P, None, None, None, P, P, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "draft_probs" in L.specverify_last_error().decode()
-    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 17, 10, None, 4, P, P, None) == 1
-    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 3, 600000, None, 4, P, P, None) == 1
+    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 17, 10, None, 4, P, P, None, 0, None) == 1
+    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 3, 600000, None, 4, P, P, None, 0, None) == 1
     assert "exceeds" in L.specverify_last_error().decode()
-    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, None, P, 4, 3, 10, None, 4, P, P, None) == 1
+    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, None, P, 4, 3, 10, None, 4, P, P, None, 0, None) == 1
     assert "seed" in L.specverify_last_error().decode()
     # n_req = 0 is a no-op that touches no device
     assert L.specverify_verify_fused(None, 0, None, None, None, None, None, None, None, 4, 3, 10, P, 0, None, None,
-                                     None) == 0
+                                     None, 0, None) == 0
+    # a workspace shorter than the query, or misaligned, is refused before any device call
+    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P, P, 8, None) == 1
+    assert "needs 256" in L.specverify_last_error().decode()
+    assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P,
+                                     ctypes.c_void_p(0x1002), 256, None) == 1
+    assert "aligned" in L.specverify_last_error().decode()
+
+
+def test_verify_fused_workspace_query():
+    out = ctypes.c_int64(-1)
+    L = sv.lib()
+    assert L.specverify_verify_fused_workspace_bytes(64, 3, ctypes.byref(out)) == 0 and out.value == 256
+    assert L.specverify_verify_fused_workspace_bytes(85, 2, ctypes.byref(out)) == 0 and out.value == 512
+    # past 256 rows, or without drafts, no workspace is used
+    assert L.specverify_verify_fused_workspace_bytes(65, 3, ctypes.byref(out)) == 0 and out.value == 0
+    assert L.specverify_verify_fused_workspace_bytes(100, 0, ctypes.byref(out)) == 0 and out.value == 0
+    assert L.specverify_verify_fused_workspace_bytes(-1, 3, ctypes.byref(out)) == 1
+    assert L.specverify_verify_fused_workspace_bytes(4, 17, ctypes.byref(out)) == 1
+    assert sv.verify_fused_workspace_bytes(64, 3) == 256
 
 
 def test_chain_reject_ragged_invalid_arguments():

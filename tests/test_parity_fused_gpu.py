@@ -175,3 +175,58 @@ def test_verify_fused_other_row_paths(sv):
         ref = oracle.verify_fused(c["logits"], dt, T, k, p, c["draft_probs"], c["draft_ids"], c["seed"],
                                   c["offset"])
         assert_match(A, Ls, ref, range(B), (V, dt, D, shift))
+
+
+def test_verify_fused_row_mode_matches_serial(sv):
+    """Small batches evaluate every row at once (one workgroup per row, the
+    caller's counters); with no workspace the same call walks each request's
+    rows in order.  Both must agree bit for bit, also through a request
+    subset that lists requests twice, and the counters must be zero after
+    every call; the oracle is checked as well."""
+    import ctypes
+    torch = __import__("torch")
+    L = sv.lib()
+    for i, (B, D, V, dt) in enumerate(((64, 3, 32000, "bf16"), (20, 7, 4096, "bf16"), (6, 16, 1001, "f32"),
+                                       (40, 5, 8192, "bf16"))):
+        N = D + 1
+        c = fuzz_case(1900 + i, B, D, V, dt)
+        rng = np.random.default_rng(1900 + i)
+        T = rng.uniform(0.5, 1.3, B).astype(np.float32)
+        T[::7] = 0.0
+        k = np.where(rng.random(B) < 0.5, rng.choice([0, 5, 50, 200], B), 0).astype(np.int32)
+        p = np.where(rng.random(B) < 0.5, rng.uniform(0.6, 0.99, B), 1.0).astype(np.float32)
+        z = dev_logits(c["logits"], dt)
+        args = [dev(T), dev(c["draft_probs"]), dev(c["draft_ids"]), dev(c["seed"]), dev(c["offset"])]
+        log(f"fused row mode vs serial {i}: B={B} D={D} V={V} dtype={dt}")
+        ws = torch.zeros(sv.verify_fused_workspace_bytes(B, D), dtype=torch.uint8, device="cuda")
+        assert ws.numel() > 0
+        acc, alen = sv.verify_fused(z, args[0], *args[1:], top_k=dev(k), top_p=dev(p), workspace=ws)
+        assert not bool((ws != 0).any().item())
+        acc2 = torch.full((B, N), SENTINEL, dtype=torch.int32, device="cuda")
+        alen2 = torch.full((B,), SENTINEL, dtype=torch.int32, device="cuda")
+        dtype_code = sv.BF16 if dt == "bf16" else sv.F32
+        kk, pp = dev(k), dev(p)
+        st = L.specverify_verify_fused(
+            ctypes.c_void_p(z.data_ptr()), dtype_code, ctypes.c_void_p(args[0].data_ptr()),
+            ctypes.c_void_p(kk.data_ptr()), ctypes.c_void_p(pp.data_ptr()), ctypes.c_void_p(args[1].data_ptr()),
+            ctypes.c_void_p(args[2].data_ptr()), ctypes.c_void_p(args[3].data_ptr()),
+            ctypes.c_void_p(args[4].data_ptr()), B, D, V, None, B, ctypes.c_void_p(acc2.data_ptr()),
+            ctypes.c_void_p(alen2.data_ptr()), None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0, L.specverify_last_error()
+        assert np.array_equal(np_i(acc), np_i(acc2)) and np.array_equal(np_i(alen), np_i(alen2)), (B, D, V)
+        ref = oracle.verify_fused(c["logits"], dt, T, k, p, c["draft_probs"], c["draft_ids"], c["seed"],
+                                  c["offset"])
+        assert_match(np_i(acc), np_i(alen), ref, range(B), ("row mode", B, D, V))
+        # a subset listing requests twice: each listed request as in the full call, others untouched
+        reqs = np.array([3, 1, 3, 0, 1, 5], np.int32)
+        acc3 = torch.full((B, N), SENTINEL, dtype=torch.int32, device="cuda")
+        alen3 = torch.full((B,), SENTINEL, dtype=torch.int32, device="cuda")
+        sv.verify_fused(z, args[0], *args[1:], top_k=kk, top_p=pp, req_index=dev(reqs), out=(acc3, alen3),
+                        workspace=ws)
+        a3, l3 = np_i(acc3), np_i(alen3)
+        for b in range(B):
+            if b in reqs:
+                assert np.array_equal(a3[b], np_i(acc)[b]) and l3[b] == np_i(alen)[b], (b, B, D, V)
+            else:
+                assert np.all(a3[b] == SENTINEL) and l3[b] == SENTINEL
+        assert not bool((ws != 0).any().item())

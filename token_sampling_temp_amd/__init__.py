@@ -24,7 +24,8 @@ Functions mirror the C entry points:
 * ``greedy_verify(target_logits, draft_ids, req_index=None, ...)``
 * ``gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, ...)``
 * ``verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None,
-  top_p=None, req_index=None)``: softmax_renorm followed by chain_reject in one launch
+  top_p=None, req_index=None, workspace=None)``: softmax_renorm followed by chain_reject in one call;
+  ``verify_fused_workspace_bytes(n_req, D)``: its counters for small batches
 
 ``accept_length`` is the number of accepted drafts L in [0, D]; a request
 emits L + 1 tokens.
@@ -54,6 +55,7 @@ SYMBOLS = (
     "specverify_greedy_verify",
     "specverify_gumbel_sample",
     "specverify_verify_fused",
+    "specverify_verify_fused_workspace_bytes",
     "specverify_sample",
     "specverify_status_string",
     "specverify_last_error",
@@ -92,12 +94,15 @@ def lib() -> ctypes.CDLL:
     L.specverify_d2t_expand.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
-    L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp,
+                                          i64, vp]
+    L.specverify_verify_fused_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_int64)]
     L.specverify_sample.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, i64, vp, vp]
     for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_chain_workspace_bytes",
                  "specverify_chain_reject_noalloc", "specverify_chain_reject_ragged",
                  "specverify_d2t_inverse", "specverify_d2t_expand", "specverify_greedy_verify",
-                 "specverify_gumbel_sample", "specverify_verify_fused", "specverify_sample"):
+                 "specverify_gumbel_sample", "specverify_verify_fused", "specverify_verify_fused_workspace_bytes",
+                 "specverify_sample"):
         getattr(L, name).restype = ctypes.c_int
     L.specverify_status_string.argtypes = [ctypes.c_int]
     L.specverify_status_string.restype = ctypes.c_char_p
@@ -303,10 +308,39 @@ def chain_reject_noalloc(draft_probs, draft_ids, target_probs, seed, offset, req
     return acc, alen
 
 
+def verify_fused_workspace_bytes(n_req, D) -> int:
+    """Bytes of per-request counters verify_fused uses for small batches (0: none)."""
+    out = ctypes.c_int64(0)
+    _check("specverify_verify_fused_workspace_bytes",
+           lib().specverify_verify_fused_workspace_bytes(int(n_req), int(D), ctypes.byref(out)))
+    return int(out.value)
+
+
+_fused_workspaces = {}
+
+
+def _fused_workspace(workspace, n_req, D, device):
+    torch = _torch()
+    n = verify_fused_workspace_bytes(n_req, D)
+    if n == 0:
+        return None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,), device, 1)
+        return workspace, int(workspace.numel())
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _fused_workspaces.get(key)
+    if ws is None or ws.numel() < n:
+        ws = torch.zeros((n,), dtype=torch.uint8, device=device)
+        _fused_workspaces[key] = ws
+    return ws, int(ws.numel())
+
+
 def verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None, top_p=None,
-                 req_index=None, out=None):
-    """Target rows from logits (softmax, top-k, top-p) then chain rejection, in one launch;
-    returns (accepted_tokens [B, D+1] int32, accept_length [B] int32)."""
+                 req_index=None, out=None, workspace=None):
+    """Target rows from logits (softmax, top-k, top-p) then chain rejection, in one call;
+    returns (accepted_tokens [B, D+1] int32, accept_length [B] int32).  Small batches use a zero-filled
+    uint8 workspace of verify_fused_workspace_bytes(n_req, D) bytes (kept per device and stream when
+    ``workspace`` is None)."""
     torch = _torch()
     _need(target_logits, "target_logits", (torch.float32, torch.bfloat16), None, 3)
     dev = target_logits.device
@@ -332,10 +366,11 @@ def verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offse
         alen = torch.empty((B,), dtype=torch.int32, device=dev)
     else:
         acc, alen = out
+    ws, ws_bytes = _fused_workspace(workspace, n_req, D, dev)
     st = lib().specverify_verify_fused(
         _ptr(target_logits), _logit_dtype(target_logits), _ptr(temperature), _ptr(top_k), _ptr(top_p),
         _ptr(draft_probs), _ptr(draft_ids), _ptr(seed), _ptr(offset), B, D, V, _ptr(req_index), n_req, _ptr(acc),
-        _ptr(alen), _stream_ptr(dev))
+        _ptr(alen), _ptr(ws), ws_bytes, _stream_ptr(dev))
     _check("specverify_verify_fused", st)
     return acc, alen
 

@@ -337,11 +337,21 @@ int specverify_sample(const void* logits, int dtype, const float* temperature, c
                                           req_index, n_req, tokens, static_cast<hipStream_t>(stream)));
 }
 
+int specverify_verify_fused_workspace_bytes(int64_t n_req, int64_t D, int64_t* bytes) {
+    const char* fn = "specverify_verify_fused_workspace_bytes";
+    SV_REQUIRE(bytes, "bytes");
+    if (n_req < 0) return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: n_req=%lld must be >= 0", fn, (long long)n_req);
+    SV_TRY(check_draft(fn, D));
+    *bytes = sv::verify_fused_workspace_bytes(n_req, (int)D);
+    g_last_error.clear();
+    return SPECVERIFY_OK;
+}
+
 int specverify_verify_fused(const void* target_logits, int dtype, const float* temperature, const int32_t* top_k,
                             const float* top_p, const float* draft_probs, const int32_t* draft_ids,
                             const uint64_t* seed, const uint64_t* offset, int64_t B, int64_t D, int64_t V,
                             const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
-                            int32_t* accept_length, void* stream) {
+                            int32_t* accept_length, void* workspace, int64_t workspace_bytes, void* stream) {
     const char* fn = "specverify_verify_fused";
     SV_TRY(check_dtype(fn, dtype));
     SV_TRY(check_draft(fn, D));
@@ -360,10 +370,17 @@ int specverify_verify_fused(const void* target_logits, int dtype, const float* t
     SV_REQUIRE(offset, "offset");
     SV_REQUIRE(accepted_tokens, "accepted_tokens");
     SV_REQUIRE(accept_length, "accept_length");
+    const int64_t need = sv::verify_fused_workspace_bytes(n_req, (int)D);
+    if (workspace && need > 0 && workspace_bytes < need)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace_bytes=%lld, n_req=%lld D=%lld needs %lld", fn,
+                    (long long)workspace_bytes, (long long)n_req, (long long)D, (long long)need);
+    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace must be 4-byte aligned", fn);
     SV_TRY(check_device());
     return launched(fn, sv::launch_verify_fused(target_logits, dtype, temperature, top_k, top_p, draft_probs,
                                                 draft_ids, seed, offset, B, (int)D, V, req_index, n_req,
-                                                accepted_tokens, accept_length, static_cast<hipStream_t>(stream)));
+                                                accepted_tokens, accept_length, need > 0 ? workspace : nullptr,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 const char* specverify_status_string(int status) {

@@ -550,6 +550,141 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_kernel(
     if (tid == 0) accept_len[b] = L;
 }
 
+// Fused verify for small batches (n_req * (D + 1) rows at most one per CU):
+// every row (request, j) gets its own workgroup, so a request's rows are
+// evaluated at the same time instead of one after another.  Each workgroup
+// computes row j's statistics and accept test exactly as verify_fused_kernel
+// does; a row that rejects (or the bonus row D) also draws its token, as it
+// would if the chain stopped there.  The row's result goes to
+// accepted[b, j] (bit 31 set for an accepted draft, else the drawn token),
+// then thread 0 adds one to the request's counter (an agent-scope release
+// RMW; the workspace holds one per request, zero between calls).  The
+// workgroup that completes the count issues an agent-scope acquire fence
+// (the counter's release sequence orders every row's result before it),
+// takes L = the first row without
+// bit 31, writes the request's tokens and resets the counter.  Rows after L
+// are read although the serial kernel would stop before them; the results
+// are bit-identical to it.  A request listed twice in req_index is done by
+// its first listing only (the others would overwrite its intermediate
+// results).
+template <typename T, int NV>
+__global__ __launch_bounds__(kFvBlock) void verify_fused_rows_kernel(
+    const T* __restrict__ logits, const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
+    const float* __restrict__ top_p, const float* __restrict__ q, const int32_t* __restrict__ x,
+    const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
+    const int32_t* __restrict__ req_index, int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len,
+    uint32_t* __restrict__ counter) {
+    __shared__ FusedShared sh;
+    const int N = D + 1;
+    const int64_t slot = blockIdx.x / N;
+    const int j = (int)(blockIdx.x - slot * N);
+    const int64_t b = req_index ? (int64_t)req_index[slot] : slot;
+    if (b < 0 || b >= B) return;   // uniform over the workgroup
+    const int tid = threadIdx.x;
+    if (req_index) {
+        // a repeated request is done by its first listing (slot < blockDim)
+        const bool dup = tid < slot && req_index[tid] == (int32_t)b;
+        if (__syncthreads_or(dup)) return;
+    }
+    const float Tm = temperature[b];
+    const int32_t k = top_k ? top_k[b] : 0;
+    const float tp = top_p ? top_p[b] : 1.0f;
+    const T* row = logits + ((int64_t)b * N + j) * V;
+    const float* qj = j < D ? q + ((int64_t)b * D + j) * V : nullptr;
+
+    // The draft id is one uniform load; q at it is loaded by thread 0 now and
+    // waited for only at the accept test, so neither holds up the row's loads.
+    // A register-resident row takes the logit at the id from the thread that
+    // holds it (rr_stats' probe); other rows read it at the test.  The
+    // uniforms are formed at the test and the draw.
+    const int32_t xj = j < D ? x[b * D + j] : -1;
+    const bool xin = xj >= 0 && (int64_t)xj < V;
+    float qx = 0.0f;
+    if (tid == 0 && xin) qx = qj[xj];
+    RowProb rp{kProbOneHot, 0.0f, 0.0f, 0.0f, 0u, 0};
+    bool probed = false;   // sh.rr.probe_key holds the key of the logit at xj
+    auto accepted_here = [&]() {   // the serial kernel's test at position j
+        if (tid == 0) {
+            bool ok = false;
+            if (xin) {
+                float pv;
+                if constexpr (sizeof(T) == 2) {
+                    if (probed) pv = key_prob(rp, sh.rr, sh.rr.probe_key);
+                    else pv = row_prob<T>(rp, sh.rr, row[xj], xj);
+                } else {
+                    pv = row_prob<T>(rp, sh.rr, row[xj], xj);
+                }
+                const uint32_t cj = uniform_code(philox_word(seed[b], offset[b], (uint64_t)j));
+                ok = (double)((float)cj * 0x1p-24f) * (double)qx < (double)pv;
+            }
+            sh.acc = ok ? 1 : 0;
+        }
+        __syncthreads();
+        return sh.acc != 0;
+    };
+    const double uf = (double)uniform_code(philox_word(seed[b], offset[b], (uint64_t)D)) * 0x1p-24;
+    bool done = false, drawn = false, acc = false;
+    int64_t y = -1;
+    if ((double)Tm < kGreedyTemperature) {
+        rp.mode = kProbOneHot;
+        rp.y = row_argmax<kFvBlock, false>(row, V, sh.rr.u.sm.am);
+    } else {
+        if constexpr (NV > 0) {
+            u32x4 w[NV];
+            uint32_t vmax[(NV + 1) / 2];
+            RrStats st;
+            const uint16_t* row16 = reinterpret_cast<const uint16_t*>(row);
+            if (rr_stats<NV, false, true>(sh.rr, row16, V, Tm, k, tp, tid, w, st, 0.0f, vmax, xin ? xj : -1)) {
+                rp = RowProb{st.table ? kProbTable : kProbRrExp, st.m, st.scale, st.inv, st.kmin, 0};
+                done = true;
+                probed = true;
+                acc = j < D && accepted_here();
+                if (!acc) {
+                    CompactDraw cd = compact_draw<NV>(sh, rp, row16, vmax, V, qj, uf, tid);
+                    if (cd.used && cd.y < 0 && qj) cd = compact_draw<NV>(sh, rp, row16, vmax, V, nullptr, uf, tid);
+                    y = cd.y;
+                    drawn = cd.used;
+                }
+            }
+        }
+        if (!done) {
+            __syncthreads();
+            const StreamStats ss = streamed_stats<T>(row, V, Tm, k, tp, sh.rr.u.sm);
+            rp = RowProb{kProbStreamed, ss.m, ss.scale, ss.inv, ss.kmin, 0};
+        }
+    }
+    if (!done) acc = j < D && accepted_here();
+    if (!acc && !drawn) {
+        y = qj ? fused_draw<T, true>(sh, rp, row, qj, V, uf) : fused_draw<T, false>(sh, rp, row, nullptr, V, uf);
+        if (y < 0 && qj) y = fused_draw<T, false>(sh, rp, row, nullptr, V, uf);
+    }
+    if (!acc && y < 0) y = (int64_t)(((uint64_t)(uf * 0x1p24) * (uint64_t)V) >> 24);
+    if (tid == 0) {
+        accepted[b * N + j] = acc ? (int32_t)0x80000000u : (int32_t)y;
+        const uint32_t done_rows =
+            __hip_atomic_fetch_add(&counter[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        const bool last = done_rows == (uint32_t)N;
+        // only the request's last workgroup acquires: it reads the other rows' results
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        sh.acc = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (!sh.acc) return;
+    // the request's last row: L = the first row without the accept bit (D if
+    // none); tokens x_0..x_{L-1}, the token drawn on row L, then -1
+    if (tid < kWave) {
+        const int32_t v = tid < N ? accepted[b * N + tid] : 0;
+        const uint64_t rej = __ballot(tid < D && v >= 0);
+        const int L = rej ? __ffsll((unsigned long long)rej) - 1 : D;
+        const int32_t yl = read_lane(v, L);
+        if (tid < N) accepted[b * N + tid] = tid < L ? x[b * D + tid] : (tid == L ? yl : -1);
+        if (tid == 0) {
+            accept_len[b] = L;
+            __hip_atomic_store(&counter[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 // Single-step sampling ("tokenspeed sampling/backends/flashinfer.py",
 // sample: softmax(logits, T), then top_k_top_p_sampling_from_probs with the
 // joint filter order, per-request seed and offset; min-p as TensorRT-LLM's
@@ -641,11 +776,37 @@ hipError_t launch_sample(const void* logits, int dtype, const float* temperature
 
 int64_t verify_fused_max_vocab() { return (int64_t)kFvMaxChunks * kFvChunk; }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+static int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+int64_t verify_fused_workspace_bytes(int64_t n_req, int D) {
+    return (D > 0 && n_req > 0 && n_req * (D + 1) <= kFusedRowsMax) ? (n_req * 4 + 255) / 256 * 256 : 0;
+}
+
 template <typename T, int NV>
 static void launch_fv(const T* logits, const float* temperature, const int32_t* top_k, const float* top_p,
                       const float* q, const int32_t* x, const uint64_t* seed, const uint64_t* offset, int64_t B,
                       int D, int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted,
-                      int32_t* accept_len, hipStream_t stream) {
+                      int32_t* accept_len, void* workspace, hipStream_t stream) {
+    // small batches: one workgroup per row when every row fits on its own CU
+    // (and the caller gave the per-request counters)
+    const int64_t rows = n_req * (D + 1);
+    if (workspace && verify_fused_workspace_bytes(n_req, D) > 0 && rows <= device_cus()) {
+        hipLaunchKernelGGL((verify_fused_rows_kernel<T, NV>), dim3((unsigned)rows), dim3(kFvBlock), 0, stream,
+                           logits, temperature, top_k, top_p, q, x, seed, offset, B, D, V, req_index, accepted,
+                           accept_len, static_cast<uint32_t*>(workspace));
+        return;
+    }
     hipLaunchKernelGGL((verify_fused_kernel<T, NV>), dim3((unsigned)n_req), dim3(kFvBlock), 0, stream, logits,
                        temperature, top_k, top_p, q, x, seed, offset, B, D, V, req_index, accepted, accept_len);
 }
@@ -654,7 +815,7 @@ hipError_t launch_verify_fused(const void* logits, int dtype, const float* tempe
                                const float* top_p, const float* draft_probs, const int32_t* draft_ids,
                                const uint64_t* seed, const uint64_t* offset, int64_t B, int D, int64_t V,
                                const int32_t* req_index, int64_t n_req, int32_t* accepted, int32_t* accept_len,
-                               hipStream_t stream) {
+                               void* workspace, hipStream_t stream) {
     if (V > verify_fused_max_vocab()) return hipErrorInvalidValue;
     if (dtype == kDtypeBF16) {
         const uint16_t* lg = static_cast<const uint16_t*>(logits);
@@ -663,7 +824,7 @@ hipError_t launch_verify_fused(const void* logits, int dtype, const float* tempe
         const bool rr = (V & 7) == 0 && (uintptr_t)lg % 16 == 0 && nv <= 20;
 #define SV_FV(NVV) \
     launch_fv<uint16_t, NVV>(lg, temperature, top_k, top_p, draft_probs, draft_ids, seed, offset, B, D, V, req_index, \
-                             n_req, accepted, accept_len, stream)
+                             n_req, accepted, accept_len, workspace, stream)
         if (!rr) SV_FV(0);
         else if (nv <= 1) SV_FV(1);
         else if (nv <= 2) SV_FV(2);
@@ -675,7 +836,7 @@ hipError_t launch_verify_fused(const void* logits, int dtype, const float* tempe
 #undef SV_FV
     } else {
         launch_fv<float, 0>(static_cast<const float*>(logits), temperature, top_k, top_p, draft_probs, draft_ids,
-                            seed, offset, B, D, V, req_index, n_req, accepted, accept_len, stream);
+                            seed, offset, B, D, V, req_index, n_req, accepted, accept_len, workspace, stream);
     }
     return hipGetLastError();
 }

@@ -64,11 +64,17 @@ hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temp
                                 hipStream_t stream);
 
 // Fused target rows + chain rejection (V <= verify_fused_max_vocab()).
+// Batches of at most kFusedRowsMax rows (n_req * (D + 1)) may evaluate every
+// row at once when given a workspace of verify_fused_workspace_bytes(n_req, D)
+// bytes (per-request counters, zero between calls); otherwise, or with none,
+// a request's rows are evaluated in order.
+constexpr int64_t kFusedRowsMax = 256;
 int64_t verify_fused_max_vocab();
+int64_t verify_fused_workspace_bytes(int64_t n_req, int D);
 hipError_t launch_verify_fused(const void* logits, int dtype, const float* temperature, const int32_t* top_k,
                                const float* top_p, const float* draft_probs, const int32_t* draft_ids,
                                const uint64_t* seed, const uint64_t* offset, int64_t B, int D, int64_t V,
                                const int32_t* req_index, int64_t n_req, int32_t* accepted, int32_t* accept_len,
-                               hipStream_t stream);
+                               void* workspace, hipStream_t stream);
 
 }  // namespace sv

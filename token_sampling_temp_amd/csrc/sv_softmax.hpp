@@ -356,6 +356,7 @@ struct RrShared {
     uint32_t sel_digit;              // selected key (top-k, top-p)
     uint64_t sel_above;              // a wave-0 result handed to the block
     uint64_t sel_mass;               // mass at or above the top-p key
+    uint32_t probe_key;              // the key of one requested element (rr_stats with a probe index)
 };
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
@@ -709,10 +710,12 @@ struct RrStats {
 // vmax (not NULL): receives the largest key of each of the thread's vectors,
 // two 16-bit keys per word (vector v in bits 16 * (v & 1) of word v / 2), so
 // that a caller can revisit only the vectors that hold kept keys.
+// probe (>= 0): the key of element `probe` is left in sh.probe_key (by the
+// thread that holds it, before the selection's barriers).
 template <int NV, bool JOINT = false, bool VMAX = false>
 __device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restrict__ row, int64_t V, float Tm,
                                          int32_t k, float tp, int tid, u32x4 (&w)[NV], RrStats& st, float mp,
-                                         uint32_t (&vmax)[(NV + 1) / 2]) {
+                                         uint32_t (&vmax)[(NV + 1) / 2], int64_t probe = -1) {
     const __amdgpu_buffer_rsrc_t rin = make_rsrc(row, (uint32_t)(V * 2));
     const int vfull = (int)(V / (kRrBlock * 8));   // vectors in range for every thread
     auto ebase = [&](int v) { return (v * kRrBlock + tid) * 8; };
@@ -746,6 +749,11 @@ __device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restric
         if constexpr (VMAX) {
             if (v & 1) vmax[v >> 1] |= vk << 16;
             else vmax[v >> 1] = vk;
+        }
+        if (probe >= 0 && (probe >> 3) == (int64_t)(v * kRrBlock + tid)) {
+            const int i = (int)(probe & 7);
+            const uint32_t wd = i < 2 ? x.x : (i < 4 ? x.y : (i < 6 ? x.z : x.w));
+            sh.probe_key = (wd >> (16 * (i & 1))) & 0xFFFFu;
         }
         visit8(x, [&](uint32_t key, int) { hist_add(sh, key); });
         w[v] = x;
