@@ -32,8 +32,8 @@
  * - stream is a hipStream_t passed as void*; NULL is the default stream.
  *   Calls are asynchronous; nothing is read back to the host.  The library
  *   never synchronises and never allocates device memory: every call uses
- *   only its arguments (chain rejection and the fused verify take a
- *   caller-owned workspace for small batches; see there).
+ *   only its arguments (chain rejection, greedy verify, Gumbel sampling
+ *   and the fused verify take an optional caller-owned workspace; see there).
  * - Host-side validation runs before any HIP call.  Return codes:
  *   SPECVERIFY_OK, SPECVERIFY_INVALID_ARGUMENT (nothing launched),
  *   SPECVERIFY_UNSUPPORTED (current device is not gfx950),
@@ -65,7 +65,7 @@ extern "C" {
 #define SPECVERIFY_MAX_DRAFT 16
 #define SPECVERIFY_STATIC_SCRATCH_BYTES (4 << 20)
 #define SPECVERIFY_RNG_SLOT_SPAN 32
-#define SPECVERIFY_VERSION 200
+#define SPECVERIFY_VERSION 201
 
 /*
  * Temperature softmax followed by top-k then top-p renormalisation.
@@ -317,15 +317,32 @@ int specverify_sample(const void* logits, int dtype, const float* temperature, c
  *                                          (flat index into predict)
  * argmax_out      [B, D+1] int32 or NULL   output: y_j for every j; requesting
  *                                          it makes every row be read
- * Rows after the first mismatch are not read unless argmax_out is given.
- * Equal values (including -0 and +0) tie; a NaN counts as the maximum, and
- * the first NaN wins.
+ * workspace, workspace_bytes
+ *                 caller-owned device memory (8-byte aligned) of at least
+ *                 specverify_greedy_verify_workspace_bytes(n_req, D) bytes,
+ *                 or NULL.  With it every (request, row) gets a workgroup of
+ *                 its own, and a row whose request already failed at an
+ *                 earlier row stops reading; without it one workgroup per
+ *                 request walks its rows in order.  The results are the same.
+ *                 Its contents must be zero before the first call and are
+ *                 left zero by every call; calls that share one workspace
+ *                 must not overlap in time (same stream, or ordered).
+ * Rows after the first mismatch are not needed unless argmax_out is given
+ * (then every row is read).  Equal values (including -0 and +0) tie; a NaN
+ * counts as the maximum, and the first NaN wins.
  */
 int specverify_greedy_verify(const void* target_logits, int dtype, const int32_t* draft_ids,
                              int64_t B, int64_t D, int64_t V, const int32_t* req_index,
                              int64_t n_req, int32_t* accepted_tokens, int32_t* accept_length,
                              int32_t* predict, int32_t* accept_index, int32_t* argmax_out,
-                             void* stream);
+                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes specverify_greedy_verify can use for n_req requests with D
+ * drafts (0: it uses none).  *bytes = 0 when D == 0 or n_req == 0, else
+ * 128 * n_req (one 128-byte line per request) rounded up to 256.  Host-only.
+ */
+int specverify_greedy_verify_workspace_bytes(int64_t n_req, int64_t D, int64_t* bytes);
 
 /*
  * Temperature-only target sampling by Gumbel-max, then strict chain acceptance.
@@ -347,14 +364,25 @@ int specverify_greedy_verify(const void* target_logits, int dtype, const int32_t
  * Row j of request b: s_v = z_v / T + G_v, G_v = -ln(-ln u_v), u_v the uniform
  * of word v of stream (seed_b, offset_b + 32 j); y_j = lowest-index argmax of
  * s, computed in float.  The stream spacing of 32 per row follows the page's
- * _RNG_SLOT_SPAN.  Rows after the first mismatch are not read unless
- * sampled_out is given.
+ * _RNG_SLOT_SPAN.  Rows after the first mismatch are not needed unless
+ * sampled_out is given (then every row is read).
+ *
+ * workspace, workspace_bytes
+ *                 as for specverify_greedy_verify, sized by
+ *                 specverify_gumbel_sample_workspace_bytes(n_req, D).
  */
 int specverify_gumbel_sample(const void* target_logits, int dtype, const float* temperature,
                              const int32_t* draft_ids, const uint64_t* seed,
                              const uint64_t* offset, int64_t B, int64_t D, int64_t V,
                              const int32_t* req_index, int64_t n_req, int32_t* accepted_tokens,
-                             int32_t* accept_length, int32_t* sampled_out, void* stream);
+                             int32_t* accept_length, int32_t* sampled_out, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes specverify_gumbel_sample can use (0: it uses none); the
+ * same size as specverify_greedy_verify_workspace_bytes.  Host-only.
+ */
+int specverify_gumbel_sample_workspace_bytes(int64_t n_req, int64_t D, int64_t* bytes);
 
 /*
  * Fused verify: target rows from logits, then chain rejection, in one call.

@@ -90,6 +90,11 @@ def test_greedy_verify_fuzz(sv):
         out2 = sv.greedy_verify(z, dev(x))
         for k in ("accepted_tokens", "accept_length", "predict", "accept_index"):
             assert np.array_equal(np_i(out2[k]), ref[k]), (k, V, D, dt)
+        # the one-workgroup-per-request form (no workspace), with and without every argmax
+        for am in (True, False):
+            out3 = sv.greedy_verify(z, dev(x), argmax=am, workspace=False)
+            for k in ("accepted_tokens", "accept_length", "predict", "accept_index") + (("argmax",) if am else ()):
+                assert np.array_equal(np_i(out3[k]), ref[k]), (k, V, D, dt, am)
 
 
 def test_greedy_special_values(sv):
@@ -145,6 +150,62 @@ def test_greedy_config4_full(sv):
     assert np.array_equal(ref["argmax"], c["planted"])
     out2 = sv.greedy_verify(dev_logits(c["logits"], "bf16"), dev(c["draft_ids"]))
     assert np.array_equal(np_i(out2["accepted_tokens"]), ref["accepted_tokens"])
+    out3 = sv.greedy_verify(dev_logits(c["logits"], "bf16"), dev(c["draft_ids"]), workspace=False)
+    for k in ("accepted_tokens", "accept_length", "predict", "accept_index"):
+        assert np.array_equal(np_i(out3[k]), ref[k]), k
+
+
+def _rowpar_subset_case(sv, fn, ws_query, check):
+    """Both strict-acceptance calls through an explicit workspace: a request
+    subset with a repeated row and indices outside [0, B), then a smaller
+    batch on the same workspace; outputs against the one-workgroup-per-request
+    form (bit-exact: same row arithmetic), untouched rows keep their sentinel,
+    and the workspace is zero after every call."""
+    torch = __import__("torch")
+    B, D, V = 40, 5, 4099
+    c = fuzz_case(77, B, D, V, "bf16")
+    rng = np.random.default_rng(77)
+    x = greedy_drafts(rng, c["logits"], "bf16", D, 0.9)
+    T = np.where(np.arange(B) % 3 == 0, 0.0, 0.8).astype(np.float32)
+    z = dev_logits(c["logits"], "bf16")
+    for idx in (np.array([3, 7, 7, 39, -1, 40, 0, 12, 5, 6, 8, 9, 10, 11, 13, 2], np.int32),
+                np.array([1, 4], np.int32)):
+        n = len(idx)
+        ws = torch.zeros((ws_query(n, D),), dtype=torch.uint8, device="cuda")
+        outs = []
+        for w in (ws, False):
+            acc = torch.full((B, D + 1), SENTINEL, dtype=torch.int32, device="cuda")
+            alen = torch.full((B,), SENTINEL, dtype=torch.int32, device="cuda")
+            fn(z, dev(x), dev(T), c, dev(idx), {"accepted_tokens": acc, "accept_length": alen}, w)
+            outs.append((np_i(acc), np_i(alen)))
+            if w is not False:
+                assert int(ws.cpu().numpy().astype(np.int64).sum()) == 0, "workspace left non-zero"
+        assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+        valid = sorted(set(int(b) for b in idx if 0 <= b < B))
+        untouched = np.setdiff1d(np.arange(B), valid)
+        assert np.all(outs[0][1][untouched] == SENTINEL)
+        check(outs[0][0], outs[0][1], c, x, T, valid)
+
+
+def test_greedy_rowpar_workspace_subset(sv):
+    def fn(z, x, T, c, idx, out, w):
+        sv.greedy_verify(z, x, req_index=idx, predict=False, accept_index=False, out=out, workspace=w)
+    def check(A, Ls, c, x, T, valid):
+        ref = oracle.greedy_verify(c["logits"], "bf16", x, requests=valid)
+        for b in valid:
+            assert list(A[b]) == list(ref["accepted_tokens"][b]) and Ls[b] == ref["accept_length"][b], b
+    log("greedy row-parallel: subset with repeats and invalid indices, explicit workspace")
+    _rowpar_subset_case(sv, fn, sv.greedy_verify_workspace_bytes, check)
+
+
+def test_gumbel_rowpar_workspace_subset(sv):
+    def fn(z, x, T, c, idx, out, w):
+        sv.gumbel_sample(z, T, x, dev(c["seed"]), dev(c["offset"]), req_index=idx, out=out, workspace=w)
+    def check(A, Ls, c, x, T, valid):
+        ref = oracle.gumbel_sample(c["logits"], "bf16", T, x, c["seed"], c["offset"], requests=valid)
+        assert_chain_match(A, Ls, ref, valid, "gumbel row-parallel subset", len_exact=False, max_excluded=1)
+    log("Gumbel row-parallel: subset with repeats and invalid indices, explicit workspace")
+    _rowpar_subset_case(sv, fn, sv.gumbel_sample_workspace_bytes, check)
 
 
 # --------------------------------------------------------------------------- chain rejection
@@ -786,6 +847,14 @@ def test_gumbel_sample_fuzz(sv):
                            len_exact=False, max_excluded=B)
         out2 = sv.gumbel_sample(dev_logits(c["logits"], dt), dev(T), dev(x), dev(c["seed"]), dev(c["offset"]))
         assert np.array_equal(np_i(out2["accepted_tokens"]), np_i(out["accepted_tokens"]))
+        # the one-workgroup-per-request form computes the same rows
+        for smp in (True, False):
+            out3 = sv.gumbel_sample(dev_logits(c["logits"], dt), dev(T), dev(x), dev(c["seed"]), dev(c["offset"]),
+                                    sampled=smp, workspace=False)
+            assert np.array_equal(np_i(out3["accepted_tokens"]), np_i(out["accepted_tokens"]))
+            assert np.array_equal(np_i(out3["accept_length"]), np_i(out["accept_length"]))
+            if smp:
+                assert np.array_equal(np_i(out3["sampled"]), s_gpu)
     log(f"gumbel fuzz flagged requests: {flagged}")
 
 
@@ -818,6 +887,15 @@ def test_config5_mixed_modes_full(sv):
     sv.softmax_renorm(z, T, dev(c["top_k"]), dev(c["top_p"]), req_index=dev(filt), out=probs)
     sv.chain_reject(dev(c["draft_probs"]), x, probs, seed, off, req_index=dev(filt), out=(acc, alen))
     A, Ls = np_i(acc), np_i(alen)
+    # greedy and Gumbel in their one-workgroup-per-request form: identical outputs
+    acc1 = torch.full((B, N), SENTINEL, dtype=torch.int32, device="cuda")
+    alen1 = torch.full((B,), SENTINEL, dtype=torch.int32, device="cuda")
+    sv.greedy_verify(z, x, req_index=dev(idx[MODE_GREEDY]), predict=False, accept_index=False,
+                     out={"accepted_tokens": acc1, "accept_length": alen1}, workspace=False)
+    sv.gumbel_sample(z, T, x, seed, off, req_index=dev(idx[MODE_TEMPERATURE]),
+                     out={"accepted_tokens": acc1, "accept_length": alen1}, workspace=False)
+    both = np.concatenate([idx[MODE_GREEDY], idx[MODE_TEMPERATURE]])
+    assert np.array_equal(np_i(acc1)[both], A[both]) and np.array_equal(np_i(alen1)[both], Ls[both])
     assert np.all((Ls >= 0) & (Ls <= D))
     for b in range(B):
         assert np.all(A[b, Ls[b] + 1:] == -1) and np.all(A[b, :Ls[b] + 1] >= 0)

@@ -21,8 +21,11 @@ Functions mirror the C entry points:
   single-step sampling with the joint top-k/top-p filter and min-p
 * ``d2t_inverse(d2t, Vd, V)`` and ``d2t_expand(draft_probs, t2d)``: draft distributions over a
   reduced draft vocabulary placed in the target vocabulary
-* ``greedy_verify(target_logits, draft_ids, req_index=None, ...)``
-* ``gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, ...)``
+* ``greedy_verify(target_logits, draft_ids, req_index=None, ..., workspace=None)``
+* ``gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, ..., workspace=None)``;
+  ``greedy_verify_workspace_bytes(n_req, D)`` and ``gumbel_sample_workspace_bytes(n_req, D)``: the
+  per-request words of their one-workgroup-per-row form (``workspace=False`` takes the
+  one-workgroup-per-request form)
 * ``verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None,
   top_p=None, req_index=None, workspace=None)``: softmax_renorm followed by chain_reject in one call;
   ``verify_fused_workspace_bytes(n_req, D)``: its counters for small batches
@@ -53,7 +56,9 @@ SYMBOLS = (
     "specverify_d2t_inverse",
     "specverify_d2t_expand",
     "specverify_greedy_verify",
+    "specverify_greedy_verify_workspace_bytes",
     "specverify_gumbel_sample",
+    "specverify_gumbel_sample_workspace_bytes",
     "specverify_verify_fused",
     "specverify_verify_fused_workspace_bytes",
     "specverify_sample",
@@ -92,8 +97,11 @@ def lib() -> ctypes.CDLL:
                                                  vp, vp, i64, vp]
     L.specverify_d2t_inverse.argtypes = [vp, i64, i64, vp, vp]
     L.specverify_d2t_expand.argtypes = [vp, vp, i64, i64, i64, vp, vp]
-    L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
-    L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
+    L.specverify_greedy_verify.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, i64, vp]
+    L.specverify_greedy_verify_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    L.specverify_gumbel_sample.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, i64,
+                                           vp]
+    L.specverify_gumbel_sample_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_int64)]
     L.specverify_verify_fused.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp,
                                           i64, vp]
     L.specverify_verify_fused_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_int64)]
@@ -101,7 +109,9 @@ def lib() -> ctypes.CDLL:
     for name in ("specverify_softmax_renorm", "specverify_chain_reject", "specverify_chain_workspace_bytes",
                  "specverify_chain_reject_noalloc", "specverify_chain_reject_ragged",
                  "specverify_d2t_inverse", "specverify_d2t_expand", "specverify_greedy_verify",
-                 "specverify_gumbel_sample", "specverify_verify_fused", "specverify_verify_fused_workspace_bytes",
+                 "specverify_greedy_verify_workspace_bytes", "specverify_gumbel_sample",
+                 "specverify_gumbel_sample_workspace_bytes", "specverify_verify_fused",
+                 "specverify_verify_fused_workspace_bytes",
                  "specverify_sample"):
         getattr(L, name).restype = ctypes.c_int
     L.specverify_status_string.argtypes = [ctypes.c_int]
@@ -308,31 +318,49 @@ def chain_reject_noalloc(draft_probs, draft_ids, target_probs, seed, offset, req
     return acc, alen
 
 
-def verify_fused_workspace_bytes(n_req, D) -> int:
-    """Bytes of per-request counters verify_fused uses for small batches (0: none)."""
+def _query(fn, n_req, D) -> int:
     out = ctypes.c_int64(0)
-    _check("specverify_verify_fused_workspace_bytes",
-           lib().specverify_verify_fused_workspace_bytes(int(n_req), int(D), ctypes.byref(out)))
+    _check(fn, getattr(lib(), fn)(int(n_req), int(D), ctypes.byref(out)))
     return int(out.value)
 
 
-_fused_workspaces = {}
+def verify_fused_workspace_bytes(n_req, D) -> int:
+    """Bytes of per-request counters verify_fused uses for small batches (0: none)."""
+    return _query("specverify_verify_fused_workspace_bytes", n_req, D)
 
 
-def _fused_workspace(workspace, n_req, D, device):
+def greedy_verify_workspace_bytes(n_req, D) -> int:
+    """Bytes of the per-request words of greedy_verify's one-workgroup-per-row form (0: none)."""
+    return _query("specverify_greedy_verify_workspace_bytes", n_req, D)
+
+
+def gumbel_sample_workspace_bytes(n_req, D) -> int:
+    """Bytes of the per-request words of gumbel_sample's one-workgroup-per-row form (0: none)."""
+    return _query("specverify_gumbel_sample_workspace_bytes", n_req, D)
+
+
+_counter_workspaces = {}
+
+
+def _counter_workspace(kind, n, workspace, device):
+    """(tensor, bytes) for a workspace of n bytes: the caller's tensor, none for n == 0 or
+    workspace=False, else a zeroed buffer kept per (kind, device, stream); the library leaves it zero."""
     torch = _torch()
-    n = verify_fused_workspace_bytes(n_req, D)
-    if n == 0:
+    if n == 0 or workspace is False:
         return None, 0
     if workspace is not None:
         _need(workspace, "workspace", (torch.uint8,), device, 1)
         return workspace, int(workspace.numel())
-    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
-    ws = _fused_workspaces.get(key)
+    key = (kind, device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _counter_workspaces.get(key)
     if ws is None or ws.numel() < n:
         ws = torch.zeros((n,), dtype=torch.uint8, device=device)
-        _fused_workspaces[key] = ws
+        _counter_workspaces[key] = ws
     return ws, int(ws.numel())
+
+
+def _fused_workspace(workspace, n_req, D, device):
+    return _counter_workspace("fused", verify_fused_workspace_bytes(n_req, D), workspace, device)
 
 
 def verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None, top_p=None,
@@ -486,10 +514,12 @@ def sample(logits, temperature, seed, offset, top_k=None, top_p=None, min_p=None
 
 
 def greedy_verify(target_logits, draft_ids, req_index=None, predict=True, accept_index=True,
-                  argmax=False, out=None):
+                  argmax=False, out=None, workspace=None):
     """Greedy chain verify; returns a dict of int32 tensors:
     accepted_tokens [B, N], accept_length [B], and optionally predict [B, N],
-    accept_index [B, N] (flat index into predict), argmax [B, N] (forces every row)."""
+    accept_index [B, N] (flat index into predict), argmax [B, N] (forces every row).
+    workspace: uint8 tensor of greedy_verify_workspace_bytes(n_req, D) bytes (zero before the
+    first call; kept per device and stream when None; False for the one-workgroup-per-request form)."""
     torch = _torch()
     _need(target_logits, "target_logits", (torch.float32, torch.bfloat16), None, 3)
     dev = target_logits.device
@@ -513,18 +543,20 @@ def greedy_verify(target_logits, draft_ids, req_index=None, predict=True, accept
     pr = mk("predict", (B, N), predict)
     ai = mk("accept_index", (B, N), accept_index)
     am = mk("argmax", (B, N), argmax)
+    ws, ws_bytes = _counter_workspace("rows", greedy_verify_workspace_bytes(n_req, D), workspace, dev)
     st = lib().specverify_greedy_verify(
         _ptr(target_logits), _logit_dtype(target_logits), _ptr(draft_ids), B, D, V, _ptr(req_index), n_req,
-        _ptr(acc), _ptr(alen), _ptr(pr), _ptr(ai), _ptr(am), _stream_ptr(dev))
+        _ptr(acc), _ptr(alen), _ptr(pr), _ptr(ai), _ptr(am), _ptr(ws), ws_bytes, _stream_ptr(dev))
     _check("specverify_greedy_verify", st)
     return o
 
 
 def gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index=None, sampled=False,
-                  out=None):
+                  out=None, workspace=None):
     """Gumbel-max temperature sampling + strict acceptance; returns a dict of
     int32 tensors accepted_tokens [B, N], accept_length [B] and optionally
-    sampled [B, N] (forces every row)."""
+    sampled [B, N] (forces every row).  workspace: as for greedy_verify, of
+    gumbel_sample_workspace_bytes(n_req, D) bytes."""
     torch = _torch()
     _need(target_logits, "target_logits", (torch.float32, torch.bfloat16), None, 3)
     dev = target_logits.device
@@ -542,10 +574,11 @@ def gumbel_sample(target_logits, temperature, draft_ids, seed, offset, req_index
                              ("sampled", (B, N), sampled)):
         if want and key not in o:
             o[key] = torch.empty(shape, dtype=torch.int32, device=dev)
+    ws, ws_bytes = _counter_workspace("rows", gumbel_sample_workspace_bytes(n_req, D), workspace, dev)
     st = lib().specverify_gumbel_sample(
         _ptr(target_logits), _logit_dtype(target_logits), _ptr(temperature), _ptr(draft_ids), _ptr(seed),
         _ptr(offset), B, D, V, _ptr(req_index), n_req, _ptr(o["accepted_tokens"]), _ptr(o["accept_length"]),
-        _ptr(o.get("sampled")), _stream_ptr(dev))
+        _ptr(o.get("sampled")), _ptr(ws), ws_bytes, _stream_ptr(dev))
     _check("specverify_gumbel_sample", st)
     return o
 

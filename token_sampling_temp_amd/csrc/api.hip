@@ -275,10 +275,42 @@ int specverify_d2t_expand(const float* draft_probs, const int32_t* t2d, int64_t 
                                               static_cast<hipStream_t>(stream)));
 }
 
+// Validates an optional row-parallel workspace of `need` bytes.
+static int check_rowpar_workspace(const char* fn, const void* workspace, int64_t workspace_bytes, int64_t need,
+                                  int64_t n_req, int64_t D) {
+    if (!workspace || need == 0) return SPECVERIFY_OK;
+    if (workspace_bytes < need)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace_bytes=%lld, n_req=%lld D=%lld needs %lld", fn,
+                    (long long)workspace_bytes, (long long)n_req, (long long)D, (long long)need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace must be 8-byte aligned", fn);
+    return SPECVERIFY_OK;
+}
+
+// Shared body of the row-parallel workspace size queries.
+static int rowpar_query(const char* fn, int64_t n_req, int64_t D, int64_t* bytes,
+                        int64_t (*size)(int64_t, int)) {
+    SV_REQUIRE(bytes, "bytes");
+    if (n_req < 0) return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: n_req=%lld must be >= 0", fn, (long long)n_req);
+    SV_TRY(check_draft(fn, D));
+    *bytes = size(n_req, (int)D);
+    g_last_error.clear();
+    return SPECVERIFY_OK;
+}
+
+int specverify_greedy_verify_workspace_bytes(int64_t n_req, int64_t D, int64_t* bytes) {
+    return rowpar_query("specverify_greedy_verify_workspace_bytes", n_req, D, bytes, sv::greedy_workspace_bytes);
+}
+
+int specverify_gumbel_sample_workspace_bytes(int64_t n_req, int64_t D, int64_t* bytes) {
+    return rowpar_query("specverify_gumbel_sample_workspace_bytes", n_req, D, bytes, sv::gumbel_workspace_bytes);
+}
+
 int specverify_greedy_verify(const void* target_logits, int dtype, const int32_t* draft_ids, int64_t B,
                              int64_t D, int64_t V, const int32_t* req_index, int64_t n_req,
                              int32_t* accepted_tokens, int32_t* accept_length, int32_t* predict,
-                             int32_t* accept_index, int32_t* argmax_out, void* stream) {
+                             int32_t* accept_index, int32_t* argmax_out, void* workspace, int64_t workspace_bytes,
+                             void* stream) {
     const char* fn = "specverify_greedy_verify";
     SV_TRY(check_dtype(fn, dtype));
     SV_TRY(check_draft(fn, D));
@@ -288,17 +320,19 @@ int specverify_greedy_verify(const void* target_logits, int dtype, const int32_t
     if (D > 0) SV_REQUIRE(draft_ids, "draft_ids");
     SV_REQUIRE(accepted_tokens, "accepted_tokens");
     SV_REQUIRE(accept_length, "accept_length");
+    SV_TRY(check_rowpar_workspace(fn, workspace, workspace_bytes, sv::greedy_workspace_bytes(n_req, (int)D), n_req,
+                                  D));
     SV_TRY(check_device());
     return launched(fn, sv::launch_greedy_verify(target_logits, dtype, draft_ids, B, (int)D, V, req_index, n_req,
                                                  accepted_tokens, accept_length, predict, accept_index, argmax_out,
-                                                 static_cast<hipStream_t>(stream)));
+                                                 workspace, static_cast<hipStream_t>(stream)));
 }
 
 int specverify_gumbel_sample(const void* target_logits, int dtype, const float* temperature,
                              const int32_t* draft_ids, const uint64_t* seed, const uint64_t* offset, int64_t B,
                              int64_t D, int64_t V, const int32_t* req_index, int64_t n_req,
                              int32_t* accepted_tokens, int32_t* accept_length, int32_t* sampled_out,
-                             void* stream) {
+                             void* workspace, int64_t workspace_bytes, void* stream) {
     const char* fn = "specverify_gumbel_sample";
     SV_TRY(check_dtype(fn, dtype));
     SV_TRY(check_draft(fn, D));
@@ -311,10 +345,12 @@ int specverify_gumbel_sample(const void* target_logits, int dtype, const float* 
     SV_REQUIRE(offset, "offset");
     SV_REQUIRE(accepted_tokens, "accepted_tokens");
     SV_REQUIRE(accept_length, "accept_length");
+    SV_TRY(check_rowpar_workspace(fn, workspace, workspace_bytes, sv::gumbel_workspace_bytes(n_req, (int)D), n_req,
+                                  D));
     SV_TRY(check_device());
     return launched(fn, sv::launch_gumbel_sample(target_logits, dtype, temperature, draft_ids, seed, offset, B,
                                                  (int)D, V, req_index, n_req, accepted_tokens, accept_length,
-                                                 sampled_out, static_cast<hipStream_t>(stream)));
+                                                 sampled_out, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int specverify_sample(const void* logits, int dtype, const float* temperature, const int32_t* top_k,

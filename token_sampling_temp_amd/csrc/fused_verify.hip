@@ -13,7 +13,6 @@
 // values, chunk sums, their order and the search are those of softmax_renorm
 // followed by chain_reject (with a 16-byte aligned probability buffer), so the
 // two paths return the same tokens.
-#include <atomic>
 #include <type_traits>
 
 #include "sv_draw.hpp"
@@ -776,19 +775,6 @@ hipError_t launch_sample(const void* logits, int dtype, const float* temperature
 
 int64_t verify_fused_max_vocab() { return (int64_t)kFvMaxChunks * kFvChunk; }
 
-// Compute units of the current device (cached per device; 0 if unknown).
-static int device_cus() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 int64_t verify_fused_workspace_bytes(int64_t n_req, int D) {
     return (D > 0 && n_req > 0 && n_req * (D + 1) <= kFusedRowsMax) ? (n_req * 4 + 255) / 256 * 256 : 0;
 }
@@ -801,7 +787,7 @@ static void launch_fv(const T* logits, const float* temperature, const int32_t* 
     // small batches: one workgroup per row when every row fits on its own CU
     // (and the caller gave the per-request counters)
     const int64_t rows = n_req * (D + 1);
-    if (workspace && verify_fused_workspace_bytes(n_req, D) > 0 && rows <= device_cus()) {
+    if (workspace && verify_fused_workspace_bytes(n_req, D) > 0 && rows <= device_compute_units()) {
         hipLaunchKernelGGL((verify_fused_rows_kernel<T, NV>), dim3((unsigned)rows), dim3(kFvBlock), 0, stream,
                            logits, temperature, top_k, top_p, q, x, seed, offset, B, D, V, req_index, accepted,
                            accept_len, static_cast<uint32_t*>(workspace));

@@ -1,6 +1,9 @@
 // Temperature-only target sampling by Gumbel-max, then strict chain
-// acceptance.  One workgroup per request walks rows j = 0..D in order and
-// stops after the first draft mismatch (unless every row is requested).
+// acceptance.  Two forms: one workgroup per request walking rows j = 0..D in
+// order and stopping after the first draft mismatch (no workspace), or, with a
+// workspace, one workgroup per (request, row) with rows after a mismatch
+// skipped through the request's stop word (sv_rowpar.hpp).  Every row is read
+// when every row's sample is requested.
 //
 // Row j of request b: s_v = z_v / T + G_v, G_v = -ln(-ln u_v), u_v the uniform
 // of Philox word v of stream (seed_b, offset_b + 32 j); the sample is the
@@ -12,6 +15,7 @@
 // values; only a near tie of the two best scores can tell them apart).
 #include "sv_argmax.hpp"
 #include "sv_launch.hpp"
+#include "sv_rowpar.hpp"
 
 namespace sv {
 
@@ -103,11 +107,13 @@ __device__ __forceinline__ void gumbel_group(const float (&f)[4], int g, int Vi,
 // thread keeps the loads of its next kPf groups in flight while it computes
 // the Philox block and the scores of the current one (consume a slot, refill
 // it), so the row's load latency hides behind the arithmetic.  Buffer loads
-// with the row as the range read zeros past its end.
+// with the row as the range read zeros past its end.  With STOP, `stop` is
+// polled once per round of kPf groups and the row is no longer read once it
+// signals (the result is then meaningless).
 constexpr int kPf = 4;
-template <int BLOCK, typename T>
+template <int BLOCK, typename T, bool STOP>
 __device__ __forceinline__ void row_gumbel_pipelined(const T* row, int Vi, float invT, uint64_t seed,
-                                                     uint64_t subseq, float& best, int& bi) {
+                                                     uint64_t subseq, float& best, int& bi, RowStop* stop) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     constexpr bool kF32 = sizeof(T) == 4;
     typedef typename std::conditional<kF32, u32x4, u32x2>::type Raw;
@@ -133,10 +139,18 @@ __device__ __forceinline__ void row_gumbel_pipelined(const T* row, int Vi, float
         }
     };
     const int tid = threadIdx.x;
+    if constexpr (STOP) {
+        stop->poll();
+        if (stop->check()) return;
+    }
     Raw slot[kPf];
 #pragma unroll
     for (int j = 0; j < kPf; ++j) slot[j] = ld(tid + j * BLOCK);
     for (int g0 = tid; g0 < ngroups; g0 += kPf * BLOCK) {
+        if constexpr (STOP) {
+            if (stop->check()) break;
+            stop->poll();
+        }
 #pragma unroll
         for (int j = 0; j < kPf; ++j) {
             __builtin_amdgcn_sched_barrier(0);
@@ -149,9 +163,9 @@ __device__ __forceinline__ void row_gumbel_pipelined(const T* row, int Vi, float
     }
 }
 
-template <int BLOCK, typename T>
+template <int BLOCK, typename T, bool STOP = false>
 __device__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed, uint64_t subseq,
-                              ArgmaxShared<BLOCK>& sh) {
+                              ArgmaxShared<BLOCK>& sh, RowStop* stop = nullptr) {
     const bool aligned = ((uintptr_t)row % (4 * sizeof(T))) == 0;
     const int Vi = (int)V;   // V < 2^31
     const int ngroups = (Vi + 3) / 4;
@@ -162,7 +176,7 @@ __device__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed
     // whole groups only (V a multiple of 4), so no load straddles the row's end
     if (aligned && (Vi & 3) == 0 &&
         V * (int64_t)sizeof(T) + (int64_t)(kPf + 1) * BLOCK * 4 * (int64_t)sizeof(T) < ((int64_t)1 << 32)) {
-        row_gumbel_pipelined<BLOCK, T>(row, Vi, invT, seed, subseq, best, bi);
+        row_gumbel_pipelined<BLOCK, T, STOP>(row, Vi, invT, seed, subseq, best, bi, stop);
         const uint64_t key = bi < 0 ? 0 : pack_key_index(float_key(best), (int64_t)bi);
         const uint64_t m = block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
         return packed_index(m);
@@ -235,12 +249,72 @@ __global__ __launch_bounds__(kGbBlock) void gumbel_sample_kernel(
     if (t == 0) accept_len[b] = L;
 }
 
+// Row-parallel form: workgroup g takes row j = g / n_req of request slot
+// g % n_req.
+template <typename T>
+__global__ __launch_bounds__(kGbBlock) void gumbel_rows_kernel(
+    const T* __restrict__ logits, const float* __restrict__ temperature, const int32_t* __restrict__ draft_ids,
+    const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
+    const int32_t* __restrict__ req_index, int64_t n_req, void* __restrict__ ws, int32_t* __restrict__ accepted,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ sampled_out) {
+    __shared__ ArgmaxShared<kGbBlock> sh;
+    __shared__ uint32_t s_stop;
+    const int N = D + 1;
+    const int j = (int)(blockIdx.x / (uint64_t)n_req);
+    const int64_t slot = (int64_t)blockIdx.x - (int64_t)j * n_req;
+    const int64_t b = req_index ? (int64_t)req_index[slot] : slot;
+    if (b < 0 || b >= B) return;
+    const RowPar rp(ws, slot);
+    const float Tm = temperature[b];
+    const int32_t xj = j < D ? draft_ids[b * D + j] : -1;
+    // row 0 is always needed; every row is needed when all samples are asked for
+    // stop once a row before j has ended the chain (never for row 0, nor when
+    // every row's sample is asked for)
+    if (threadIdx.x == 0) s_stop = 0;
+    __syncthreads();
+    RowStop stop((sampled_out || j == 0) ? nullptr : rp.word, ((uint64_t)1 << j) - 1, &s_stop, true);
+    const T* row = logits + ((int64_t)b * N + j) * V;
+    const int64_t y = (double)Tm < kGreedyTemperature
+                          ? row_argmax<kGbBlock, true, T, true>(row, V, sh, &stop)
+                          : row_gumbel<kGbBlock, T, true>(row, V, 1.0f / Tm, seed[b],
+                                                          offset[b] + kRngSlotSpan * (uint64_t)j, sh, &stop);
+    if (threadIdx.x >= kWave) return;
+    int32_t yt = -1;
+    const int L = rp.arrive(j, N, j == D || xj != (int32_t)y, (int32_t)y, yt);
+    if (L < 0) return;
+    const int t = threadIdx.x;
+    if (t < N) {
+        const int64_t o = b * N + t;
+        accepted[o] = t <= L ? yt : -1;
+        if (sampled_out) sampled_out[o] = yt;
+    }
+    if (t == 0) accept_len[b] = L;
+}
+
+int64_t gumbel_workspace_bytes(int64_t n_req, int D) {
+    return (D > 0 && n_req > 0) ? rowpar_workspace_bytes(n_req) : 0;
+}
+
 hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temperature,
                                 const int32_t* draft_ids, const uint64_t* seed, const uint64_t* offset,
                                 int64_t B, int D, int64_t V, const int32_t* req_index, int64_t n_req,
-                                int32_t* accepted, int32_t* accept_len, int32_t* sampled_out,
+                                int32_t* accepted, int32_t* accept_len, int32_t* sampled_out, void* workspace,
                                 hipStream_t stream) {
-    const dim3 grid((unsigned)n_req), block(kGbBlock);
+    const dim3 block(kGbBlock);
+    // as for greedy verify: rows spread over CUs below two requests per CU
+    if (workspace && gumbel_workspace_bytes(n_req, D) > 0 && n_req < 2 * (int64_t)device_compute_units()) {
+        const dim3 grid((unsigned)(n_req * (D + 1)));
+        if (dtype == kDtypeBF16)
+            hipLaunchKernelGGL(gumbel_rows_kernel<uint16_t>, grid, block, 0, stream,
+                               static_cast<const uint16_t*>(logits), temperature, draft_ids, seed, offset, B, D, V,
+                               req_index, n_req, workspace, accepted, accept_len, sampled_out);
+        else
+            hipLaunchKernelGGL(gumbel_rows_kernel<float>, grid, block, 0, stream, static_cast<const float*>(logits),
+                               temperature, draft_ids, seed, offset, B, D, V, req_index, n_req, workspace, accepted,
+                               accept_len, sampled_out);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)n_req);
     if (dtype == kDtypeBF16)
         hipLaunchKernelGGL(gumbel_sample_kernel<uint16_t>, grid, block, 0, stream,
                            static_cast<const uint16_t*>(logits), temperature, draft_ids, seed, offset, B, D, V,

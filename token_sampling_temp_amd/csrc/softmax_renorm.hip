@@ -3,8 +3,6 @@
 // path go to one persistent workgroup per CU; other rows get one workgroup per
 // (request, position) row, streamed.  T < 1e-5 writes a one-hot at the
 // lowest-index argmax.
-#include <atomic>
-
 #include "sv_launch.hpp"
 #include "sv_softmax.hpp"
 
@@ -89,19 +87,6 @@ static void launch_rr(unsigned grid, hipStream_t stream, const uint16_t* logits,
                        temperature, top_k, top_p, req_index, n_req, out);
 }
 
-// Compute units of the current device (cached per device; 256 if unknown).
-static int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64_t npos, int64_t V,
                                  const float* temperature, const int32_t* top_k, const float* top_p,
                                  const int32_t* req_index, int64_t n_req, float* probs_out,
@@ -110,7 +95,7 @@ hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64
     if (dtype == kDtypeBF16 && V <= (int64_t)kRrBlock * 8 * kRrMaxNV) {
         // one persistent workgroup per compute unit (the LDS footprint allows no more)
         const int64_t rows = n_req * npos;
-        const unsigned g = (unsigned)(rows < (int64_t)device_cus() ? rows : (int64_t)device_cus());
+        const unsigned g = (unsigned)(rows < (int64_t)device_compute_units() ? rows : (int64_t)device_compute_units());
         const int64_t nv = (V + kRrBlock * 8 - 1) / (kRrBlock * 8);
         const uint16_t* lg = static_cast<const uint16_t*>(logits);
         const int np = (int)npos;

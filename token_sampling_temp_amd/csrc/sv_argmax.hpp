@@ -29,94 +29,139 @@ __device__ int64_t row_argmax_exact(const T* row, int64_t V, ArgmaxShared<BLOCK>
     return packed_index(m);
 }
 
-// Fast path: each thread keeps the maximum of its elements and the first
-// 16-byte vector (or scalar) where that maximum appeared; the block maximum is
-// reduced as a float (so -0 == +0), and the threads holding it re-read their
-// one vector to locate the lowest index.  Rows containing a NaN (detected from
-// the magnitude bits) take the exact path.
-template <int BLOCK, bool NT, typename T>
-__device__ int64_t row_argmax(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh) {
+// Fast path: each thread keeps the maximum of its elements and the index of
+// its first occurrence (found inside the 16-byte vector when the vector's
+// maximum beats the running one); one packed (value key, index) maximum over
+// the block then gives the value and its lowest index, -0 and +0 tying
+// through the key.  Rows containing a NaN (detected from the magnitude bits)
+// take the exact path.
+//
+// Rows whose byte length fits a buffer descriptor stream through one with the
+// next batch of kArgmaxBatch loads issued before the current one is folded
+// (loads past the row's end read zeros and are never folded), so every
+// thread keeps between one and two batches in flight; each vector is loaded
+// once.
+//
+// With STOP, `stop` is polled once per batch and the row is no longer read
+// once it signals (the caller's sign that the row's result is no longer
+// needed; the returned index is then meaningless).  Waves leave the loop on
+// their own, with no barrier, and all of them still take part in the block
+// reduction.
+constexpr int kArgmaxBatch = 4;
+
+template <int BLOCK, bool NT, typename T, bool STOP = false>
+__device__ int64_t row_argmax(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh, RowStop* stop = nullptr) {
     constexpr int E = RowSplit<T>::kEpv;
+    constexpr int U = kArgmaxBatch;
     const RowSplit<T> s(row, V);
     const int tid = threadIdx.x;
     float best = -INFINITY;
-    int64_t bpos = -1;   // first element of the recorded vector/scalar
-    int bw = 0;          // its width (E or 1)
+    int64_t bidx = -1;   // index of the thread's first maximum
     uint32_t mag = 0;
 
     if (tid < s.head) {
         const float v = load_elem(row + tid);
         mag = mag_acc_scalar(mag, v, T{});
         best = v;
-        bpos = tid;
-        bw = 1;
+        bidx = tid;
     }
     const T* body = row + s.head;
-    auto vec_max = [](const float (&f)[E]) {
-        float m = f[0];
-#pragma unroll
-        for (int e = 1; e < E; ++e) m = fmaxf(m, f[e]);
-        return m;
-    };
-    int64_t i = tid;
-    for (; i + 3 * BLOCK < s.nvec; i += 4 * BLOCK) {
-        u32x4 a[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = load_vec<NT>(body, i + u * BLOCK);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            float f[E];
-            unpack(a[u], f);
-            mag = mag_acc(mag, a[u], T{});
-            const float m = vec_max(f);
-            if (bpos < 0 || m > best) {
-                best = m;
-                bpos = s.head + (i + u * BLOCK) * E;
-                bw = E;
-            }
-        }
-    }
-    for (; i < s.nvec; i += BLOCK) {
-        const u32x4 a = load_vec<NT>(body, i);
+    // vector k of the body: its maximum, and where it first occurs if it beats best
+    auto fold = [&](const u32x4 a, int64_t k) {
         float f[E];
         unpack(a, f);
         mag = mag_acc(mag, a, T{});
-        const float m = vec_max(f);
-        if (bpos < 0 || m > best) {
+        float m = f[0];
+#pragma unroll
+        for (int e = 1; e < E; ++e) m = fmaxf(m, f[e]);
+        if (bidx < 0 || m > best) {
+            int e0 = E - 1;
+#pragma unroll
+            for (int e = E - 2; e >= 0; --e)
+                if (f[e] == m) e0 = e;
             best = m;
-            bpos = s.head + i * E;
-            bw = E;
+            bidx = s.head + k * E + e0;
+        }
+    };
+    auto poll = [&]() {
+        if constexpr (STOP) stop->poll();
+    };
+    auto stopped = [&]() {
+        if constexpr (STOP) return stop->check();
+        else return false;
+    };
+    poll();
+    int64_t i = tid;
+    const int64_t body_bytes = s.nvec * 16;
+    if (body_bytes + (int64_t)2 * U * BLOCK * 16 < ((int64_t)1 << 32)) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(body, (uint32_t)body_bytes);
+        constexpr int kAux = NT ? 2 : 0;
+        auto ld = [&](int64_t k) -> u32x4 {
+            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)k * 16u, 0, kAux));
+        };
+        u32x4 cur[U];
+        if (i + (U - 1) * BLOCK < s.nvec) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = ld(i + u * BLOCK);
+            for (;;) {
+                const int64_t nx = i + U * BLOCK;
+                // checked before the next batch goes out: one batch at most is
+                // read after the signal shows
+                if (stopped()) {
+                    i = s.nvec;
+                    break;
+                }
+                poll();
+                u32x4 nxt[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) nxt[u] = ld(nx + u * BLOCK);
+#pragma unroll
+                for (int u = 0; u < U; ++u) fold(cur[u], i + u * BLOCK);
+                i = nx;
+                if (i + (U - 1) * BLOCK >= s.nvec) {
+                    // the last batch, partly or wholly past the end
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (i + u * BLOCK < s.nvec) fold(nxt[u], i + u * BLOCK);
+                    i = s.nvec;
+                    break;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+            }
+        }
+    } else {
+        for (; i + (U - 1) * BLOCK < s.nvec; i += U * BLOCK) {
+            if (stopped()) {
+                i = s.nvec;
+                break;
+            }
+            u32x4 a[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) a[u] = load_vec<NT>(body, i + u * BLOCK);
+            poll();
+#pragma unroll
+            for (int u = 0; u < U; ++u) fold(a[u], i + u * BLOCK);
         }
     }
+    for (; i < s.nvec; i += BLOCK) fold(load_vec<NT>(body, i), i);
     if (tid < s.tail) {
         const int64_t idx = s.head + s.nvec * E + tid;
         const float v = load_elem(row + idx);
         mag = mag_acc_scalar(mag, v, T{});
-        if (bpos < 0 || v > best) {
+        if (bidx < 0 || v > best) {
             best = v;
-            bpos = idx;
-            bw = 1;
+            bidx = idx;
         }
     }
 
-    const uint32_t nan_flag = mag_has_nan(mag, T{}) ? 1u : 0u;
-    const uint32_t any_nan = block_reduce<BLOCK>(nan_flag, OpOrU32{}, 0u, sh.red_m);
-    if (any_nan) return row_argmax_exact<BLOCK>(row, V, sh);
-
-    const float M = block_reduce<BLOCK>(bpos >= 0 ? best : -INFINITY, OpMaxF{}, -INFINITY, sh.red_f);
-    int64_t cand = INT64_MAX;
-    if (bpos >= 0 && best == M) {
-        if (bw == 1) {
-            cand = bpos;
-        } else {
-            float f[E];
-            unpack(load_vec<false>(row + bpos, 0), f);
-#pragma unroll
-            for (int e = E - 1; e >= 0; --e)
-                if (f[e] == M) cand = bpos + e;
-        }
-    }
-    return block_reduce<BLOCK>(cand, OpMinI64{}, (int64_t)INT64_MAX, sh.red_i);
+    // a NaN anywhere makes the packed key all ones, which no number reaches
+    const uint64_t key = mag_has_nan(mag, T{}) ? ~(uint64_t)0
+                         : bidx < 0          ? (uint64_t)0
+                                             : pack_key_index(float_key(best), bidx);
+    const uint64_t m = block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
+    if (m == ~(uint64_t)0) return row_argmax_exact<BLOCK>(row, V, sh);
+    return packed_index(m);
 }
 
 }  // namespace sv

@@ -90,6 +90,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
 }
 
+// Early-stop signal for a workgroup reading one row.  For a row read at
+// memory speed the caller's 64-bit word is polled by wave 0 alone, because a
+// wave's vector loads complete in issue order and a poll that waits on a
+// contended line would hold back every load issued after it; wave 0 raises a
+// flag in LDS that the other waves read.  For a row bound by arithmetic
+// (`every_wave`) each wave polls for itself and so stops without first
+// spending a round of work.  A poll issued by poll() is consumed by the next
+// check().  With a null word nothing stops.
+struct RowStop {
+    const uint64_t* word;
+    uint64_t mask;    // stop once (*word & mask) != 0
+    uint32_t* flag;   // LDS word, zero before the row starts
+    bool every_wave;
+    uint64_t seen;    // the polling wave's last value
+
+    __device__ RowStop(const uint64_t* w, uint64_t m, uint32_t* f, bool every)
+        : word(w), mask(m), flag(f), every_wave(every), seen(0) {}
+    __device__ __forceinline__ bool polls() const { return every_wave || threadIdx.x < kWave; }
+    __device__ __forceinline__ void poll() {
+        if (word && polls()) seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ __forceinline__ bool check() {
+        if (!word) return false;
+        if (polls()) {
+            const bool f = __builtin_amdgcn_readfirstlane((int)((seen & mask) != 0));
+            if (f && !every_wave) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return f;
+        }
+        return __builtin_amdgcn_readfirstlane(
+                   (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0;
+    }
+};
+
 // Workgroup barrier that orders LDS only: it waits for this wave's LDS
 // operations, not for its outstanding global loads and stores (a plain
 // __syncthreads() waits for those too).  For code whose threads exchange

@@ -5,7 +5,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace sv {
+
+// Compute units of the current device, cached per device (256, the MI355X
+// count, when the runtime cannot tell).
+inline int device_compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
@@ -14,7 +30,9 @@ constexpr int kMaxDraft = 16;
 hipError_t launch_greedy_verify(const void* logits, int dtype, const int32_t* draft_ids, int64_t B, int D,
                                 int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted,
                                 int32_t* accept_len, int32_t* predict, int32_t* accept_index,
-                                int32_t* argmax_out, hipStream_t stream);
+                                int32_t* argmax_out, void* workspace, hipStream_t stream);
+// Bytes of the row-parallel workspace greedy verify takes (0: none used).
+int64_t greedy_workspace_bytes(int64_t n_req, int D);
 
 // Chain rejection's workspace in bytes for n_req requests over V entries (0:
 // none).  It holds n_req 32-bit counters, zero before and after every call
@@ -60,8 +78,10 @@ hipError_t launch_softmax_renorm(const void* logits, int dtype, int64_t B, int64
 hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temperature,
                                 const int32_t* draft_ids, const uint64_t* seed, const uint64_t* offset,
                                 int64_t B, int D, int64_t V, const int32_t* req_index, int64_t n_req,
-                                int32_t* accepted, int32_t* accept_len, int32_t* sampled_out,
+                                int32_t* accepted, int32_t* accept_len, int32_t* sampled_out, void* workspace,
                                 hipStream_t stream);
+// Bytes of the row-parallel workspace Gumbel sampling takes (0: none used).
+int64_t gumbel_workspace_bytes(int64_t n_req, int D);
 
 // Fused target rows + chain rejection (V <= verify_fused_max_vocab()).
 // Batches of at most kFusedRowsMax rows (n_req * (D + 1)) may evaluate every
