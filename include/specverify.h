@@ -408,10 +408,11 @@ int specverify_gumbel_sample_workspace_bytes(int64_t n_req, int64_t D, int64_t* 
  *                 and n_req * (D + 1) at most 256 and at most the device's
  *                 compute units) evaluate every target row of a request at
  *                 once, one workgroup per row, and need
- *                 specverify_verify_fused_workspace_bytes(n_req, D) bytes of
- *                 per-request counters (4-byte aligned, all zero when a call
- *                 starts; every call leaves them zero, so zero it once and
- *                 reuse it; calls sharing it must not overlap).  With NULL,
+ *                 specverify_verify_fused_workspace_bytes(n_req, D) bytes
+ *                 (one 128-byte line per request where the rows meet;
+ *                 8-byte aligned, all zero when a call starts; every call
+ *                 leaves it zero, so zero it once and reuse it; calls sharing
+ *                 it must not overlap).  With NULL,
  *                 those batches evaluate a request's rows in order instead
  *                 (same results, longer latency).  A short or misaligned
  *                 workspace returns SPECVERIFY_INVALID_ARGUMENT.
@@ -431,8 +432,9 @@ int specverify_verify_fused(const void* target_logits, int dtype, const float* t
                             void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
- * Workspace size of specverify_verify_fused: 4 bytes per request, rounded up
- * to 256, when D > 0 and n_req * (D + 1) <= 256; else 0 (no workspace used).
+ * Workspace size of specverify_verify_fused: 128 bytes per request, rounded
+ * up to 256, when D > 0 and n_req * (D + 1) <= 256; else 0 (no workspace
+ * used).
  * Host-only.  n_req >= 0, 0 <= D <= 16, bytes non-NULL; else
  * SPECVERIFY_INVALID_ARGUMENT.
  */

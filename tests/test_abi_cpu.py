@@ -184,23 +184,24 @@ def test_verify_fused_invalid_arguments():
                                      None, 0, None) == 0
     # a workspace shorter than the query, or misaligned, is refused before any device call
     assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P, P, 8, None) == 1
-    assert "needs 256" in L.specverify_last_error().decode()
+    assert "needs 512" in L.specverify_last_error().decode()
     assert L.specverify_verify_fused(P, 1, P, None, None, P, P, P, P, 4, 3, 10, None, 4, P, P,
-                                     ctypes.c_void_p(0x1002), 256, None) == 1
+                                     ctypes.c_void_p(0x1004), 512, None) == 1
     assert "aligned" in L.specverify_last_error().decode()
 
 
 def test_verify_fused_workspace_query():
     out = ctypes.c_int64(-1)
     L = sv.lib()
-    assert L.specverify_verify_fused_workspace_bytes(64, 3, ctypes.byref(out)) == 0 and out.value == 256
-    assert L.specverify_verify_fused_workspace_bytes(85, 2, ctypes.byref(out)) == 0 and out.value == 512
+    # one 128-byte line per request, rounded up to 256
+    assert L.specverify_verify_fused_workspace_bytes(64, 3, ctypes.byref(out)) == 0 and out.value == 8192
+    assert L.specverify_verify_fused_workspace_bytes(85, 2, ctypes.byref(out)) == 0 and out.value == 11008
     # past 256 rows, or without drafts, no workspace is used
     assert L.specverify_verify_fused_workspace_bytes(65, 3, ctypes.byref(out)) == 0 and out.value == 0
     assert L.specverify_verify_fused_workspace_bytes(100, 0, ctypes.byref(out)) == 0 and out.value == 0
     assert L.specverify_verify_fused_workspace_bytes(-1, 3, ctypes.byref(out)) == 1
     assert L.specverify_verify_fused_workspace_bytes(4, 17, ctypes.byref(out)) == 1
-    assert sv.verify_fused_workspace_bytes(64, 3) == 256
+    assert sv.verify_fused_workspace_bytes(64, 3) == 8192
 
 
 def test_chain_reject_ragged_invalid_arguments():

@@ -410,8 +410,8 @@ int specverify_verify_fused(const void* target_logits, int dtype, const float* t
     if (workspace && need > 0 && workspace_bytes < need)
         return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace_bytes=%lld, n_req=%lld D=%lld needs %lld", fn,
                     (long long)workspace_bytes, (long long)n_req, (long long)D, (long long)need);
-    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
-        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace must be 4-byte aligned", fn);
+    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+        return fail(SPECVERIFY_INVALID_ARGUMENT, "%s: workspace must be 8-byte aligned", fn);
     SV_TRY(check_device());
     return launched(fn, sv::launch_verify_fused(target_logits, dtype, temperature, top_k, top_p, draft_probs,
                                                 draft_ids, seed, offset, B, (int)D, V, req_index, n_req,

@@ -17,6 +17,7 @@
 
 #include "sv_draw.hpp"
 #include "sv_launch.hpp"
+#include "sv_rowpar.hpp"
 #include "sv_softmax.hpp"
 
 namespace sv {
@@ -290,6 +291,74 @@ __device__ __forceinline__ float key_prob(const RowProb rp, const RrShared& sh, 
     return key >= rp.kmin ? fast_exp2((key_to_float(key) - rp.m) * rp.scale) * rp.inv : 0.0f;
 }
 
+struct CompactDraw {
+    int64_t y;   // the drawn index, -1 when the weights have no positive mass
+    bool used;   // false: nothing drawn (too many vectors or kept entries)
+};
+
+// The draw of compact_draw over n listed kept entries (sh.clist, any order):
+// rank by index while the draft probabilities are gathered, one block-wide
+// scan of the weights in index order, and the first crossing of u_f * R.
+// Whole workgroup.
+__device__ __forceinline__ CompactDraw draw_listed(FusedShared& sh, const RowProb rp, uint32_t n,
+                                                   const float* __restrict__ qr, double uf, int tid) {
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    // ---- rank by index; gather the draft probabilities meanwhile
+    if ((uint32_t)tid < n) {
+        const uint64_t e = sh.clist[tid];
+        const uint32_t idx = (uint32_t)(e >> 16);
+        const float qv = qr ? qr[idx] : 0.0f;   // waited for only after the ranking loop
+        uint32_t rank = 0;
+        const uint32_t n2 = n & ~1u;
+        for (uint32_t j = 0; j < n2; j += 2) {
+            const uint64_t a = sh.clist[j], c = sh.clist[j + 1];
+            rank += (a < e ? 1u : 0u) + (c < e ? 1u : 0u);
+        }
+        if (n & 1u) rank += sh.clist[n - 1] < e ? 1u : 0u;
+        sh.cidx[rank] = idx;
+        sh.cp[rank] = key_prob(rp, sh.rr, (uint32_t)(e & 0xFFFFu));
+        sh.cq[rank] = qv;
+    }
+    lds_barrier();
+    // ---- block-wide inclusive scan of the weights in index order
+    const bool in = (uint32_t)tid < n;
+    const double r = in ? rval(sh.cp[tid], sh.cq[tid], qr != nullptr) : 0.0;
+    const double winc = wave_inclusive_sum(r, lane);
+    if (lane == kWave - 1) sh.wsum[wid] = winc;
+    lds_barrier();
+    double off = 0.0, R = 0.0;
+#pragma unroll
+    for (int i = 0; i < kFvWaves; ++i) {
+        const double t = sh.wsum[i];
+        if (i < wid) off += t;
+        R += t;
+    }
+    if (!(R > 0.0)) return CompactDraw{-1, true};   // uniform
+    const double T = uf * R;
+    const double incl = off + winc;
+    const uint64_t hit = __ballot(in && r > 0.0 && incl > T);
+    const uint64_t posv = __ballot(in && r > 0.0);
+    // per wave: the first crossing (>= 0), else -2 - its last positive entry,
+    // else -1
+    if (lane == 0) {
+        sh.whit[wid] = hit    ? wid * kWave + (__ffsll((unsigned long long)hit) - 1)
+                       : posv ? -2 - (wid * kWave + (63 - __clzll((unsigned long long)posv)))
+                              : -1;
+    }
+    lds_barrier();
+    int first = -1, last = -1;
+#pragma unroll
+    for (int i = 0; i < kFvWaves; ++i) {
+        const int h = sh.whit[i];
+        if (h >= 0 && first < 0) first = h;
+        if (h <= -2) last = -2 - h;   // waves in order: the last one seen is the largest
+    }
+    // no crossing: rounding left T beyond every partial sum, so the draw is
+    // the last positive entry
+    const int t = first >= 0 ? first : last;
+    return CompactDraw{t >= 0 ? (int64_t)sh.cidx[t] : -1, true};
+}
+
 // Inverse-CDF draw over the kept entries of a register-resident row: every
 // weight outside the kept set (keys below kmin) is zero, for the bonus draw
 // (p) and the residual (max(0, p - q)) alike, so only the kept entries are
@@ -303,11 +372,6 @@ __device__ __forceinline__ float key_prob(const RowProb rp, const RrShared& sh, 
 // order finds y = min{ j : sum_{v <= j} r_v > u_f * R }.  Whole workgroup.
 // Nothing is drawn (used = false) when more than kCompactCap vectors or kept
 // entries would be involved.
-struct CompactDraw {
-    int64_t y;   // the drawn index, -1 when the weights have no positive mass
-    bool used;   // false: nothing drawn (too many vectors or kept entries)
-};
-
 template <int NV>
 __device__ __forceinline__ CompactDraw compact_draw(FusedShared& sh, const RowProb rp,
                                                     const uint16_t* __restrict__ row,
@@ -368,60 +432,58 @@ __device__ __forceinline__ CompactDraw compact_draw(FusedShared& sh, const RowPr
         if (cnt && key >= kmin && idx < V) sh.clist[epos++] = ((uint64_t)idx << 16) | key;
     }
     lds_barrier();
-    // ---- rank by index; gather the draft probabilities meanwhile
-    if ((uint32_t)tid < n) {
-        const uint64_t e = sh.clist[tid];
-        const uint32_t idx = (uint32_t)(e >> 16);
-        const float qv = qr ? qr[idx] : 0.0f;   // waited for only after the ranking loop
-        uint32_t rank = 0;
-        const uint32_t n2 = n & ~1u;
-        for (uint32_t j = 0; j < n2; j += 2) {
-            const uint64_t a = sh.clist[j], c = sh.clist[j + 1];
-            rank += (a < e ? 1u : 0u) + (c < e ? 1u : 0u);
+    return draw_listed(sh, rp, n, qr, uf, tid);
+}
+
+// compact_draw for a row still held in registers (w: rr_stats' keys, NV
+// vectors per thread): each thread scans only its vectors whose largest key
+// (vmax) reaches kmin and appends their kept entries, so no vector is read
+// again.
+template <int NV>
+__device__ __forceinline__ CompactDraw compact_draw_regs(FusedShared& sh, const RowProb rp, const u32x4 (&w)[NV],
+                                                         const uint32_t (&vmax)[(NV + 1) / 2], int64_t V,
+                                                         const float* __restrict__ qr, double uf, int tid) {
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    const uint32_t kmin = rp.kmin;
+    auto hot = [&](int v) { return ((vmax[v >> 1] >> (16 * (v & 1))) & 0xFFFFu) >= kmin; };
+    auto key_at = [&](int v, int i) {
+        const uint32_t wd = i < 2 ? w[v].x : (i < 4 ? w[v].y : (i < 6 ? w[v].z : w[v].w));
+        return (wd >> (16 * (i & 1))) & 0xFFFFu;
+    };
+    // whole vectors lie inside the row or past its end (V is a multiple of 8)
+    auto inside = [&](int v) { return (int64_t)(v * kRrBlock + tid) * 8 < V; };
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        if (hot(v) && inside(v)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cnt += key_at(v, i) >= kmin ? 1u : 0u;
         }
-        if (n & 1u) rank += sh.clist[n - 1] < e ? 1u : 0u;
-        sh.cidx[rank] = idx;
-        sh.cp[rank] = key_prob(rp, sh.rr, (uint32_t)(e & 0xFFFFu));
-        sh.cq[rank] = qv;
-    }
+    // block-wide exclusive scan of the counts through sh.whit
+    const uint32_t inc = wave_inclusive_sum(cnt, lane);
+    lds_barrier();   // earlier readers of whit are done
+    if (lane == kWave - 1) sh.whit[wid] = (int32_t)inc;
     lds_barrier();
-    // ---- block-wide inclusive scan of the weights in index order
-    const bool in = (uint32_t)tid < n;
-    const double r = in ? rval(sh.cp[tid], sh.cq[tid], qr != nullptr) : 0.0;
-    const double winc = wave_inclusive_sum(r, lane);
-    if (lane == kWave - 1) sh.wsum[wid] = winc;
-    lds_barrier();
-    double off = 0.0, R = 0.0;
+    uint32_t epos = inc - cnt, n = 0;
 #pragma unroll
     for (int i = 0; i < kFvWaves; ++i) {
-        const double t = sh.wsum[i];
-        if (i < wid) off += t;
-        R += t;
+        const uint32_t t = (uint32_t)sh.whit[i];
+        if (i < wid) epos += t;
+        n += t;
     }
-    if (!(R > 0.0)) return CompactDraw{-1, true};   // uniform
-    const double T = uf * R;
-    const double incl = off + winc;
-    const uint64_t hit = __ballot(in && r > 0.0 && incl > T);
-    const uint64_t posv = __ballot(in && r > 0.0);
-    // per wave: the first crossing (>= 0), else -2 - its last positive entry,
-    // else -1
-    if (lane == 0) {
-        sh.whit[wid] = hit    ? wid * kWave + (__ffsll((unsigned long long)hit) - 1)
-                       : posv ? -2 - (wid * kWave + (63 - __clzll((unsigned long long)posv)))
-                              : -1;
-    }
-    lds_barrier();
-    int first = -1, last = -1;
+    if (!(n > 0 && n <= (uint32_t)kCompactCap)) return CompactDraw{-1, false};   // uniform
 #pragma unroll
-    for (int i = 0; i < kFvWaves; ++i) {
-        const int h = sh.whit[i];
-        if (h >= 0 && first < 0) first = h;
-        if (h <= -2) last = -2 - h;   // waves in order: the last one seen is the largest
-    }
-    // no crossing: rounding left T beyond every partial sum, so the draw is
-    // the last positive entry
-    const int t = first >= 0 ? first : last;
-    return CompactDraw{t >= 0 ? (int64_t)sh.cidx[t] : -1, true};
+    for (int v = 0; v < NV; ++v)
+        if (hot(v) && inside(v)) {
+            const uint32_t base = (uint32_t)(v * kRrBlock + tid) * 8u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t key = key_at(v, i);
+                if (key >= kmin) sh.clist[epos++] = ((uint64_t)(base + i) << 16) | key;
+            }
+        }
+    lds_barrier();
+    return draw_listed(sh, rp, n, qr, uf, tid);
 }
 
 // NV > 0: bf16 logits whose rows are 16-byte aligned with V a multiple of 8
@@ -554,25 +616,21 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_kernel(
 // evaluated at the same time instead of one after another.  Each workgroup
 // computes row j's statistics and accept test exactly as verify_fused_kernel
 // does; a row that rejects (or the bonus row D) also draws its token, as it
-// would if the chain stopped there.  The row's result goes to
-// accepted[b, j] (bit 31 set for an accepted draft, else the drawn token),
-// then thread 0 adds one to the request's counter (an agent-scope release
-// RMW; the workspace holds one per request, zero between calls).  The
-// workgroup that completes the count issues an agent-scope acquire fence
-// (the counter's release sequence orders every row's result before it),
-// takes L = the first row without
-// bit 31, writes the request's tokens and resets the counter.  Rows after L
-// are read although the serial kernel would stop before them; the results
-// are bit-identical to it.  A request listed twice in req_index is done by
-// its first listing only (the others would overwrite its intermediate
-// results).
+// would if the chain stopped there.  Rows meet through the request's line of
+// the workspace (sv_rowpar.hpp): each stores its drawn token and counts
+// itself in, flagging the chain's end if it rejected or is row D; the last
+// workgroup takes L = the first flagged row and writes x_0..x_{L-1}, the
+// token row L drew, then -1.  Rows after L are read although the serial
+// kernel would stop before them; the results are bit-identical to it.  A
+// request listed twice has a line per listing and gets the same outputs
+// twice.
 template <typename T, int NV>
 __global__ __launch_bounds__(kFvBlock) void verify_fused_rows_kernel(
     const T* __restrict__ logits, const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
     const float* __restrict__ top_p, const float* __restrict__ q, const int32_t* __restrict__ x,
     const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
     const int32_t* __restrict__ req_index, int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len,
-    uint32_t* __restrict__ counter) {
+    void* __restrict__ ws) {
     __shared__ FusedShared sh;
     const int N = D + 1;
     const int64_t slot = blockIdx.x / N;
@@ -580,11 +638,6 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_rows_kernel(
     const int64_t b = req_index ? (int64_t)req_index[slot] : slot;
     if (b < 0 || b >= B) return;   // uniform over the workgroup
     const int tid = threadIdx.x;
-    if (req_index) {
-        // a repeated request is done by its first listing (slot < blockDim)
-        const bool dup = tid < slot && req_index[tid] == (int32_t)b;
-        if (__syncthreads_or(dup)) return;
-    }
     const float Tm = temperature[b];
     const int32_t k = top_k ? top_k[b] : 0;
     const float tp = top_p ? top_p[b] : 1.0f;
@@ -621,7 +674,10 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_rows_kernel(
         __syncthreads();
         return sh.acc != 0;
     };
-    const double uf = (double)uniform_code(philox_word(seed[b], offset[b], (uint64_t)D)) * 0x1p-24;
+    // the draw's uniform, formed only by rows that draw
+    auto draw_uniform = [&]() {
+        return (double)uniform_code(philox_word(seed[b], offset[b], (uint64_t)D)) * 0x1p-24;
+    };
     bool done = false, drawn = false, acc = false;
     int64_t y = -1;
     if ((double)Tm < kGreedyTemperature) {
@@ -639,8 +695,18 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_rows_kernel(
                 probed = true;
                 acc = j < D && accepted_here();
                 if (!acc) {
-                    CompactDraw cd = compact_draw<NV>(sh, rp, row16, vmax, V, qj, uf, tid);
-                    if (cd.used && cd.y < 0 && qj) cd = compact_draw<NV>(sh, rp, row16, vmax, V, nullptr, uf, tid);
+                    const double uf = draw_uniform();
+                    // a short row keeps its keys in registers for the draw;
+                    // a long one revisits the vectors that hold kept keys
+                    CompactDraw cd;
+                    if constexpr (NV <= 4) {
+                        cd = compact_draw_regs<NV>(sh, rp, w, vmax, V, qj, uf, tid);
+                        if (cd.used && cd.y < 0 && qj)
+                            cd = compact_draw_regs<NV>(sh, rp, w, vmax, V, nullptr, uf, tid);
+                    } else {
+                        cd = compact_draw<NV>(sh, rp, row16, vmax, V, qj, uf, tid);
+                        if (cd.used && cd.y < 0 && qj) cd = compact_draw<NV>(sh, rp, row16, vmax, V, nullptr, uf, tid);
+                    }
                     y = cd.y;
                     drawn = cd.used;
                 }
@@ -654,34 +720,22 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_rows_kernel(
     }
     if (!done) acc = j < D && accepted_here();
     if (!acc && !drawn) {
+        const double uf = draw_uniform();
         y = qj ? fused_draw<T, true>(sh, rp, row, qj, V, uf) : fused_draw<T, false>(sh, rp, row, nullptr, V, uf);
         if (y < 0 && qj) y = fused_draw<T, false>(sh, rp, row, nullptr, V, uf);
     }
-    if (!acc && y < 0) y = (int64_t)(((uint64_t)(uf * 0x1p24) * (uint64_t)V) >> 24);
-    if (tid == 0) {
-        accepted[b * N + j] = acc ? (int32_t)0x80000000u : (int32_t)y;
-        const uint32_t done_rows =
-            __hip_atomic_fetch_add(&counter[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        const bool last = done_rows == (uint32_t)N;
-        // only the request's last workgroup acquires: it reads the other rows' results
-        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        sh.acc = last ? 1 : 0;
-    }
-    __syncthreads();
-    if (!sh.acc) return;
-    // the request's last row: L = the first row without the accept bit (D if
-    // none); tokens x_0..x_{L-1}, the token drawn on row L, then -1
-    if (tid < kWave) {
-        const int32_t v = tid < N ? accepted[b * N + tid] : 0;
-        const uint64_t rej = __ballot(tid < D && v >= 0);
-        const int L = rej ? __ffsll((unsigned long long)rej) - 1 : D;
-        const int32_t yl = read_lane(v, L);
-        if (tid < N) accepted[b * N + tid] = tid < L ? x[b * D + tid] : (tid == L ? yl : -1);
-        if (tid == 0) {
-            accept_len[b] = L;
-            __hip_atomic_store(&counter[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (!acc && y < 0) y = (int64_t)(((uint64_t)(draw_uniform() * 0x1p24) * (uint64_t)V) >> 24);
+    // the hand-off of sv_rowpar.hpp: a row ends the chain when its draft is
+    // rejected (or it is the bonus row); the request's last workgroup gets
+    // L = the first such row and the token row L drew
+    if (tid >= kWave) return;
+    int32_t yt = -1;
+    const int L = RowPar(ws, slot).arrive(j, N, j == D || !acc, (int32_t)(acc ? 0 : y), yt);
+    if (L < 0) return;
+    // tokens x_0..x_{L-1}, the token drawn on row L, then -1
+    const int32_t yl = read_lane(yt, L);
+    if (tid < N) accepted[b * N + tid] = tid < L ? x[b * D + tid] : (tid == L ? yl : -1);
+    if (tid == 0) accept_len[b] = L;
 }
 
 // Single-step sampling ("tokenspeed sampling/backends/flashinfer.py",
@@ -776,7 +830,7 @@ hipError_t launch_sample(const void* logits, int dtype, const float* temperature
 int64_t verify_fused_max_vocab() { return (int64_t)kFvMaxChunks * kFvChunk; }
 
 int64_t verify_fused_workspace_bytes(int64_t n_req, int D) {
-    return (D > 0 && n_req > 0 && n_req * (D + 1) <= kFusedRowsMax) ? (n_req * 4 + 255) / 256 * 256 : 0;
+    return (D > 0 && n_req > 0 && n_req * (D + 1) <= kFusedRowsMax) ? rowpar_workspace_bytes(n_req) : 0;
 }
 
 template <typename T, int NV>
@@ -785,12 +839,12 @@ static void launch_fv(const T* logits, const float* temperature, const int32_t* 
                       int D, int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted,
                       int32_t* accept_len, void* workspace, hipStream_t stream) {
     // small batches: one workgroup per row when every row fits on its own CU
-    // (and the caller gave the per-request counters)
+    // (and the caller gave the workspace)
     const int64_t rows = n_req * (D + 1);
     if (workspace && verify_fused_workspace_bytes(n_req, D) > 0 && rows <= device_compute_units()) {
         hipLaunchKernelGGL((verify_fused_rows_kernel<T, NV>), dim3((unsigned)rows), dim3(kFvBlock), 0, stream,
                            logits, temperature, top_k, top_p, q, x, seed, offset, B, D, V, req_index, accepted,
-                           accept_len, static_cast<uint32_t*>(workspace));
+                           accept_len, workspace);
         return;
     }
     hipLaunchKernelGGL((verify_fused_kernel<T, NV>), dim3((unsigned)n_req), dim3(kFvBlock), 0, stream, logits,
