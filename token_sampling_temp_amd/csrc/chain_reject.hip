@@ -327,18 +327,36 @@ __device__ int64_t draw_row_single(const float* pr, int64_t V, double uf, ChainS
     return sh.y;
 }
 
-// Cross-workgroup hand-off of chunk sums (LLVM AMDGPU memory model, agent
-// scope).  Every workgroup of a request stores its sums with plain stores;
-// after a workgroup barrier, thread 0 adds one to the request's counter with
-// an acquire-release RMW at agent scope.  The release half orders the whole
-// workgroup's stores (they happen before it through the barrier) ahead of the
-// increment; the workgroup whose increment returns C - 1 is the last one, and
-// the acquire half of that same RMW, followed by a barrier, orders its loads
-// of every other workgroup's sums after their stores.  On gfx950 the compiler
-// implements the release with an L2 write-back (buffer_wbl2) and the acquire
-// with an L2 invalidate (buffer_inv): each split workgroup pays both once.
+// Cross-workgroup hand-off of chunk sums, built on single-location
+// coherence alone (no ordering between different words is assumed, so no
+// L2 write-back or invalidate is needed; on gfx950 an agent-scope release
+// costs a write-back of the L2).  A chunk sum is never negative, so its sign
+// bit is free: each workgroup stores sum | 2^63 with a relaxed 64-bit atomic
+// store, then counts itself in with a relaxed add on the request's counter.
+// The workgroup whose add returns C - 1 reads every sum, waiting until bit
+// 63 shows (a workgroup barrier puts every store of a workgroup before its
+// add, so the stores have been issued and the wait ends; the bound only
+// keeps a broken invariant from hanging the device), and once it holds a
+// sum writes zero back.
+constexpr uint64_t kSumWritten = 1ull << 63;
+
+__device__ __forceinline__ void publish_sum(double* p, double v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v) | kSumWritten,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ double take_sum(const double* p) {
+    uint64_t u = 0;
+    for (int spin = 0; spin < (1 << 20); ++spin) {
+        u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (u & kSumWritten) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return __longlong_as_double((long long)(u & ~kSumWritten));
+}
+
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, int C) {
-    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(C - 1);
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(C - 1);
 }
 
 // Segment pass for rows that are 16-byte aligned with V a multiple of 4 (and
@@ -666,7 +684,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
         const int64_t ch = chunk0 + (int64_t)lane * kChainWaves + wid;
         if (lane < R && ch < nchunks) {
             if (solo) sh.chunk[ch] = mine;
-            else partial[slot * nchunks + ch] = mine;
+            else publish_sum(&partial[slot * nchunks + ch], mine);
         }
     }
     __syncthreads();
@@ -687,7 +705,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t i = tid + (int64_t)k * kChainBlock;
-            v[k] = i < nchunks ? part[i] : 0.0;
+            v[k] = i < nchunks ? take_sum(&part[i]) : 0.0;
         }
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
@@ -702,7 +720,8 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
         const int cstar =
             nchunks <= 256 ? pick_chunk256(sh.chunk, (int)nchunks, uf, R_tot, base, force_last)
             : sums_in_lds  ? wave_pick((int)nchunks, [&](int i) { return sh.chunk[i]; }, R_tot, uf, base, force_last)
-                           : wave_pick((int)nchunks, [&](int i) { return part[i]; }, R_tot, uf, base, force_last);
+                           : wave_pick((int)nchunks, [&](int i) { return take_sum(&part[i]); }, R_tot, uf, base,
+                                       force_last);
         int64_t y = -1;
         if (cstar >= 0) {
             int64_t lastpos;
@@ -717,9 +736,14 @@ __global__ __launch_bounds__(kChainBlock) void chain_reject_kernel(
     if (!solo) {
         // every workspace byte this call used goes back to zero (its counter
         // below), so the workspace can serve any later call whatever its
-        // layout; the next kernel boundary orders these stores
+        // layout; each sum is held (its written bit seen) before it is
+        // cleared, and the next kernel boundary orders these stores
         double* mine_part = partial + slot * nchunks;
-        for (int64_t i = tid; i < nchunks; i += kChainBlock) mine_part[i] = 0.0;
+        for (int64_t i = tid; i < nchunks; i += kChainBlock) {
+            take_sum(&mine_part[i]);
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(&mine_part[i]), (uint64_t)0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     int64_t y = sh.y;
     if (y < 0 && (resid || point)) y = draw_row_single(pr, V, uf, sh);
