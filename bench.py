@@ -24,8 +24,12 @@ probabilities), ``large_vocab_ragged`` (per-request verify lengths U{1..6}
 over packed rows; rows/s counts the verified rows), ``large_vocab_ragged_d2t``
 (the same with draft rows over a 32000-entry draft vocabulary read through
 the inverse d2t table), ``d2t_expand`` (1280
-draft rows of a 32000-entry draft vocabulary placed in V=128256) and
-``sample`` (single-step sampling of 1024 bf16 rows of V=129280).
+draft rows of a 32000-entry draft vocabulary placed in V=128256),
+``sample`` (single-step sampling of 1024 bf16 rows of V=129280) and
+``gumbel`` (the mixed batch's 256 temperature-only requests through the
+Gumbel-max call alone; arithmetic-bound, so its roofline is the vector
+ALU's: entries/s against the issue rate of the kernel's instruction mix and
+against a probe running the same arithmetic with no memory traffic).
 
 The CPU baseline is the numpy oracle timed on this host on the same inputs
 (whole batches repeated for --cpu-seconds), single threaded.  For the chain
@@ -59,6 +63,21 @@ if ROOT not in sys.path:
 METRIC = "verified vocab rows/sec (batch×(D+1)) + achieved HBM GB/s vs MI355X peak"
 PEAK_HBM_GBS = 8000.0
 PROBE_GRANULE = 64     # bytes a single-element probe costs in HBM (one 64-byte line)
+# Vector ALU issue of MI355X: 256 CUs x 4 SIMDs at 2.4 GHz, one wave64
+# instruction per SIMD every 4 cycles (16 lanes per cycle).
+SIMD_CYCLES_PER_S = 256 * 4 * 2.4e9
+# The Gumbel-max hot loop as compiled for gfx950 (one pipelined iteration of
+# gumbel_sample.hip = 4 groups of 4 entries per lane) issues 473 VALU
+# instructions: 136 v_xor, 68 v_mad_u64_u32 (the Philox products), 48
+# v_mul_f32, 32 v_log_f32, 16 v_fmac_f32 and 173 others (compares, selects,
+# adds, shifts, conversions).  On gfx950 the 64-bit multiply-add and the
+# logarithm issue at the full rate like the rest (the arithmetic probe,
+# svprobe_gumbel_alu, runs this mix at 3.9 cycles per wave64 instruction), so
+# a group costs 473 / 4 instructions x 4 cycles per wave64.
+GUMBEL_VALU_PER_GROUP = 473 / 4
+GUMBEL_CYCLES_PER_GROUP = GUMBEL_VALU_PER_GROUP * 4
+# entries per second with every SIMD issuing that loop without a stall
+GUMBEL_ALU_PEAK_GES = SIMD_CYCLES_PER_S * 64 * 4 / GUMBEL_CYCLES_PER_GROUP / 1e9
 
 
 def log(msg):
@@ -74,7 +93,7 @@ def parse():
                     choices=["large_vocab_chain_reject", "large_vocab_target_only", "large_vocab_ragged",
                              "large_vocab_ragged_d2t", "d2t_expand",
                              "sample", "topk_topp_chain", "topk_topp_fused", "greedy",
-                             "mixed", "mixed_fused"])
+                             "mixed", "mixed_fused", "gumbel"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -541,7 +560,7 @@ class SampleWorkload:
     with top-k in {0, 20, 100}, top-p 1 or U[0.8, 0.95] and min-p in {0, 0.05} (joint filter)."""
     name = "sample"
     kernel = "sample_kernel"
-    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_common.hpp")
+    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_rowpar.hpp", "sv_common.hpp")
     counters = "sample_counters.txt"
     dtype = "bf16"
 
@@ -600,7 +619,7 @@ class SampleWorkload:
 class GreedyWorkload:
     name = "greedy"
     kernel = "greedy_verify_kernel"
-    sources = ("greedy_verify.hip", "sv_argmax.hpp", "sv_common.hpp")
+    sources = ("greedy_verify.hip", "sv_argmax.hpp", "sv_rowpar.hpp", "sv_common.hpp")
     counters = "greedy_verify_counters.txt"
     dtype = "bf16"
 
@@ -654,6 +673,7 @@ class GreedyWorkload:
 class TopkToppWorkload:
     name = "topk_topp_chain"
     kernel = "softmax_renorm_rr_kernel"
+    dominant_call = "softmax_renorm"
     sources = ("softmax_renorm.hip", "sv_softmax.hpp", "sv_argmax.hpp", "sv_common.hpp")
     counters = "softmax_renorm_topk_topp_counters.txt"
     dtype = "bf16"
@@ -734,10 +754,11 @@ class TopkToppWorkload:
 class TopkToppFusedWorkload(TopkToppWorkload):
     """The top-k/top-p batch (B=64 D=3 V=32000 bf16, T 0.7, k 50, top_p 0.9) through the fused call: target rows
     from logits and chain rejection in one call, no probabilities stored.  64 x 4 rows fit one per CU, so the
-    call evaluates every row of a request at once and assembles the chain in a second, tiny kernel."""
+    call evaluates every row of a request at once; the request's last row to finish assembles its outputs."""
     name = "topk_topp_fused"
     kernel = "verify_fused_rows_kernel"
-    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_common.hpp")
+    dominant_call = "verify_fused"
+    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_rowpar.hpp", "sv_common.hpp")
     counters = "verify_fused_topk_topp_counters.txt"
 
     def __init__(self, dev, replicas):
@@ -780,6 +801,7 @@ class MixedWorkload:
     4096 r apart) rotate so that no call finds the previous call's rows in the Infinity Cache."""
     name = "mixed"
     kernel = "softmax_renorm_rr_kernel"
+    dominant_call = "softmax_renorm"
     sources = ("softmax_renorm.hip", "sv_softmax.hpp", "sv_argmax.hpp", "sv_common.hpp")
     counters = "softmax_renorm_mixed_counters.txt"
     dtype = "bf16"
@@ -912,13 +934,137 @@ class MixedWorkload:
                 "sample": f"{n} requests (random order over all modes), {el:.1f}s single-threaded numpy"}
 
 
+class GumbelWorkload:
+    """The mixed batch's 256 temperature-only requests (B=1024 D=7 V=129280 bf16) through
+    gumbel_sample alone, R = 4 replicas.  Arithmetic-bound: each entry costs a quarter of a
+    Philox4x32-10 block and two hardware logarithms, so its roofline is the vector ALU's."""
+    name = "gumbel"
+    kernel = "gumbel_rows_kernel"
+    sources = ("gumbel_sample.hip", "sv_gumbel.hpp", "sv_rowpar.hpp", "sv_argmax.hpp", "sv_common.hpp")
+    counters = "gumbel_sample_counters.txt"
+    valu_counters = "gumbel_sample_valu_counters.txt"
+    dtype = "bf16"
+    bound = "alu"
+
+    def __init__(self, dev, replicas):
+        from workloads import MODE_TEMPERATURE, make_config
+        import torch
+        import token_sampling_temp_amd as sv
+        self.sv = sv
+        h = make_config(5)
+        self.host = h
+        self.B, self.D, self.V = h["B"], h["D"], h["V"]
+        self.R = replicas or 4
+        self.x = _t(h["draft_ids"], dev)
+        self.T = _t(h["temperature"], dev)
+        self.seed = _t(h["seed"], dev)
+        self.idx_host = np.nonzero(h["modes"] == MODE_TEMPERATURE)[0].astype(np.int32)
+        self.idx = _t(self.idx_host, dev)
+        self.reps = []
+        for r in range(self.R):
+            off = (h["offset"] + np.uint64(4096 * r)).astype(np.uint64)
+            self.reps.append(dict(z=_bf16(h["logits"], dev), off=_t(off, dev)))
+        N = self.D + 1
+        self.out = {"accepted_tokens": torch.empty((self.B, N), dtype=torch.int32, device=dev),
+                    "accept_length": torch.empty((self.B,), dtype=torch.int32, device=dev)}
+        self.rows = len(self.idx_host) * N
+
+    def step(self, i):
+        r = self.reps[i % self.R]
+        self.sv.gumbel_sample(r["z"], self.T, self.x, self.seed, r["off"], req_index=self.idx, out=self.out)
+
+    def _lengths(self):
+        Ls = []
+        for i in range(self.R):
+            self.step(i)
+            Ls.append(self.out["accept_length"].cpu().numpy().astype(np.int64)[self.idx_host])
+        return Ls
+
+    def algorithmic_bytes(self):
+        """The rows strict acceptance needs (L + 1 per request), read once."""
+        Ls = self._lengths()
+        self.L = np.concatenate(Ls)
+        self.entries = float(np.mean([((L + 1) * self.V).sum() for L in Ls]))
+        return self.entries * 2
+
+    def extra(self):
+        return {"mean_accept_length": round(float(self.L.mean()), 4)}
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "requests": len(self.idx_host), "draft_tokens": self.D,
+                "vocab": self.V, "input": "bf16 logits, per-request temperature in [0.5, 1.2]",
+                "replicas": self.R}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        rows, t0, n = 0, time.perf_counter(), 0
+        while True:
+            b = int(self.idx_host[n % len(self.idx_host)])
+            r = oracle.gumbel_sample(h["logits"], "bf16", h["temperature"], h["draft_ids"], h["seed"], h["offset"],
+                                     requests=[b])
+            rows += int(r["accept_length"][b]) + 1
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} requests ({rows} sampled rows), {el:.1f}s single-threaded numpy float64"}
+
+
+def gumbel_alu_ceiling(dev):
+    """Entries/s the Gumbel-max arithmetic reaches with no memory traffic (the sampling kernel's
+    per-group function on 1024-thread workgroups, logits made in registers), best of a few grids."""
+    import ctypes
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "token_sampling_temp_amd", "libsvprobe.so"))
+    L.svprobe_gumbel_alu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.svprobe_gumbel_alu.restype = ctypes.c_int
+    sink = torch.zeros(16 * 4096, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    best = (0.0, None)
+    groups = 256
+    for grid in (256, 512, 1024):
+        def run():
+            st = L.svprobe_gumbel_alu(groups, grid, 1 << 30, ctypes.c_void_p(sink.data_ptr()), sp)
+            assert st == 0, st
+        for _ in range(3):
+            run()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        n = 10
+        for _ in range(n):
+            run()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        ges = grid * 1024 * groups * 4 * n / (s0.elapsed_time(s1) * 1e-3) / 1e9
+        if ges > best[0]:
+            best = (ges, {"grid": grid, "groups_per_thread": groups})
+    return best
+
+
+def load_valu_cycles(summary, digest):
+    """Weighted VALU cycles per launch from a committed counter summary taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_digest:\s*([0-9a-f]+)", txt)
+    m_c = re.search(r"weighted_valu_cycles_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_c or m_src.group(1) != digest:
+        return None
+    return float(m_c.group(1))
+
+
 class MixedFusedWorkload(MixedWorkload):
     """The mixed batch with its top-k and top-p requests through the fused call
     (target rows from logits and chain rejection in one launch, no probabilities
     stored): greedy_verify, gumbel_sample, verify_fused."""
     name = "mixed_fused"
     kernel = "verify_fused_kernel"
-    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_common.hpp")
+    dominant_call = "verify_fused"
+    sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_rowpar.hpp", "sv_common.hpp")
     counters = "verify_fused_mixed_counters.txt"
     needs_probs = False
 
@@ -973,7 +1119,7 @@ class MixedFusedWorkload(MixedWorkload):
 WORKLOADS = {c.name: c for c in (ChainWorkload, TargetOnlyWorkload, RaggedWorkload, RaggedD2tWorkload,
                                  DraftVocabWorkload,
                                  SampleWorkload, GreedyWorkload, TopkToppWorkload, TopkToppFusedWorkload,
-                                 MixedWorkload, MixedFusedWorkload)}
+                                 MixedWorkload, MixedFusedWorkload, GumbelWorkload)}
 
 
 def _spread(us):
@@ -1085,11 +1231,34 @@ def main():
     }
     if calls:
         out["per_call"] = calls
-        dom = calls.get(wl.kernel.replace("_kernel", ""))
+        dom = calls.get(getattr(wl, "dominant_call", wl.kernel.replace("_kernel", "")))
         if dom:   # the dominant kernel timed on its own
             us = dom["us"]
             out["roofline"]["achieved"] = alg_bytes / (us * 1e-6) / 1e9
             out["roofline"]["frac"] = out["roofline"]["achieved"] / PEAK_HBM_GBS
+    if getattr(wl, "bound", "hbm") == "alu":
+        # arithmetic-bound: entries per second against the vector ALU's issue rate for the
+        # kernel's instruction mix, and against the same arithmetic with no memory traffic
+        ges = wl.entries / (ms * 1e-3) / 1e9
+        log("measuring the Gumbel arithmetic ceiling")
+        ceil, ceil_cfg = gumbel_alu_ceiling(dev)
+        hbm = out["roofline"]
+        out["roofline"] = {"bound": "alu", "kernel": wl.kernel, "achieved": ges, "peak": GUMBEL_ALU_PEAK_GES,
+                           "unit": "G entries/s", "frac": ges / GUMBEL_ALU_PEAK_GES, "traffic": traffic,
+                           "peak_derivation": f"{SIMD_CYCLES_PER_S / 1e9:.1f} G SIMD-cycles/s x 64 lanes x 4 "
+                           f"entries per {GUMBEL_CYCLES_PER_GROUP:.0f} cycles (one wave64 group)",
+                           "algorithmic_entries_per_launch": wl.entries, "kernel_source_digest": digest,
+                           "measured_alu_ceiling_Gentries": round(ceil, 1), "alu_ceiling_config": ceil_cfg,
+                           "frac_of_alu_ceiling": ges / ceil,
+                           "hbm_GBps": hbm["achieved"], "hbm_frac": hbm["frac"]}
+        cyc = load_valu_cycles(wl.valu_counters, digest)
+        if cyc is not None:   # every VALU instruction the kernel issued, from the counter summary
+            out["roofline"]["valu_busy_frac"] = cyc / SIMD_CYCLES_PER_S / (ms * 1e-3)
+        if getattr(wl, "parity", None) is not None:
+            out["parity"] = wl.parity
+        out.update(wl.extra())
+        print(json.dumps(out), flush=True)
+        return
     out["roofline"]["measured_read_stream_GBps"] = round(peak_read, 1)
     out["roofline"]["read_stream_config"] = peak_cfg
     out["roofline"]["frac_of_stream_peak"] = out["roofline"]["achieved"] / peak_read

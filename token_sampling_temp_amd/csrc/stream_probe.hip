@@ -1,12 +1,17 @@
-// Read-stream probe: the HBM read rate a plain kernel reaches on this GPU,
-// used by the benchmark as the measured ceiling beside the 8 TB/s data-sheet
-// peak.  Not part of the verification library.
+// Measurement probes used by the benchmark, not part of the verification
+// library: the HBM read rate a plain kernel reaches on this GPU (the
+// measured ceiling beside the 8 TB/s data-sheet peak), and the rate the
+// Gumbel-max arithmetic reaches with no memory traffic at all (the measured
+// ceiling of that arithmetic-bound kernel).
 //
+// Read stream:
 // Each workgroup reads one contiguous region with non-temporal 16-byte loads,
 // U loads in flight per thread, and folds the words with XOR so the loads
 // cannot be removed; one word per workgroup is written to `sink`.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "sv_gumbel.hpp"
 
 namespace {
 
@@ -40,6 +45,34 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* __restric
     if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + threadIdx.x / 64] = acc;
 }
 
+// Gumbel-max arithmetic alone: 1024-thread workgroups (as the sampling
+// kernel) where every thread folds `groups` entry groups with the sampling
+// kernel's own per-group function; the logits are made from the group index
+// (four bit operations per group, as many as unpacking four bf16 logits), so
+// nothing is loaded.  One word per wave goes to sink.
+__global__ __launch_bounds__(1024) void gumbel_alu_kernel(int groups, int V, float invT, uint64_t seed,
+                                                          uint64_t subseq, uint32_t* __restrict__ sink) {
+    float best = -INFINITY;
+    int bi = -1;
+    const int g0 = (int)(blockIdx.x * 1024 + threadIdx.x);
+    const int stride = (int)(gridDim.x * 1024);
+    for (int k = 0; k < groups; ++k) {
+        const int g = g0 + k * stride;
+        const uint32_t bits = 0x3F800000u | (((uint32_t)g & 0xFFFFu) << 4);
+        const float f[4] = {__uint_as_float(bits), __uint_as_float(bits | 1u), __uint_as_float(bits | 2u),
+                            __uint_as_float(bits | 3u)};
+        sv::gumbel_group(f, g, V, invT, seed, subseq, best, bi);
+    }
+    uint32_t acc = __float_as_uint(best) ^ (uint32_t)bi;
+    acc ^= __shfl_xor(acc, 1);
+    acc ^= __shfl_xor(acc, 2);
+    acc ^= __shfl_xor(acc, 4);
+    acc ^= __shfl_xor(acc, 8);
+    acc ^= __shfl_xor(acc, 16);
+    acc ^= __shfl_xor(acc, 32);
+    if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 16 + threadIdx.x / 64] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -60,6 +93,20 @@ int svprobe_read_stream(const void* buf, int64_t bytes, int grid, int loads, uin
     else if (loads == 8) hipLaunchKernelGGL(read_stream_kernel<8>, dim3(grid), dim3(256), 0, st, b, nvec, per_wg, sink);
     else if (loads == 16) hipLaunchKernelGGL(read_stream_kernel<16>, dim3(grid), dim3(256), 0, st, b, nvec, per_wg, sink);
     else return 1;
+    return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// Run the Gumbel-max arithmetic on `grid` workgroups of 1024 threads, each
+// thread folding `groups` groups of 4 entries (grid * 1024 * groups * 4
+// entries in all; V bounds the entry index as in the kernel and should exceed
+// it).  sink: device memory of 16 * grid words.  Returns 0 on success, 1 for
+// bad arguments, 3 for a launch error.
+int svprobe_gumbel_alu(int groups, int grid, int V, uint32_t* sink, void* stream) {
+    if (!sink || groups < 1 || grid < 1 || grid > 65536 || V < 1 ||
+        (int64_t)grid * 1024 * groups > (int64_t)INT32_MAX / 4)
+        return 1;
+    hipLaunchKernelGGL(gumbel_alu_kernel, dim3(grid), dim3(1024), 0, static_cast<hipStream_t>(stream), groups, V,
+                       1.25f, (uint64_t)0x243F6A8885A308D3ull, (uint64_t)7, sink);
     return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
