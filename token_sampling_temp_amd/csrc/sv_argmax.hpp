@@ -14,17 +14,16 @@ struct ArgmaxShared {
 };
 
 // Exact slow path: packed (order-preserving key, index) maximum.  Handles NaN
-// (every NaN is the largest key; the first one wins).
+// (every NaN is the largest key; the first one wins).  Only rows holding a
+// NaN come here, so it reads one element at a time and keeps few registers
+// (a call's register count is the largest of its callees').
 template <int BLOCK, typename T>
-__device__ int64_t row_argmax_exact(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh) {
-    uint64_t best = 0;
-    bool any = false;
-    row_foreach<BLOCK, false>(row, V, [&](float v, int64_t idx) {
-        const uint64_t k = pack_key_index(float_key(v), idx);
-        if (!any || k > best) best = k;
-        any = true;
-    });
-    if (!any) best = 0;
+__device__ __noinline__ int64_t row_argmax_exact(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh) {
+    uint64_t best = 0;   // below every packed key of an element
+    for (int64_t i = threadIdx.x; i < V; i += BLOCK) {
+        const uint64_t k = pack_key_index(float_key(load_elem(row + i)), i);
+        best = k > best ? k : best;
+    }
     const uint64_t m = block_reduce<BLOCK>(best, OpMaxU64{}, (uint64_t)0, sh.red_u);
     return packed_index(m);
 }

@@ -712,8 +712,6 @@ struct RrStats {
 // that a caller can revisit only the vectors that hold kept keys.
 // probe (>= 0): the key of element `probe` is left in sh.probe_key (by the
 // thread that holds it, before the selection's barriers).
-// ISSUED: the caller has already issued the loads into w (rr_issue), so
-// that they need not wait for anything the caller reads first.
 template <int NV>
 __device__ __forceinline__ void rr_issue(const uint16_t* __restrict__ row, int64_t V, int tid, u32x4 (&w)[NV]) {
     const __amdgpu_buffer_rsrc_t rin = make_rsrc(row, (uint32_t)(V * 2));
@@ -722,14 +720,14 @@ __device__ __forceinline__ void rr_issue(const uint16_t* __restrict__ row, int64
         w[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, tid * 16, v * kRrBlock * 16, 0));
 }
 
-template <int NV, bool JOINT = false, bool VMAX = false, bool ISSUED = false>
+template <int NV, bool JOINT = false, bool VMAX = false>
 __device__ __forceinline__ bool rr_stats(RrShared& sh, const uint16_t* __restrict__ row, int64_t V, float Tm,
                                          int32_t k, float tp, int tid, u32x4 (&w)[NV], RrStats& st, float mp,
                                          uint32_t (&vmax)[(NV + 1) / 2], int64_t probe = -1) {
     const int vfull = (int)(V / (kRrBlock * 8));   // vectors in range for every thread
     auto ebase = [&](int v) { return (v * kRrBlock + tid) * 8; };
     // ---- issue the row's loads
-    if constexpr (!ISSUED) rr_issue<NV>(row, V, tid, w);
+    rr_issue<NV>(row, V, tid, w);
     // ---- clear the histogram (the previous row's table reads are done first)
     lds_barrier();
     {
