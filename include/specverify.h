@@ -404,18 +404,20 @@ int specverify_gumbel_sample_workspace_bytes(int64_t n_req, int64_t D, int64_t* 
  * accept_length   [B] int32        output
  *
  * workspace, workspace_bytes
- *                 caller-owned device memory or NULL.  Small batches (D > 0
- *                 and n_req * (D + 1) at most 256 and at most the device's
- *                 compute units) evaluate every target row of a request at
- *                 once, one workgroup per row, and need
+ *                 caller-owned device memory or NULL.  With it (D > 0) every
+ *                 (request, target row) gets a workgroup of its own, rows
+ *                 dispatched in row order: when all rows fit on the device's
+ *                 compute units at once every row is evaluated, otherwise a
+ *                 row after one that already ended its request's chain is
+ *                 skipped.  It takes
  *                 specverify_verify_fused_workspace_bytes(n_req, D) bytes
  *                 (one 128-byte line per request where the rows meet;
  *                 8-byte aligned, all zero when a call starts; every call
  *                 leaves it zero, so zero it once and reuse it; calls sharing
- *                 it must not overlap).  With NULL,
- *                 those batches evaluate a request's rows in order instead
- *                 (same results, longer latency).  A short or misaligned
- *                 workspace returns SPECVERIFY_INVALID_ARGUMENT.
+ *                 it must not overlap).  With NULL, one workgroup per request
+ *                 evaluates its rows in order instead (same results).  A
+ *                 short or misaligned workspace returns
+ *                 SPECVERIFY_INVALID_ARGUMENT.
  *
  * Equivalent to specverify_softmax_renorm on the logits followed by
  * specverify_chain_reject on its output (same tokens whenever that output
@@ -433,8 +435,7 @@ int specverify_verify_fused(const void* target_logits, int dtype, const float* t
 
 /*
  * Workspace size of specverify_verify_fused: 128 bytes per request, rounded
- * up to 256, when D > 0 and n_req * (D + 1) <= 256; else 0 (no workspace
- * used).
+ * up to 256, when D > 0 and n_req > 0; else 0 (no workspace used).
  * Host-only.  n_req >= 0, 0 <= D <= 16, bytes non-NULL; else
  * SPECVERIFY_INVALID_ARGUMENT.
  */

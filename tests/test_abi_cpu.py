@@ -196,8 +196,8 @@ def test_verify_fused_workspace_query():
     # one 128-byte line per request, rounded up to 256
     assert L.specverify_verify_fused_workspace_bytes(64, 3, ctypes.byref(out)) == 0 and out.value == 8192
     assert L.specverify_verify_fused_workspace_bytes(85, 2, ctypes.byref(out)) == 0 and out.value == 11008
-    # past 256 rows, or without drafts, no workspace is used
-    assert L.specverify_verify_fused_workspace_bytes(65, 3, ctypes.byref(out)) == 0 and out.value == 0
+    # any batch with drafts takes one; without drafts none is used
+    assert L.specverify_verify_fused_workspace_bytes(65, 3, ctypes.byref(out)) == 0 and out.value == 8448
     assert L.specverify_verify_fused_workspace_bytes(100, 0, ctypes.byref(out)) == 0 and out.value == 0
     assert L.specverify_verify_fused_workspace_bytes(-1, 3, ctypes.byref(out)) == 1
     assert L.specverify_verify_fused_workspace_bytes(4, 17, ctypes.byref(out)) == 1

@@ -28,7 +28,7 @@ Functions mirror the C entry points:
   one-workgroup-per-request form)
 * ``verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None,
   top_p=None, req_index=None, workspace=None)``: softmax_renorm followed by chain_reject in one call;
-  ``verify_fused_workspace_bytes(n_req, D)``: its counters for small batches
+  ``verify_fused_workspace_bytes(n_req, D)``: the per-request lines of its one-workgroup-per-row form
 
 ``accept_length`` is the number of accepted drafts L in [0, D]; a request
 emits L + 1 tokens.
@@ -325,7 +325,7 @@ def _query(fn, n_req, D) -> int:
 
 
 def verify_fused_workspace_bytes(n_req, D) -> int:
-    """Bytes of per-request counters verify_fused uses for small batches (0: none)."""
+    """Bytes of the per-request lines verify_fused's one-workgroup-per-row form uses (0: none)."""
     return _query("specverify_verify_fused_workspace_bytes", n_req, D)
 
 
@@ -366,9 +366,9 @@ def _fused_workspace(workspace, n_req, D, device):
 def verify_fused(target_logits, temperature, draft_probs, draft_ids, seed, offset, top_k=None, top_p=None,
                  req_index=None, out=None, workspace=None):
     """Target rows from logits (softmax, top-k, top-p) then chain rejection, in one call;
-    returns (accepted_tokens [B, D+1] int32, accept_length [B] int32).  Small batches use a zero-filled
-    uint8 workspace of verify_fused_workspace_bytes(n_req, D) bytes (kept per device and stream when
-    ``workspace`` is None)."""
+    returns (accepted_tokens [B, D+1] int32, accept_length [B] int32).  With a zero-filled uint8
+    workspace of verify_fused_workspace_bytes(n_req, D) bytes (kept per device and stream when
+    ``workspace`` is None; False for none) every target row gets a workgroup of its own."""
     torch = _torch()
     _need(target_logits, "target_logits", (torch.float32, torch.bfloat16), None, 3)
     dev = target_logits.device

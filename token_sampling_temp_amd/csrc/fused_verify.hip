@@ -611,16 +611,18 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_kernel(
     if (tid == 0) accept_len[b] = L;
 }
 
-// Fused verify for small batches (n_req * (D + 1) rows at most one per CU):
-// every row (request, j) gets its own workgroup, so a request's rows are
-// evaluated at the same time instead of one after another.  Each workgroup
+// Fused verify, one workgroup per row (request, j), rows dispatched in row
+// order (every request's row 0 first): a request's rows are evaluated side
+// by side instead of one after another.  When the rows outnumber the CUs
+// (skip_ended), a row whose request already has an ended row before it is
+// only counted in (its result cannot be used).  Each workgroup
 // computes row j's statistics and accept test exactly as verify_fused_kernel
 // does; a row that rejects (or the bonus row D) also draws its token, as it
 // would if the chain stopped there.  Rows meet through the request's line of
 // the workspace (sv_rowpar.hpp): each stores its drawn token and counts
 // itself in, flagging the chain's end if it rejected or is row D; the last
 // workgroup takes L = the first flagged row and writes x_0..x_{L-1}, the
-// token row L drew, then -1.  Rows after L are read although the serial
+// token row L drew, then -1.  Rows after L may be read although the serial
 // kernel would stop before them; the results are bit-identical to it.  A
 // request listed twice has a line per listing and gets the same outputs
 // twice.
@@ -629,15 +631,35 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_rows_kernel(
     const T* __restrict__ logits, const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
     const float* __restrict__ top_p, const float* __restrict__ q, const int32_t* __restrict__ x,
     const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
-    const int32_t* __restrict__ req_index, int32_t* __restrict__ accepted, int32_t* __restrict__ accept_len,
-    void* __restrict__ ws) {
+    const int32_t* __restrict__ req_index, int64_t n_req, int32_t* __restrict__ accepted,
+    int32_t* __restrict__ accept_len, void* __restrict__ ws, int skip_ended) {
     __shared__ FusedShared sh;
     const int N = D + 1;
-    const int64_t slot = blockIdx.x / N;
-    const int j = (int)(blockIdx.x - slot * N);
+    // row-major: every request's row 0 is dispatched before any row 1
+    const int j = (int)(blockIdx.x / (uint64_t)n_req);
+    const int64_t slot = (int64_t)blockIdx.x - (int64_t)j * n_req;
     const int64_t b = req_index ? (int64_t)req_index[slot] : slot;
     if (b < 0 || b >= B) return;   // uniform over the workgroup
     const int tid = threadIdx.x;
+    const RowPar rpar(ws, slot);
+    if (skip_ended && j > 0) {
+        // a row after one that already ended the chain is not needed: count it in and leave
+        if (tid == 0) {
+            const uint64_t w = __hip_atomic_load(rpar.word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sh.acc = (w & (((uint64_t)1 << j) - 1)) != 0 ? 1 : 0;
+        }
+        __syncthreads();
+        if (sh.acc) {
+            if (tid >= kWave) return;
+            int32_t yt = -1;
+            const int L = rpar.arrive(j, N, false, 0, yt);
+            if (L < 0) return;
+            const int32_t yl = read_lane(yt, L);
+            if (tid < N) accepted[b * N + tid] = tid < L ? x[b * D + tid] : (tid == L ? yl : -1);
+            if (tid == 0) accept_len[b] = L;
+            return;
+        }
+    }
     const float Tm = temperature[b];
     const int32_t k = top_k ? top_k[b] : 0;
     const float tp = top_p ? top_p[b] : 1.0f;
@@ -730,7 +752,7 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_rows_kernel(
     // L = the first such row and the token row L drew
     if (tid >= kWave) return;
     int32_t yt = -1;
-    const int L = RowPar(ws, slot).arrive(j, N, j == D || !acc, (int32_t)(acc ? 0 : y), yt);
+    const int L = rpar.arrive(j, N, j == D || !acc, (int32_t)(acc ? 0 : y), yt);
     if (L < 0) return;
     // tokens x_0..x_{L-1}, the token drawn on row L, then -1
     const int32_t yl = read_lane(yt, L);
@@ -830,7 +852,7 @@ hipError_t launch_sample(const void* logits, int dtype, const float* temperature
 int64_t verify_fused_max_vocab() { return (int64_t)kFvMaxChunks * kFvChunk; }
 
 int64_t verify_fused_workspace_bytes(int64_t n_req, int D) {
-    return (D > 0 && n_req > 0 && n_req * (D + 1) <= kFusedRowsMax) ? rowpar_workspace_bytes(n_req) : 0;
+    return (D > 0 && n_req > 0) ? rowpar_workspace_bytes(n_req) : 0;
 }
 
 template <typename T, int NV>
@@ -838,13 +860,14 @@ static void launch_fv(const T* logits, const float* temperature, const int32_t* 
                       const float* q, const int32_t* x, const uint64_t* seed, const uint64_t* offset, int64_t B,
                       int D, int64_t V, const int32_t* req_index, int64_t n_req, int32_t* accepted,
                       int32_t* accept_len, void* workspace, hipStream_t stream) {
-    // small batches: one workgroup per row when every row fits on its own CU
-    // (and the caller gave the workspace)
+    // with the workspace: one workgroup per row; rows that cannot all run at
+    // once skip the rows after one that ended the chain
     const int64_t rows = n_req * (D + 1);
-    if (workspace && verify_fused_workspace_bytes(n_req, D) > 0 && rows <= device_compute_units()) {
+    if (workspace && verify_fused_workspace_bytes(n_req, D) > 0) {
+        const int skip = rows > device_compute_units() ? 1 : 0;
         hipLaunchKernelGGL((verify_fused_rows_kernel<T, NV>), dim3((unsigned)rows), dim3(kFvBlock), 0, stream,
-                           logits, temperature, top_k, top_p, q, x, seed, offset, B, D, V, req_index, accepted,
-                           accept_len, workspace);
+                           logits, temperature, top_k, top_p, q, x, seed, offset, B, D, V, req_index, n_req,
+                           accepted, accept_len, workspace, skip);
         return;
     }
     hipLaunchKernelGGL((verify_fused_kernel<T, NV>), dim3((unsigned)n_req), dim3(kFvBlock), 0, stream, logits,

@@ -83,12 +83,10 @@ hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temp
 // Bytes of the row-parallel workspace Gumbel sampling takes (0: none used).
 int64_t gumbel_workspace_bytes(int64_t n_req, int D);
 
-// Fused target rows + chain rejection (V <= verify_fused_max_vocab()).
-// Batches of at most kFusedRowsMax rows (n_req * (D + 1)) may evaluate every
-// row at once when given a workspace of verify_fused_workspace_bytes(n_req, D)
-// bytes (per-request counters, zero between calls); otherwise, or with none,
-// a request's rows are evaluated in order.
-constexpr int64_t kFusedRowsMax = 256;
+// Fused target rows + chain rejection (V <= verify_fused_max_vocab()).  With
+// a workspace of verify_fused_workspace_bytes(n_req, D) bytes (one line per
+// request, zero between calls) every (request, row) gets a workgroup;
+// without one, a request's rows are evaluated in order.
 int64_t verify_fused_max_vocab();
 int64_t verify_fused_workspace_bytes(int64_t n_req, int D);
 hipError_t launch_verify_fused(const void* logits, int dtype, const float* temperature, const int32_t* top_k,
