@@ -1062,7 +1062,7 @@ class MixedFusedWorkload(MixedWorkload):
     (target rows from logits and chain rejection in one launch, no probabilities
     stored): greedy_verify, gumbel_sample, verify_fused."""
     name = "mixed_fused"
-    kernel = "verify_fused_kernel"
+    kernel = "verify_fused_rows_kernel"
     dominant_call = "verify_fused"
     sources = ("fused_verify.hip", "sv_softmax.hpp", "sv_draw.hpp", "sv_argmax.hpp", "sv_rowpar.hpp", "sv_common.hpp")
     counters = "verify_fused_mixed_counters.txt"
