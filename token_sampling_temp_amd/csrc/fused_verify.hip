@@ -111,6 +111,13 @@ __device__ __forceinline__ void load_q4(const float* row, int64_t idx, int64_t V
     }
 }
 
+// Probability of a kept key under register-resident statistics: the value
+// row_prob gives the logit with that key.
+__device__ __forceinline__ float key_prob(const RowProb rp, const RrShared& sh, uint32_t key) {
+    if (rp.mode == kProbTable) return sh.u.lut[max((int)key + 1 - (int)rp.kmin, 0)];
+    return key >= rp.kmin ? fast_exp2((key_to_float(key) - rp.m) * rp.scale) * rp.inv : 0.0f;
+}
+
 // Inverse-CDF draw of one index from r_v = max(0, p_v - q_v) (resid) or p_v,
 // p given by rp on the logit row zr.  Whole workgroup; returns -1 when the
 // weights have no positive mass.  Chunk c of 1024 entries is summed by one
@@ -145,7 +152,70 @@ __device__ __forceinline__ int64_t fused_draw(FusedShared& sh, const RowProb rp,
     // loads, two chunks of a wave in flight (wave w takes w, w + 16, ...)
     const int nfull = (int)(V / kFvChunk);
     int cdone = 0;   // chunks below this are summed
-    if (zvec && qvec) {
+    if constexpr (!RESID && sizeof(T) == 2) {
+        // bf16 rows without draft probabilities, 16-byte aligned: buffer loads
+        // of 16 bytes (8 entries per lane, two per chunk), four chunks of a
+        // wave in flight, every chunk including a partial last one; entries
+        // past the row read zeros and are left out.  (Chunk sums are taken
+        // over the same entries in another order than below; only their
+        // rounding differs.)
+        if ((uintptr_t)zr % 16 == 0) {
+            constexpr int kDep = 4;
+            const int nr = nch > wid ? (nch - wid + kFvWaves - 1) / kFvWaves : 0;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(zr, (uint32_t)(V * 2));
+            u32x4 zb[kDep][2];
+            auto ld = [&](int slot, int r) {
+                const uint32_t base = (uint32_t)(wid + r * kFvWaves) * (uint32_t)(kFvChunk * 2) + (uint32_t)lane * 16u;
+                zb[slot][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, base, 0, 0));
+                zb[slot][1] =
+                    __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + kFvChunk, 0, 0));
+            };
+            // register-resident statistics: one key conversion per pair of logits
+            const bool by_key = rp.mode == kProbTable || rp.mode == kProbRrExp;
+            // guard: the row's last, partial chunk (entries at or past V left
+            // out); each call below passes a constant
+            auto sum_chunk = [&](int slot, int c, bool guard) {
+                double acc = 0.0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t wd[4] = {zb[slot][h].x, zb[slot][h].y, zb[slot][h].z, zb[slot][h].w};
+                    const int64_t i0 = (int64_t)c * kFvChunk + h * (kFvChunk / 2) + lane * 8;
+                    double s8 = 0.0;
+                    if (by_key) {
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const uint32_t k2 = keys_of_pair(wd[d]);
+                            if (!guard || i0 + 2 * d < V) s8 += (double)key_prob(rp, sh.rr, k2 & 0xFFFFu);
+                            if (!guard || i0 + 2 * d + 1 < V) s8 += (double)key_prob(rp, sh.rr, k2 >> 16);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (!guard || i0 + e < V)
+                                s8 += (double)row_prob<T>(rp, sh.rr, (uint16_t)(wd[e >> 1] >> (16 * (e & 1))), i0 + e);
+                    }
+                    acc += s8;
+                }
+                publish(acc, c);
+            };
+            auto sum = [&](int slot, int r) {
+                const int c = wid + r * kFvWaves;
+                if (c < nfull) sum_chunk(slot, c, false);
+                else sum_chunk(slot, c, true);
+            };
+#pragma unroll
+            for (int j = 0; j < kDep; ++j) ld(j, j);
+            for (int r0 = 0; r0 < nr; r0 += kDep) {
+#pragma unroll
+                for (int j = 0; j < kDep; ++j) {
+                    if (r0 + j < nr) sum(j, r0 + j);
+                    ld(j, r0 + j + kDep);
+                }
+            }
+            cdone = nch;
+        }
+    }
+    if (cdone == 0 && zvec && qvec) {
         typedef typename std::conditional<sizeof(T) == 2, uint2, float4>::type ZV;
         ZV zb[2][4];
         u32x4 qb[2][4];
@@ -284,12 +354,6 @@ __device__ __forceinline__ int64_t fused_draw(FusedShared& sh, const RowProb rp,
     return sh.y;
 }
 
-// Probability of a kept key under register-resident statistics: the value
-// row_prob gives the logit with that key.
-__device__ __forceinline__ float key_prob(const RowProb rp, const RrShared& sh, uint32_t key) {
-    if (rp.mode == kProbTable) return sh.u.lut[max((int)key + 1 - (int)rp.kmin, 0)];
-    return key >= rp.kmin ? fast_exp2((key_to_float(key) - rp.m) * rp.scale) * rp.inv : 0.0f;
-}
 
 struct CompactDraw {
     int64_t y;   // the drawn index, -1 when the weights have no positive mass
