@@ -489,7 +489,8 @@ def test_d2t_expand(sv):
     rng = np.random.default_rng(1401)
     for i, (rows, Vd, V, kind) in enumerate([(7, 100, 1000, "sorted"), (5, 999, 1003, "shuffled"),
                                              (3, 1000, 1000, "shuffled"), (6, 37, 4097, None),
-                                             (1280, 3200, 12826, "sorted"), (4, 32000, 128256, "sorted")]):
+                                             (1280, 3200, 12826, "sorted"), (4, 32000, 128256, "sorted"),
+                                             (1281, 3200, 12824, "shuffled"), (37, 32000, 128256, "sorted")]):
         q = rng.random((rows, Vd)).astype(np.float32)
         d2t = None if kind is None else make_d2t(i, Vd, V, shuffled=kind == "shuffled")
         log(f"d2t expand {i}: rows={rows} Vd={Vd} V={V} table={kind}")
@@ -511,6 +512,17 @@ def test_d2t_expand(sv):
     assert np.array_equal(out.cpu().numpy(), oracle.d2t_expand(q, d2t, V))
     f = flat.cpu().numpy()
     assert np.all(f[:3] == 7.0) and np.all(f[3 + rows * V:] == 7.0)
+    # an aligned output view (column tiles, a partial last tile) inside guard bands
+    rows, Vd, V = 9, 3000, 5004
+    q = rng.random((rows, Vd)).astype(np.float32)
+    d2t = make_d2t(10, Vd, V, shuffled=True)
+    flat = torch.full((rows * V + 8,), 7.0, device="cuda")
+    out = flat[4:4 + rows * V].view(rows, V)
+    log(f"d2t expand aligned view in guard bands: rows={rows} Vd={Vd} V={V}")
+    sv.d2t_expand(dev(q), sv.d2t_inverse(dev(d2t), Vd, V), out=out)
+    assert np.array_equal(out.cpu().numpy(), oracle.d2t_expand(q, d2t, V))
+    f = flat.cpu().numpy()
+    assert np.all(f[:4] == 7.0) and np.all(f[4 + rows * V:] == 7.0)
 
 
 def test_d2t_shared_targets(sv):
