@@ -71,26 +71,40 @@ __global__ __launch_bounds__(kGreedyBlock) void greedy_rows_kernel(
     if (b < 0 || b >= B) return;
     const RowPar rp(ws, slot);
     const int32_t xj = j < D ? draft_ids[b * D + j] : -1;
-    // stop once a row before j has ended the chain (never for row 0, nor when
-    // every row's argmax is asked for)
-    if (threadIdx.x == 0) s_stop = 0;
+    // the request's last workgroup writes the outputs
+    auto finish = [&](int L, int32_t yt) {
+        const int t = threadIdx.x;
+        if (t < N) {
+            const int64_t o = b * N + t;
+            const int32_t v = t <= L ? yt : -1;
+            accepted[o] = v;
+            if (predict) predict[o] = v;
+            if (accept_index) accept_index[o] = t <= L ? (int32_t)o : -1;
+            if (argmax_out) argmax_out[o] = yt;
+        }
+        if (t == 0) accept_len[b] = L;
+    };
+    // row 0 is always needed, and every row when every argmax is asked for;
+    // another row whose request already ended before it counts itself in and
+    // leaves at once, else it stops as soon as an earlier row ends the chain
+    const bool may_stop = !argmax_out && j > 0;
+    if (threadIdx.x == 0)
+        s_stop = may_stop && (__hip_atomic_load(rp.word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+                              (((uint64_t)1 << j) - 1)) != 0;
     __syncthreads();
-    RowStop stop((argmax_out || j == 0) ? nullptr : rp.word, ((uint64_t)1 << j) - 1, &s_stop, false);
+    if (s_stop) {
+        if (threadIdx.x >= kWave) return;
+        int32_t yt = -1;
+        const int L = rp.arrive(j, N, false, 0, yt);
+        if (L >= 0) finish(L, yt);
+        return;
+    }
+    RowStop stop(may_stop ? rp.word : nullptr, ((uint64_t)1 << j) - 1, &s_stop, false);
     const int64_t y = row_argmax<kGreedyBlock, true, T, true>(logits + ((int64_t)b * N + j) * V, V, sh, &stop);
     if (threadIdx.x >= kWave) return;
     int32_t yt = -1;
     const int L = rp.arrive(j, N, j == D || xj != (int32_t)y, (int32_t)y, yt);
-    if (L < 0) return;
-    const int t = threadIdx.x;
-    if (t < N) {
-        const int64_t o = b * N + t;
-        const int32_t v = t <= L ? yt : -1;
-        accepted[o] = v;
-        if (predict) predict[o] = v;
-        if (accept_index) accept_index[o] = t <= L ? (int32_t)o : -1;
-        if (argmax_out) argmax_out[o] = yt;
-    }
-    if (t == 0) accept_len[b] = L;
+    if (L >= 0) finish(L, yt);
 }
 
 template <typename T, int BLOCK>

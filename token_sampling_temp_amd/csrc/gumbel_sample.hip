@@ -216,12 +216,32 @@ __global__ __launch_bounds__(kGbBlock) void gumbel_rows_kernel(
     const RowPar rp(ws, slot);
     const float Tm = temperature[b];
     const int32_t xj = j < D ? draft_ids[b * D + j] : -1;
-    // row 0 is always needed; every row is needed when all samples are asked for
-    // stop once a row before j has ended the chain (never for row 0, nor when
-    // every row's sample is asked for)
-    if (threadIdx.x == 0) s_stop = 0;
+    // the request's last workgroup writes the outputs
+    auto finish = [&](int L, int32_t yt) {
+        const int t = threadIdx.x;
+        if (t < N) {
+            const int64_t o = b * N + t;
+            accepted[o] = t <= L ? yt : -1;
+            if (sampled_out) sampled_out[o] = yt;
+        }
+        if (t == 0) accept_len[b] = L;
+    };
+    // row 0 is always needed, and every row when all samples are asked for;
+    // another row whose request already ended before it counts itself in and
+    // leaves at once, else it stops as soon as an earlier row ends the chain
+    const bool may_stop = !sampled_out && j > 0;
+    if (threadIdx.x == 0)
+        s_stop = may_stop && (__hip_atomic_load(rp.word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+                              (((uint64_t)1 << j) - 1)) != 0;
     __syncthreads();
-    RowStop stop((sampled_out || j == 0) ? nullptr : rp.word, ((uint64_t)1 << j) - 1, &s_stop, true);
+    if (s_stop) {
+        if (threadIdx.x >= kWave) return;
+        int32_t yt = -1;
+        const int L = rp.arrive(j, N, false, 0, yt);
+        if (L >= 0) finish(L, yt);
+        return;
+    }
+    RowStop stop(may_stop ? rp.word : nullptr, ((uint64_t)1 << j) - 1, &s_stop, true);
     const T* row = logits + ((int64_t)b * N + j) * V;
     const int64_t y = (double)Tm < kGreedyTemperature
                           ? row_argmax<kGbBlock, true, T, true>(row, V, sh, &stop)
@@ -230,14 +250,7 @@ __global__ __launch_bounds__(kGbBlock) void gumbel_rows_kernel(
     if (threadIdx.x >= kWave) return;
     int32_t yt = -1;
     const int L = rp.arrive(j, N, j == D || xj != (int32_t)y, (int32_t)y, yt);
-    if (L < 0) return;
-    const int t = threadIdx.x;
-    if (t < N) {
-        const int64_t o = b * N + t;
-        accepted[o] = t <= L ? yt : -1;
-        if (sampled_out) sampled_out[o] = yt;
-    }
-    if (t == 0) accept_len[b] = L;
+    if (L >= 0) finish(L, yt);
 }
 
 int64_t gumbel_workspace_bytes(int64_t n_req, int D) {
