@@ -939,7 +939,7 @@ class GumbelWorkload:
     gumbel_sample alone, R = 4 replicas.  Arithmetic-bound: each entry costs a quarter of a
     Philox4x32-10 block and two hardware logarithms, so its roofline is the vector ALU's."""
     name = "gumbel"
-    kernel = "gumbel_rows_kernel"
+    kernel = "gumbel_staged_kernel"
     sources = ("gumbel_sample.hip", "sv_gumbel.hpp", "sv_rowpar.hpp", "sv_argmax.hpp", "sv_common.hpp")
     counters = "gumbel_sample_counters.txt"
     valu_counters = "gumbel_sample_valu_counters.txt"

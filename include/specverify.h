@@ -65,7 +65,7 @@ extern "C" {
 #define SPECVERIFY_MAX_DRAFT 16
 #define SPECVERIFY_STATIC_SCRATCH_BYTES (4 << 20)
 #define SPECVERIFY_RNG_SLOT_SPAN 32
-#define SPECVERIFY_VERSION 201
+#define SPECVERIFY_VERSION 202
 
 /*
  * Temperature softmax followed by top-k then top-p renormalisation.
@@ -369,7 +369,12 @@ int specverify_greedy_verify_workspace_bytes(int64_t n_req, int64_t D, int64_t* 
  *
  * workspace, workspace_bytes
  *                 as for specverify_greedy_verify, sized by
- *                 specverify_gumbel_sample_workspace_bytes(n_req, D).
+ *                 specverify_gumbel_sample_workspace_bytes(n_req, D).  Without
+ *                 sampled_out, row 0 of every request is sampled first and
+ *                 only the requests whose row 0 matched its draft go on, their
+ *                 later rows cut into pieces over all compute units; with it,
+ *                 every (request, row) gets a workgroup.  The results are the
+ *                 same in every form.
  */
 int specverify_gumbel_sample(const void* target_logits, int dtype, const float* temperature,
                              const int32_t* draft_ids, const uint64_t* seed,
@@ -379,8 +384,10 @@ int specverify_gumbel_sample(const void* target_logits, int dtype, const float* 
                              int64_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes specverify_gumbel_sample can use (0: it uses none); the
- * same size as specverify_greedy_verify_workspace_bytes.  Host-only.
+ * Workspace bytes specverify_gumbel_sample can use (0: it uses none): 0 when
+ * D == 0 or n_req == 0, else 128 * n_req (one line per request) + 256 +
+ * 128 * n_req * D (one line per later row, for its pieces), rounded up to
+ * 256.  Host-only.
  */
 int specverify_gumbel_sample_workspace_bytes(int64_t n_req, int64_t D, int64_t* bytes);
 

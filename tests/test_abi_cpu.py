@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = sv.lib()
-    assert sv.version() == 201
+    assert sv.version() == 202
     assert L.specverify_status_string(0) == b"SPECVERIFY_OK"
     assert L.specverify_status_string(1) == b"SPECVERIFY_INVALID_ARGUMENT"
     assert L.specverify_status_string(2) == b"SPECVERIFY_UNSUPPORTED"
@@ -139,11 +139,17 @@ def test_greedy_and_gumbel_and_softmax_invalid_arguments():
 def test_rowpar_workspace_query_and_validation():
     out = ctypes.c_int64(-1)
     L = sv.lib()
+    # greedy: one 128-byte line (ended rows, row count, D + 1 tokens) per request, rounded up to 256
+    q = L.specverify_greedy_verify_workspace_bytes
+    assert q(256, 7, ctypes.byref(out)) == 0 and out.value == 256 * 128
+    assert q(5, 3, ctypes.byref(out)) == 0 and out.value == 768
+    assert q(100, 16, ctypes.byref(out)) == 0 and out.value == 12800
+    # Gumbel: the same lines, a 256-byte count, then a 128-byte line per (request, later row)
+    q = L.specverify_gumbel_sample_workspace_bytes
+    assert q(256, 7, ctypes.byref(out)) == 0 and out.value == 256 * 128 + 256 + 256 * 7 * 128
+    assert q(5, 3, ctypes.byref(out)) == 0 and out.value == 2816   # 640 + 256 + 1920 = 2816
+    assert q(100, 16, ctypes.byref(out)) == 0 and out.value == 12800 + 256 + 204800
     for q in (L.specverify_greedy_verify_workspace_bytes, L.specverify_gumbel_sample_workspace_bytes):
-        # one 128-byte line (ended rows, row count, D + 1 tokens) per request, rounded up to 256
-        assert q(256, 7, ctypes.byref(out)) == 0 and out.value == 256 * 128
-        assert q(5, 3, ctypes.byref(out)) == 0 and out.value == 768
-        assert q(100, 16, ctypes.byref(out)) == 0 and out.value == 12800
         # no drafts or no requests: the one-row form needs none
         assert q(100, 0, ctypes.byref(out)) == 0 and out.value == 0
         assert q(0, 3, ctypes.byref(out)) == 0 and out.value == 0
@@ -151,15 +157,15 @@ def test_rowpar_workspace_query_and_validation():
         assert q(4, 17, ctypes.byref(out)) == 1
         assert q(4, 3, None) == 1
     assert sv.greedy_verify_workspace_bytes(512, 3) == 512 * 128
-    assert sv.gumbel_sample_workspace_bytes(256, 7) == 256 * 128
+    assert sv.gumbel_sample_workspace_bytes(256, 7) == 256 * 128 + 256 + 256 * 7 * 128
     # (logits, dtype, x, B, D, V, req_index, n_req, acc, alen, predict, accept_index, argmax, ws, ws_bytes, stream)
     assert L.specverify_greedy_verify(P, 0, P, 4, 3, 10, None, 4, P, P, None, None, None, P, 8, None) == 1
     assert "needs 512" in L.specverify_last_error().decode()
     assert L.specverify_greedy_verify(P, 0, P, 4, 3, 10, None, 4, P, P, None, None, None,
                                       ctypes.c_void_p(0x1004), 512, None) == 1
     assert "aligned" in L.specverify_last_error().decode()
-    assert L.specverify_gumbel_sample(P, 1, P, P, P, P, 4, 3, 10, None, 4, P, P, None, P, 511, None) == 1
-    assert "needs 512" in L.specverify_last_error().decode()
+    assert L.specverify_gumbel_sample(P, 1, P, P, P, P, 4, 3, 10, None, 4, P, P, None, P, 2303, None) == 1
+    assert "needs 2304" in L.specverify_last_error().decode()
     # the empty batch never looks at the workspace
     assert L.specverify_greedy_verify(None, 0, None, 4, 3, 10, P, 0, None, None, None, None, None, P, 0, None) == 0
 

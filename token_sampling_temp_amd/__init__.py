@@ -335,7 +335,7 @@ def greedy_verify_workspace_bytes(n_req, D) -> int:
 
 
 def gumbel_sample_workspace_bytes(n_req, D) -> int:
-    """Bytes of the per-request words of gumbel_sample's one-workgroup-per-row form (0: none)."""
+    """Bytes of gumbel_sample's workspace: request lines, a helper count and a line per later row (0: none)."""
     return _query("specverify_gumbel_sample_workspace_bytes", n_req, D)
 
 

@@ -13,6 +13,8 @@
 // The scores are float: z / T as z * (1/T), and both logarithms from the
 // hardware base-2 logarithm times ln 2 (a few ulp from correctly rounded
 // values; only a near tie of the two best scores can tell them apart).
+#include <algorithm>
+
 #include "sv_argmax.hpp"
 #include "sv_gumbel.hpp"
 #include "sv_launch.hpp"
@@ -62,7 +64,8 @@ __device__ __forceinline__ void load_group4<uint16_t>(const uint16_t* row, int64
 constexpr int kPf = 4;
 template <int BLOCK, typename T, bool STOP>
 __device__ __forceinline__ void row_gumbel_pipelined(const T* row, int Vi, float invT, uint64_t seed,
-                                                     uint64_t subseq, float& best, int& bi, RowStop* stop) {
+                                                     uint64_t subseq, float& best, int& bi, RowStop* stop,
+                                                     int gbase) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     constexpr bool kF32 = sizeof(T) == 4;
     typedef typename std::conditional<kF32, u32x4, u32x2>::type Raw;
@@ -107,14 +110,17 @@ __device__ __forceinline__ void row_gumbel_pipelined(const T* row, int Vi, float
             float f[4];
             unpack4(slot[j], f);
             slot[j] = ld(g + kPf * BLOCK);
-            if (g < ngroups) gumbel_group(f, g, Vi, invT, seed, subseq, best, bi);
+            if (g < ngroups) gumbel_group(f, g, Vi, invT, seed, subseq, best, bi, gbase);
         }
     }
 }
 
+// The packed (score key, index) maximum of the row's scores, indices from
+// the start of `row`; gbase: the Philox block of its first group (a piece
+// of a longer row starting at entry 4 gbase).
 template <int BLOCK, typename T, bool STOP = false>
-__device__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed, uint64_t subseq,
-                              ArgmaxShared<BLOCK>& sh, RowStop* stop = nullptr) {
+__device__ uint64_t row_gumbel_packed(const T* row, int64_t V, float invT, uint64_t seed, uint64_t subseq,
+                                      ArgmaxShared<BLOCK>& sh, RowStop* stop = nullptr, int gbase = 0) {
     const bool aligned = ((uintptr_t)row % (4 * sizeof(T))) == 0;
     const int Vi = (int)V;   // V < 2^31
     const int ngroups = (Vi + 3) / 4;
@@ -125,16 +131,15 @@ __device__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed
     // whole groups only (V a multiple of 4), so no load straddles the row's end
     if (aligned && (Vi & 3) == 0 &&
         V * (int64_t)sizeof(T) + (int64_t)(kPf + 1) * BLOCK * 4 * (int64_t)sizeof(T) < ((int64_t)1 << 32)) {
-        row_gumbel_pipelined<BLOCK, T, STOP>(row, Vi, invT, seed, subseq, best, bi, stop);
+        row_gumbel_pipelined<BLOCK, T, STOP>(row, Vi, invT, seed, subseq, best, bi, stop, gbase);
         const uint64_t key = bi < 0 ? 0 : pack_key_index(float_key(best), (int64_t)bi);
-        const uint64_t m = block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
-        return packed_index(m);
+        return block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
     }
     for (int g = threadIdx.x; g < ngroups; g += BLOCK) {
         const int v0 = g * 4;
         float f[4];
         load_group4<T>(row, v0, V, aligned, f);
-        const uint4 w = philox_block_mad(seed, subseq, (uint64_t)g);
+        const uint4 w = philox_block_mad(seed, subseq, (uint64_t)(g + gbase));
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
         if (v0 + 3 < Vi) {
 #pragma unroll
@@ -157,8 +162,13 @@ __device__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed
         }
     }
     const uint64_t key = bi < 0 ? 0 : pack_key_index(float_key(best), (int64_t)bi);
-    const uint64_t m = block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
-    return packed_index(m);
+    return block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
+}
+
+template <int BLOCK, typename T, bool STOP = false>
+__device__ __forceinline__ int64_t row_gumbel(const T* row, int64_t V, float invT, uint64_t seed, uint64_t subseq,
+                                              ArgmaxShared<BLOCK>& sh, RowStop* stop = nullptr) {
+    return packed_index(row_gumbel_packed<BLOCK, T, STOP>(row, V, invT, seed, subseq, sh, stop));
 }
 
 template <typename T>
@@ -253,8 +263,181 @@ __global__ __launch_bounds__(kGbBlock) void gumbel_rows_kernel(
     if (L >= 0) finish(L, yt);
 }
 
+// Staged form (strict acceptance, samples of later rows not asked for).
+// Drafts from another distribution rarely match a Gumbel sample, so most
+// requests end at row 0; giving every (request, row) its own workgroup
+// leaves a long tail of workgroups that start only to find their request
+// ended.  Here workgroup g < n_req samples row 0 of request slot g; the
+// request ends there (its outputs are written at once) or continues.  The
+// other gridDim - n_req workgroups (helpers) wait for every request's row-0
+// verdict, list the requests that continue, and share the rows 1..D of
+// those requests cut into S pieces of seg entries (S chosen in the kernel
+// from how many rows remain).  The pieces of a row meet in the workspace:
+// each stores its packed (score key, absolute index) maximum with bit 31 set
+// (an index below 2^31 keeps that bit in its field anyway, so 0 means not
+// yet written) and counts itself in; the last combines them.  Each finished
+// row joins the request's hand-off (sv_rowpar.hpp), row 0 having counted
+// itself in first.
+//
+// Workspace: n_req hand-off lines, the request's state in bytes 120..123 of
+// its line (0 not yet known, 1 continues, 2 done); then a 256-byte block whose
+// first word counts finished helpers; then one 128-byte line per (request,
+// row 1..D) for the pieces (a count, then S values from byte 8).  The last
+// helper clears the states and its count; the hand-off and piece lines are
+// cleared by their last users, so the workspace is zero at rest.
+constexpr int64_t kGbStateOff = 120;
+constexpr int64_t kGbPieceLine = 128;
+constexpr int kGbPiecesMax = 15;
+
+template <typename T>
+__global__ __launch_bounds__(kGbBlock) void gumbel_staged_kernel(
+    const T* __restrict__ logits, const float* __restrict__ temperature, const int32_t* __restrict__ draft_ids,
+    const uint64_t* __restrict__ seed, const uint64_t* __restrict__ offset, int64_t B, int D, int64_t V,
+    const int32_t* __restrict__ req_index, int64_t n_req, void* __restrict__ ws, int32_t* __restrict__ accepted,
+    int32_t* __restrict__ accept_len) {
+    __shared__ ArgmaxShared<kGbBlock> sh;
+    __shared__ uint32_t s_stop;
+    __shared__ uint32_t s_wsum[kGbBlock / kWave];
+    __shared__ int32_t s_cont[kGbBlock];
+    const int N = D + 1;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    char* const wsb = static_cast<char*>(ws);
+    auto state_of = [&](int64_t slot) { return reinterpret_cast<uint32_t*>(wsb + slot * kRowParLine + kGbStateOff); };
+    // the outputs of request b (wave 0)
+    auto finish = [&](int64_t b, int L, int32_t yt) {
+        if (lane < N) accepted[b * N + lane] = lane <= L ? yt : -1;
+        if (lane == 0) accept_len[b] = L;
+    };
+    if ((int64_t)blockIdx.x < n_req) {
+        // ---- row 0 of request slot blockIdx.x
+        const int64_t slot = blockIdx.x;
+        const int64_t b = req_index ? (int64_t)req_index[slot] : slot;
+        uint32_t* const st = state_of(slot);
+        if (b < 0 || b >= B) {
+            if (tid == 0) __hip_atomic_store(st, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        const float Tm = temperature[b];
+        const T* row = logits + (int64_t)b * N * V;
+        const int64_t y = (double)Tm < kGreedyTemperature
+                              ? row_argmax<kGbBlock, true>(row, V, sh)
+                              : row_gumbel<kGbBlock>(row, V, 1.0f / Tm, seed[b], offset[b], sh);
+        if (tid >= kWave) return;
+        if (draft_ids[b * D] != (int32_t)y) {   // the chain ends at row 0
+            finish(b, 0, (int32_t)y);
+            if (lane == 0) __hip_atomic_store(st, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        if (lane == 0) __hip_atomic_store(st, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const RowPar rp(ws, slot);
+        int32_t yt = -1;
+        const int L = rp.arrive(0, N, false, (int32_t)y, yt);
+        if (L >= 0) finish(b, L, yt);
+        return;
+    }
+    // ---- helpers.  Every row-0 workgroup was dispatched before this one and
+    // waits on nothing, so each wait below ends; the bound only keeps a
+    // broken invariant from hanging the device.
+    const int64_t h = (int64_t)blockIdx.x - n_req, H = (int64_t)gridDim.x - n_req;
+    uint32_t cont = 0;
+    if (tid < n_req) {
+        uint32_t v = 0;
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            v = __hip_atomic_load(state_of(tid), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        cont = v == 1u ? 1u : 0u;
+    }
+    // the continuing request slots, in slot order
+    const uint32_t inc = wave_inclusive_sum(cont, lane);
+    if (lane == kWave - 1) s_wsum[wid] = inc;
+    __syncthreads();
+    uint32_t pos = inc - cont, ncont = 0;
+#pragma unroll
+    for (int i = 0; i < kGbBlock / kWave; ++i) {
+        const uint32_t t = s_wsum[i];
+        if (i < wid) pos += t;
+        ncont += t;
+    }
+    if (cont) s_cont[pos] = tid;
+    __syncthreads();
+    // pieces per row: about one piece per helper over all the rows to
+    // evaluate, each of at least 4096 entries and a multiple of 64 (so a
+    // piece keeps the row's alignment), at most kGbPiecesMax
+    const int64_t nrows = (int64_t)ncont * D;
+    int S = (int)max((int64_t)1, min((int64_t)kGbPiecesMax, min(nrows > 0 ? H / nrows : 1, V / 4096)));
+    const int64_t seg = ((V + S - 1) / S + 63) / 64 * 64;
+    S = (int)((V + seg - 1) / seg);
+    const int64_t per_req = (int64_t)D * S;
+    const int64_t items = (int64_t)ncont * per_req;
+    for (int64_t it = h; it < items; it += H) {
+        const int64_t k = it / per_req;
+        const int rem = (int)(it - k * per_req);
+        const int j = 1 + rem / S, piece = rem - (rem / S) * S;
+        const int64_t slot = s_cont[k];
+        const int64_t b = req_index ? (int64_t)req_index[slot] : slot;
+        const RowPar rp(ws, slot);
+        char* const line = wsb + n_req * kRowParLine + 256 + (slot * D + (j - 1)) * kGbPieceLine;
+        uint32_t* const cnt = reinterpret_cast<uint32_t*>(line);
+        uint64_t* const part = reinterpret_cast<uint64_t*>(line + 8);
+        const float Tm = temperature[b];
+        if (tid == 0) s_stop = 0;
+        __syncthreads();
+        // a piece of a row after one that ended the chain stops early
+        RowStop stop(rp.word, ((uint64_t)1 << j) - 1, &s_stop, true);
+        const int64_t off = (int64_t)piece * seg;
+        const T* row = logits + ((int64_t)b * N + j) * V + off;
+        const int64_t len = min(seg, V - off);
+        const uint64_t m = (double)Tm < kGreedyTemperature
+                               ? row_argmax_packed<kGbBlock, true, T, true>(row, len, sh, &stop)
+                               : row_gumbel_packed<kGbBlock, T, true>(row, len, 1.0f / Tm, seed[b],
+                                                                      offset[b] + kRngSlotSpan * (uint64_t)j, sh,
+                                                                      &stop, (int)(off / 4));
+        if (tid < kWave) {
+            const uint64_t mine = (m & 0xFFFFFFFF00000000ull) |
+                                  (uint64_t)((0xFFFFFFFFu - (uint32_t)(packed_index(m) + off)) | 0x80000000u);
+            uint32_t prev = 0;
+            if (lane == 0) {
+                __hip_atomic_store(&part[piece], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if ((uint32_t)__builtin_amdgcn_readfirstlane((int)prev) == (uint32_t)(S - 1)) {
+                // the row's last piece: every piece stored its value before
+                // its count, so each wait ends
+                uint64_t v = 0;
+                if (lane < S) {
+                    for (int spin = 0; spin < (1 << 20); ++spin) {
+                        v = __hip_atomic_load(&part[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (v) break;
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    __hip_atomic_store(&part[lane], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int64_t y = packed_index(wave_allreduce(v, OpMaxU64{}));
+                const int32_t xj = j < D ? draft_ids[b * D + j] : -1;
+                int32_t yt = -1;
+                const int L = rp.arrive(j, N, j == D || xj != (int32_t)y, (int32_t)y, yt);
+                if (L >= 0) finish(b, L, yt);
+            }
+        }
+        __syncthreads();   // the next item reuses the reduction's LDS and the stop flag
+    }
+    // ---- the last helper to finish sets the states and its count back to zero
+    uint32_t* const done = reinterpret_cast<uint32_t*>(wsb + n_req * kRowParLine);
+    if (tid == 0)
+        s_stop = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(H - 1);
+    __syncthreads();
+    if (s_stop) {
+        if (tid < n_req) __hip_atomic_store(state_of(tid), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 int64_t gumbel_workspace_bytes(int64_t n_req, int D) {
-    return (D > 0 && n_req > 0) ? rowpar_workspace_bytes(n_req) : 0;
+    if (D <= 0 || n_req <= 0) return 0;
+    return (n_req * kRowParLine + 256 + n_req * D * kGbPieceLine + 255) / 256 * 256;
 }
 
 hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temperature,
@@ -263,8 +446,23 @@ hipError_t launch_gumbel_sample(const void* logits, int dtype, const float* temp
                                 int32_t* accepted, int32_t* accept_len, int32_t* sampled_out, void* workspace,
                                 hipStream_t stream) {
     const dim3 block(kGbBlock);
-    // as for greedy verify: rows spread over CUs below two requests per CU
-    if (workspace && gumbel_workspace_bytes(n_req, D) > 0 && n_req < 2 * (int64_t)device_compute_units()) {
+    const int64_t cus = device_compute_units();
+    // below two requests per CU, with a workspace: the staged form when only
+    // the accepted tokens are asked for, else one workgroup per row
+    if (workspace && gumbel_workspace_bytes(n_req, D) > 0 && n_req < 2 * cus && !sampled_out &&
+        n_req <= kGbBlock) {
+        const dim3 grid((unsigned)(n_req + cus));
+        if (dtype == kDtypeBF16)
+            hipLaunchKernelGGL(gumbel_staged_kernel<uint16_t>, grid, block, 0, stream,
+                               static_cast<const uint16_t*>(logits), temperature, draft_ids, seed, offset, B, D, V,
+                               req_index, n_req, workspace, accepted, accept_len);
+        else
+            hipLaunchKernelGGL(gumbel_staged_kernel<float>, grid, block, 0, stream, static_cast<const float*>(logits),
+                               temperature, draft_ids, seed, offset, B, D, V, req_index, n_req, workspace, accepted,
+                               accept_len);
+        return hipGetLastError();
+    }
+    if (workspace && gumbel_workspace_bytes(n_req, D) > 0 && n_req < 2 * cus) {
         const dim3 grid((unsigned)(n_req * (D + 1)));
         if (dtype == kDtypeBF16)
             hipLaunchKernelGGL(gumbel_rows_kernel<uint16_t>, grid, block, 0, stream,

@@ -18,14 +18,13 @@ struct ArgmaxShared {
 // NaN come here, so it reads one element at a time and keeps few registers
 // (a call's register count is the largest of its callees').
 template <int BLOCK, typename T>
-__device__ __noinline__ int64_t row_argmax_exact(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh) {
+__device__ __noinline__ uint64_t row_argmax_exact(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh) {
     uint64_t best = 0;   // below every packed key of an element
     for (int64_t i = threadIdx.x; i < V; i += BLOCK) {
         const uint64_t k = pack_key_index(float_key(load_elem(row + i)), i);
         best = k > best ? k : best;
     }
-    const uint64_t m = block_reduce<BLOCK>(best, OpMaxU64{}, (uint64_t)0, sh.red_u);
-    return packed_index(m);
+    return block_reduce<BLOCK>(best, OpMaxU64{}, (uint64_t)0, sh.red_u);
 }
 
 // Fast path: each thread keeps the maximum of its elements and the index of
@@ -48,8 +47,13 @@ __device__ __noinline__ int64_t row_argmax_exact(const T* row, int64_t V, Argmax
 // reduction.
 constexpr int kArgmaxBatch = 4;
 
+//
+// row_argmax_packed returns the packed (value key, index) maximum itself
+// (0 for an empty row), which combines across pieces of a row by a plain
+// 64-bit maximum once the indices are made absolute; row_argmax returns the
+// index.
 template <int BLOCK, bool NT, typename T, bool STOP = false>
-__device__ int64_t row_argmax(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh, RowStop* stop = nullptr) {
+__device__ uint64_t row_argmax_packed(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh, RowStop* stop = nullptr) {
     constexpr int E = RowSplit<T>::kEpv;
     constexpr int U = kArgmaxBatch;
     const RowSplit<T> s(row, V);
@@ -160,7 +164,13 @@ __device__ int64_t row_argmax(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh, 
                                              : pack_key_index(float_key(best), bidx);
     const uint64_t m = block_reduce<BLOCK>(key, OpMaxU64{}, (uint64_t)0, sh.red_u);
     if (m == ~(uint64_t)0) return row_argmax_exact<BLOCK>(row, V, sh);
-    return packed_index(m);
+    return m;
+}
+
+template <int BLOCK, bool NT, typename T, bool STOP = false>
+__device__ __forceinline__ int64_t row_argmax(const T* row, int64_t V, ArgmaxShared<BLOCK>& sh,
+                                              RowStop* stop = nullptr) {
+    return packed_index(row_argmax_packed<BLOCK, NT, T, STOP>(row, V, sh, stop));
 }
 
 }  // namespace sv

@@ -43,11 +43,12 @@ __device__ __forceinline__ float gumbel_score(float z, float invT, uint32_t w) {
 }
 
 // Scores of group g (entries 4g .. 4g+3, those below Vi) folded into the
-// thread's (best, bi); entries arrive in increasing index order.
+// thread's (best, bi); entries arrive in increasing index order.  gbase: the
+// Philox block of group 0 (a piece of a row that starts at entry 4 gbase).
 __device__ __forceinline__ void gumbel_group(const float (&f)[4], int g, int Vi, float invT, uint64_t seed,
-                                             uint64_t subseq, float& best, int& bi) {
+                                             uint64_t subseq, float& best, int& bi, int gbase = 0) {
     const int v0 = g * 4;
-    const uint4 w = philox_block_mad(seed, subseq, (uint64_t)g);
+    const uint4 w = philox_block_mad(seed, subseq, (uint64_t)(g + gbase));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
