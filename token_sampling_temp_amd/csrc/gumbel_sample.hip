@@ -369,12 +369,17 @@ __global__ __launch_bounds__(kGbBlock) void gumbel_staged_kernel(
     int S = (int)max((int64_t)1, min((int64_t)kGbPiecesMax, min(nrows > 0 ? H / nrows : 1, V / 4096)));
     const int64_t seg = ((V + S - 1) / S + 63) / 64 * 64;
     S = (int)((V + seg - 1) / seg);
-    const int64_t per_req = (int64_t)D * S;
-    const int64_t items = (int64_t)ncont * per_req;
+    // items in row order (every continuing request's row 1, then row 2, ...),
+    // the pieces of a row together: when many requests continue, helpers
+    // take the earlier rows first and a later row of a request whose chain
+    // ended meanwhile stops early
+    const int64_t per_row = (int64_t)ncont * S;
+    const int64_t items = per_row * D;
     for (int64_t it = h; it < items; it += H) {
-        const int64_t k = it / per_req;
-        const int rem = (int)(it - k * per_req);
-        const int j = 1 + rem / S, piece = rem - (rem / S) * S;
+        const int j = 1 + (int)(it / per_row);
+        const int64_t rem = it - (int64_t)(j - 1) * per_row;
+        const int64_t k = rem / S;
+        const int piece = (int)(rem - k * S);
         const int64_t slot = s_cont[k];
         const int64_t b = req_index ? (int64_t)req_index[slot] : slot;
         const RowPar rp(ws, slot);
@@ -394,7 +399,14 @@ __global__ __launch_bounds__(kGbBlock) void gumbel_staged_kernel(
                                : row_gumbel_packed<kGbBlock, T, true>(row, len, 1.0f / Tm, seed[b],
                                                                       offset[b] + kRngSlotSpan * (uint64_t)j, sh,
                                                                       &stop, (int)(off / 4));
-        if (tid < kWave) {
+        if (tid < kWave && S == 1) {
+            // a whole row: no pieces to meet
+            const int64_t y = packed_index(m);
+            const int32_t xj = j < D ? draft_ids[b * D + j] : -1;
+            int32_t yt = -1;
+            const int L = rp.arrive(j, N, j == D || xj != (int32_t)y, (int32_t)y, yt);
+            if (L >= 0) finish(b, L, yt);
+        } else if (tid < kWave) {
             const uint64_t mine = (m & 0xFFFFFFFF00000000ull) |
                                   (uint64_t)((0xFFFFFFFFu - (uint32_t)(packed_index(m) + off)) | 0x80000000u);
             uint32_t prev = 0;
