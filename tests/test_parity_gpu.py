@@ -870,6 +870,37 @@ def test_gumbel_sample_fuzz(sv):
     log(f"gumbel fuzz flagged requests: {flagged}")
 
 
+def test_gumbel_staged_many_continuing(sv):
+    """The staged Gumbel form when most requests continue past row 0 (drafts
+    are the oracle's own samples, so chains run to the bonus row): the
+    helpers then take whole later rows, not pieces.  Against the oracle and
+    the one-workgroup-per-request form, two calls on one workspace, which is
+    zero afterwards."""
+    torch = __import__("torch")
+    B, D, V = 96, 7, 8192
+    c = fuzz_case(470, B, D, V, "bf16")
+    rng = np.random.default_rng(470)
+    T = rng.uniform(0.5, 1.5, B).astype(np.float32)
+    T[::7] = 0.0   # some greedy rows among them
+    full = oracle.gumbel_sample(c["logits"], "bf16", T, np.zeros((B, D), np.int32), c["seed"], c["offset"],
+                                all_rows=True)
+    x = np.where(rng.random((B, D)) < 0.95, full["sampled"][:, :D], rng.integers(0, V, size=(B, D))).astype(np.int32)
+    ref = oracle.gumbel_sample(c["logits"], "bf16", T, x, c["seed"], c["offset"], all_rows=True)
+    ws = torch.zeros((sv.gumbel_sample_workspace_bytes(B, D),), dtype=torch.uint8, device="cuda")
+    args = (dev_logits(c["logits"], "bf16"), dev(T), dev(x), dev(c["seed"]), dev(c["offset"]))
+    log(f"gumbel staged, many continuing: B={B} D={D} V={V}")
+    for _ in range(2):
+        out = sv.gumbel_sample(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+        assert_chain_match(np_i(out["accepted_tokens"]), np_i(out["accept_length"]), ref, range(B), (V, D),
+                           len_exact=False, max_excluded=B)
+        per = sv.gumbel_sample(*args, workspace=False)
+        assert np.array_equal(np_i(per["accepted_tokens"]), np_i(out["accepted_tokens"]))
+        assert np.array_equal(np_i(per["accept_length"]), np_i(out["accept_length"]))
+    assert float(np.mean(np_i(out["accept_length"]))) > 3.0   # most chains run deep
+
+
 # --------------------------------------------------------------------------- config 5 (mixed modes)
 def test_config5_mixed_modes_full(sv):
     """The mixed batch (B=1024 D=7 V=129280 bf16), each mode through
